@@ -1,0 +1,24 @@
+"""CPU oracle for the A8W8 decode linears -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The product path never routes through it.
+"""
+
+from .a8w8_oracle import (  # noqa: F401
+    bf16_to_f32,
+    dequant,
+    dequant_weight_bf16,
+    down_split,
+    exp_f32,
+    int_gemm,
+    layer_linears_decode,
+    linear_decode,
+    mlp_block_decode,
+    prefill_mlp,
+    quantize_rows,
+    reduce_residual_bf16,
+    rmsnorm,
+    rne_bf16,
+    silu_mul,
+    split_k_ranges,
+)

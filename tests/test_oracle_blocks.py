@@ -1,0 +1,145 @@
+"""Pins of the oracle's composed blocks: linear, MLP, layer and prefill.
+
+The stages are pinned one by one in the other oracle tests; here each composition is
+checked against exact FP64 math on the dequantized weights (no activation
+quantization) within a bound derived from the INT8 step size, and the linear is
+checked against a closed form and a per-element quantization error bound.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import (bf16_to_f32, dequant_weight_bf16, int_gemm, layer_linears_decode,
+                    linear_decode, mlp_block_decode, prefill_mlp, quantize_rows, rne_bf16)
+from w8a8_quantized_decode_amd import synth
+
+C0 = synth.CONFIGS[0]
+
+
+def _f(b):
+    return bf16_to_f32(b).astype(np.float64)
+
+
+def _rms_f64(x, gamma, eps):
+    return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps) * gamma
+
+
+def _silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def test_linear_identity_weights_round_trip():
+    # N = K, w = 127*I, s_w = fl32(1/127): y = q * s_x up to FP32 rounding, so the
+    # linear is a quantize/dequantize round trip: |y - v| <= s_x/2 (+ BF16 output rounding)
+    rng = np.random.default_rng(1)
+    K = 256
+    v = rng.standard_normal((3, K)).astype(np.float32)
+    q, s = quantize_rows(v)
+    w = (127 * np.eye(K)).astype(np.int8)
+    sw = np.full(K, np.float32(1) / np.float32(127), dtype=np.float32)
+    y, acc = linear_decode(q, s, w, sw)
+    assert np.array_equal(acc, 127 * q.astype(np.int64))
+    yf = _f(y)
+    bound = s[:, None].astype(np.float64) * (0.5 + 2.0**-16) + np.abs(yf) * 2.0**-8 + 1e-7
+    assert np.all(np.abs(yf - v) <= bound)
+
+
+def test_linear_error_bound_against_exact_math():
+    rng = np.random.default_rng(2)
+    M, N, K = 4, 96, 512
+    v = rng.standard_normal((M, K)).astype(np.float32)
+    w = rng.integers(-127, 128, size=(N, K), dtype=np.int8)
+    sw = rng.uniform(1e-3, 1e-2, size=N).astype(np.float32)
+    res = synth.normal_bf16(3, (M, N))
+    q, s = quantize_rows(v)
+    y, _ = linear_decode(q, s, w, sw, residual_bits=res)
+    wdeq = w.astype(np.float64) * sw.astype(np.float64)[:, None]
+    exact = v.astype(np.float64) @ wdeq.T + _f(res)
+    # per element: (s_x/2) * sum_k |W_deq[n,k]| (+ quotient rounding) + BF16 rounding
+    qerr = (s.astype(np.float64)[:, None] * (0.5 + 2.0**-16)) * np.abs(wdeq).sum(axis=1)[None, :]
+    bound = qerr + np.abs(exact) * 2.0**-8 * 1.01 + 1e-6
+    assert np.all(np.abs(_f(y) - exact) <= bound)
+
+
+def _mlp_exact(d, eps):
+    x = _f(d["x"])
+    xn = _rms_f64(x, _f(d["gamma_post"]), eps)
+    g = xn @ (d["w_gate"].astype(np.float64) * d["s_gate"][:, None]).T
+    u = xn @ (d["w_up"].astype(np.float64) * d["s_up"][:, None]).T
+    h = _silu(g) * u
+    return h @ (d["w_down"].astype(np.float64) * d["s_down"][:, None]).T, h
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 4])
+def test_mlp_block_against_exact_math(split_k):
+    d = synth.mlp_inputs(C0, M=3)
+    out, st = mlp_block_decode(d["x"], d["gamma_post"], C0.eps, d["w_gate"], d["s_gate"],
+                               d["w_up"], d["s_up"], d["w_down"], d["s_down"], d["res"],
+                               split_k=split_k)
+    down_exact, h_exact = _mlp_exact(d, C0.eps)
+    down_q = _f(out) - _f(d["res"])
+    rel = np.linalg.norm(down_q - down_exact) / np.linalg.norm(down_exact)
+    # two INT8 quantizations (x and h) with absmax scaling: normwise error of a few %
+    assert rel < 0.05, rel
+    hrel = np.linalg.norm(st["h"] - h_exact) / np.linalg.norm(h_exact)
+    assert hrel < 0.03, hrel
+    # the INT32 partials of the split Down add up to the unsplit accumulator
+    assert np.array_equal(sum(st["acc_down"]), int_gemm(st["q_h"], d["w_down"]))
+
+
+def test_gate_and_up_are_not_interchangeable():
+    d = synth.mlp_inputs(C0, M=2)
+    out, _ = mlp_block_decode(d["x"], d["gamma_post"], C0.eps, d["w_gate"], d["s_gate"],
+                              d["w_up"], d["s_up"], d["w_down"], d["s_down"], d["res"])
+    swapped, _ = mlp_block_decode(d["x"], d["gamma_post"], C0.eps, d["w_up"], d["s_up"],
+                                  d["w_gate"], d["s_gate"], d["w_down"], d["s_down"], d["res"])
+    down_exact, _ = _mlp_exact(d, C0.eps)
+    e_ok = np.linalg.norm(_f(out) - _f(d["res"]) - down_exact)
+    e_sw = np.linalg.norm(_f(swapped) - _f(d["res"]) - down_exact)
+    assert e_sw > 10 * e_ok
+
+
+def test_layer_against_exact_math():
+    cfg = C0
+    d = synth.layer_inputs(cfg, M=2)
+    out, st = layer_linears_decode(d["x"], d["gamma_in"], d["gamma_post"], cfg.eps,
+                                   d["w_qkv"], d["s_qkv"], d["w_o"], d["s_o"], d["w_gate"],
+                                   d["s_gate"], d["w_up"], d["s_up"], d["w_down"],
+                                   d["s_down"], cfg.n_q_heads, cfg.head_dim, cfg.split_k)
+    x = _f(d["x"])
+    xn = _rms_f64(x, _f(d["gamma_in"]), cfg.eps)
+    qkv = xn @ (d["w_qkv"].astype(np.float64) * d["s_qkv"][:, None]).T
+    assert st["qkv"].shape == (2, cfg.n_qkv)
+    r = np.linalg.norm(_f(st["qkv"]) - qkv) / np.linalg.norm(qkv)
+    assert r < 0.03, r
+    attn = qkv[:, : cfg.n_q_heads * cfg.head_dim]
+    h1 = attn @ (d["w_o"].astype(np.float64) * d["s_o"][:, None]).T + x
+    r = np.linalg.norm(_f(st["h1"]) - h1) / np.linalg.norm(h1)
+    assert r < 0.03, r
+    # the MLP half runs on the oracle's own h1 as both input and residual
+    dd = dict(d, x=st["h1"])
+    down_exact, _ = _mlp_exact(dd, cfg.eps)
+    r = np.linalg.norm(_f(out) - _f(st["h1"]) - down_exact) / np.linalg.norm(down_exact)
+    assert r < 0.05, r
+
+
+def test_prefill_weight_tiles_and_output():
+    d = synth.mlp_inputs(C0, M=8)
+    wq = dequant_weight_bf16(d["w_gate"], d["s_gate"])
+    exact_w = d["w_gate"].astype(np.float64) * d["s_gate"].astype(np.float64)[:, None]
+    # FP32 product then BF16: within half a BF16 ulp (2**-8 relative) plus one FP32 rounding
+    assert np.all(np.abs(_f(wq) - exact_w) <= np.abs(exact_w) * (2.0**-8 + 2.0**-24) * 1.0001)
+    out, st = prefill_mlp(d["x"], d["gamma_post"], C0.eps, d["w_gate"], d["s_gate"],
+                          d["w_up"], d["s_up"], d["w_down"], d["s_down"], d["res"])
+    assert np.array_equal(st["a"], rne_bf16(st["xn"]))
+    x = _f(d["x"])
+    xn = _rms_f64(x, _f(d["gamma_post"]), C0.eps)
+    g = xn @ exact_w.T
+    u = xn @ (d["w_up"].astype(np.float64) * d["s_up"][:, None]).T
+    down = (_silu(g) * u) @ (d["w_down"].astype(np.float64) * d["s_down"][:, None]).T
+    r = np.linalg.norm(_f(out) - _f(d["res"]) - down) / np.linalg.norm(down)
+    # BF16 activations, weights and h: a few BF16 roundings normwise
+    assert r < 0.01, r
+    # FP64 accumulation rounded once: g equals the exactly rounded BF16 dot products
+    gg = _f(st["a"]) @ _f(wq).T
+    assert np.array_equal(st["g"], gg.astype(np.float32))
