@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the A8W8 decode linears on one MI355X.
+
+One step = one call of a8w8_layer_linears (QKV, O, Gate/Up, split-K Down with all the
+quantize / dequant / SiLU / RNE work) on a Qwen3-14B-shaped layer at decode batch 1.
+Steps rotate over several independently generated weight sets (1.3 GB at the default
+4 sets) so the 256 MB last-level cache cannot serve weights from a previous step.
+
+Prints one JSON line: INT8-weight HBM GB/s (value), microseconds per layer, the
+roofline of the dominant kernel (the Gate/Up GEMM) from HIP events recorded around it
+on the library's stream, and the CPU oracle's throughput on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--config 2|3]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/layer and INT8-weight HBM GB/s (% of peak), A8W8 decode linears at batch 1"
+HBM_PEAK_GBS = 8000.0
+GATEUP_KERNEL = 5     # kernel number of the Gate/Up GEMM inside a8w8_layer_linears
+PMC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_pmc.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
+    p.add_argument("--config", type=int, default=2, help="2: layer M=1; 3: 40-layer M=16 stack")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_decode.hip", "device_common.h", "internal.h"):
+        with open(os.path.join(ROOT, "w8a8_quantized_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None if the
+    summary is missing or was taken on a different kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if pmc.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return pmc.get("hbm_bytes_per_dispatch")
+
+
+def cpu_baseline(cfg, seconds: float):
+    """The oracle as it stands, timed on whole layers of the same workload."""
+    import oracle as O
+    from w8a8_quantized_decode_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        cores = os.cpu_count() or 1
+    done, t_total, layer = 0, 0.0, 0
+    wbytes = 0
+    while t_total < seconds and layer < 8:
+        d = synth.layer_inputs(cfg, layer=100 + layer, M=cfg.M)
+        t0 = time.perf_counter()
+        O.layer_linears_decode(d["x"], d["gamma_in"], d["gamma_post"], cfg.eps, d["w_qkv"],
+                               d["s_qkv"], d["w_o"], d["s_o"], d["w_gate"], d["s_gate"],
+                               d["w_up"], d["s_up"], d["w_down"], d["s_down"], cfg.n_q_heads,
+                               cfg.head_dim, cfg.split_k)
+        t_total += time.perf_counter() - t0
+        wbytes += sum(d[k].nbytes for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"))
+        done += 1
+        layer += 1
+    return {"value": round(wbytes / t_total / 1e9, 3), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} Qwen3-14B layer-linears decode passes at M={cfg.M} "
+                      f"(input generation excluded), {t_total:.1f} s",
+            "us_per_layer": round(t_total / done * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    import torch
+    from w8a8_quantized_decode_amd import binding as B
+    from w8a8_quantized_decode_amd import synth
+
+    cfg = synth.CONFIGS[args.config]
+    if cfg.kind not in ("layer", "stack"):
+        raise SystemExit("bench.py times the layer-linears configs (2 or 3)")
+    layers = cfg.layers if cfg.kind == "stack" else 1
+    M, H, I, n_qkv = cfg.M, cfg.H, cfg.I, cfg.n_qkv
+    nsets = layers if cfg.kind == "stack" else max(1, args.sets)
+    print(f"[bench] config {cfg.index}: {cfg.name}; generating {nsets} weight sets",
+          file=sys.stderr, flush=True)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    sets = []
+    for s in range(nsets):
+        d = synth.layer_inputs(cfg, layer=s, M=M, with_x=(s == 0))
+        sets.append(dict(
+            gin=up(d["gamma_in"]), gpost=up(d["gamma_post"]),
+            qkv=(up(d["w_qkv"]), up(d["s_qkv"])), o=(up(d["w_o"]), up(d["s_o"])),
+            gate=(up(d["w_gate"]), up(d["s_gate"])), up=(up(d["w_up"]), up(d["s_up"])),
+            down=(up(d["w_down"]), up(d["s_down"]))))
+        if s == 0:
+            x0 = up(d["x"])
+        del d
+    wbytes_layer = (n_qkv * H + H * H + 2 * I * H + H * I)
+    ws = torch.zeros(B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, M, H, I, n_qkv, cfg.split_k),
+                     dtype=torch.uint8, device="cuda")
+    xa = torch.empty_like(x0)
+    xb = torch.empty_like(x0)
+
+    def layer_call(s, x_in, x_out, taps=None):
+        w = sets[s]
+        B.a8w8_layer_linears(x_in, w["gin"], w["gpost"], cfg.eps, w["qkv"], w["o"], w["gate"],
+                             w["up"], w["down"], x_out, ws, cfg.n_q_heads, cfg.n_kv_heads,
+                             cfg.head_dim, split_k=cfg.split_k, taps=taps)
+
+    def step(i, taps_fn=None):
+        # One step = one layer (config 2, weight set i mod sets) or the whole 40-layer
+        # stack (config 3).  Every step starts from the same input x0.
+        if cfg.kind == "stack":
+            src, dst = x0, xa
+            for l in range(layers):
+                layer_call(l, src, dst, taps_fn(l) if taps_fn else None)
+                src, dst = dst, (xb if dst is xa else xa)
+        else:
+            layer_call(i % nsets, x0, xa, taps_fn(0) if taps_fn else None)
+
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    layers_per_step = layers
+    us_per_layer = ms_per_step * 1e3 / layers_per_step
+    gbs = wbytes_layer * layers_per_step / (ms_per_step * 1e-3) / 1e9
+
+    # Roofline of the dominant kernel: HIP events recorded by the library right before
+    # and after the Gate/Up GEMM launch, on the same stream.
+    n_ev = min(args.steps, 100)
+    evs = []
+    stream = torch.cuda.current_stream()
+    for _ in range(n_ev * layers_per_step):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    it = iter(evs)
+
+    def taps_fn(_l):
+        a, b = next(it)
+        return {"mlp": {"ev_start": a.cuda_event, "ev_stop": b.cuda_event,
+                        "ev_kernel": GATEUP_KERNEL}}
+    for i in range(n_ev):
+        step(i, taps_fn)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    gu_bytes = 2 * I * H + 2 * I * 4 + M * H + M * 4 + M * I * 4   # weights, scales, q_x, s_x, h
+    achieved = gu_bytes / (k_ms * 1e-3) / 1e9
+    traffic = measured_traffic(gu_bytes)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "decode_gemm_kernel<EPI_SILU> (Gate/Up)", "kernel_us": round(k_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": gu_bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth.CONFIGS[2], args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic (seeded PCG64, Qwen3-14B shapes, random INT8 weights)",
+        "us_per_layer": round(us_per_layer, 2),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "config": {"workload": cfg.name, "M": M, "hidden": H, "intermediate": I,
+                   "n_qkv": n_qkv, "split_k": cfg.split_k, "layers_per_step": layers_per_step,
+                   "weight_sets": nsets, "int8_weight_bytes_per_layer": wbytes_layer,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+/*
+ * a8w8.h -- C ABI of liba8w8: the A8W8 decode-step linears of a Qwen3-14B-shaped
+ * transformer layer on MI355X (gfx950).
+ *
+ * What is computed (sources: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode
+ * scheduling and data paths", sections What changed > Decode scheduling and > Gate/Up
+ * INT8 path, Validation, and its CodeRabbit walkthrough table; pypto-serving PR #48
+ * "Add native Qwen3 14B A8W8 serving path", CodeRabbit comment on _hf_linear_to_bf16
+ * and the PR body section Compatibility and boundaries):
+ *
+ *   RMSNorm -> per-row dynamic INT8 quantization (FP32 row scale) -> INT8 x INT8 ->
+ *   INT32 GEMM against INT8 weights with per-output-channel FP32 scales -> dequant
+ *   (activation-row scale, then weight-channel scale) -> SiLU(gate) * up -> per-row
+ *   requantization -> Down projection split along K into independent partitions, each
+ *   dequantized to an FP32 partial -> partials summed, BF16 residual added, narrowed
+ *   to BF16 with round-to-nearest-even.  QKV and O use the same quantize -> INT8 GEMM ->
+ *   dequant pattern.  A W8A16 prefill mode dequantizes INT8 weight tiles to BF16 for
+ *   BF16 matrix cores (PR #810, Gate/Up INT8 path: prefill keeps the shared INT8
+ *   weights by dequantizing each tile to BF16).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are caller-owned DEVICE memory on the current HIP device.
+ *     The library allocates nothing and keeps no pointer after a call returns.
+ *   - BF16 values travel as uint16_t bit patterns.  Tensors are row-major and dense
+ *     unless a leading dimension says otherwise.  Every pointer must be 16-byte aligned.
+ *   - Weights are [N_out, K_in] row-major INT8; the FP32 scale has one entry per output
+ *     channel (per row of the weight).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work;
+ *     buffers must stay alive until the stream has passed it.
+ *   - All arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and a status other than A8W8_OK is returned.  M == 0 is
+ *     a valid no-op.  No exception crosses the ABI and nothing aborts.  Values are not
+ *     checked: non-finite inputs give unspecified outputs.  Kernel faults surface at
+ *     the caller's next synchronization, as for any HIP kernel.
+ *   - No output may alias an input except where stated.
+ */
+#ifndef A8W8_H
+#define A8W8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum a8w8_status {
+  A8W8_OK = 0,
+  A8W8_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  A8W8_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, or not
+                               a multiple the kernels need                          */
+  A8W8_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                     */
+  A8W8_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than a8w8_workspace_bytes  */
+  A8W8_ERR_UNSUPPORTED = 5, /* valid request this build does not implement          */
+  A8W8_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed           */
+} a8w8_status;
+
+typedef enum a8w8_mode {
+  A8W8_MODE_DECODE_A8W8 = 0,   /* INT8 activations x INT8 weights, INT32 accumulate */
+  A8W8_MODE_PREFILL_W8A16 = 1  /* BF16 activations x BF16-dequantized weight tiles  */
+} a8w8_mode;
+
+typedef enum a8w8_op {
+  A8W8_OP_MLP_BLOCK = 0,
+  A8W8_OP_LAYER_LINEARS = 1
+} a8w8_op;
+
+/* One quantized weight: w [N_out, K_in] INT8, scale [N_out] FP32. */
+typedef struct a8w8_qweight {
+  const int8_t* w;
+  const float* scale;
+} a8w8_qweight;
+
+/*
+ * Diagnostic taps of the MLP block.  Every member may be NULL; a non-NULL device
+ * pointer receives that intermediate (written in addition to the normal work).  Sizes
+ * use the call's M, H (hidden), I (intermediate) and split_k.
+ *
+ * Decode mode:
+ *   xn [M,H] FP32 RMSNorm output; q_x [M,H] INT8 codes; s_x [M] row scales;
+ *   acc_gate, acc_up [M,I] INT32; h [M,I] FP32 = silu(g)*u; q_h [M,I] INT8; s_h [M];
+ *   acc_down [split_k,M,H] INT32 per K partition; p_down [split_k,M,H] FP32 partials.
+ * Prefill mode:
+ *   xn [M,H] FP32; a_bf16 [M,H] BF16 activations; g, u [M,I] FP32 accumulators;
+ *   h_bf16 [M,I] BF16; d [M,H] FP32 Down accumulator (before the residual).
+ *
+ * Timing hook: when ev_start and ev_stop are non-NULL hipEvent_t handles, the call
+ * records ev_start right before and ev_stop right after launching its kernel number
+ * ev_kernel (0-based, in launch order; see each entry point), on `stream`.
+ */
+typedef struct a8w8_mlp_taps {
+  float* xn;
+  int8_t* q_x;
+  float* s_x;
+  int32_t* acc_gate;
+  int32_t* acc_up;
+  float* h;
+  int8_t* q_h;
+  float* s_h;
+  int32_t* acc_down;
+  float* p_down;
+  uint16_t* a_bf16;
+  float* g;
+  float* u;
+  uint16_t* h_bf16;
+  float* d;
+  void* ev_start;
+  void* ev_stop;
+  int ev_kernel;
+} a8w8_mlp_taps;
+
+/*
+ * Diagnostic taps of the layer linears (decode).  Same rules as a8w8_mlp_taps.
+ *   xn_in [M,H] FP32; q_in [M,H]; s_in [M]; acc_qkv [M,n_qkv] INT32;
+ *   qkv [M,n_qkv] BF16; q_attn [M,n_q*head_dim]; s_attn [M]; acc_o [M,H] INT32;
+ *   h1 [M,H] BF16 (attention-block output = MLP input and residual); mlp = MLP taps.
+ * Kernel numbers for the timing hook run 0..3 for the attention side, then the MLP
+ * block's kernels follow with their own numbering plus 4.
+ */
+typedef struct a8w8_layer_taps {
+  float* xn_in;
+  int8_t* q_in;
+  float* s_in;
+  int32_t* acc_qkv;
+  uint16_t* qkv;
+  int8_t* q_attn;
+  float* s_attn;
+  int32_t* acc_o;
+  uint16_t* h1;
+  a8w8_mlp_taps mlp;
+} a8w8_layer_taps;
+
+/*
+ * Per-row dynamic INT8 quantization of BF16 rows, optionally after RMSNorm.
+ *   x_bf16 [M, ldx] BF16 (row stride ldx elements, ldx >= K, ldx % 8 == 0);
+ *   gamma_bf16 [K] BF16 RMSNorm gain, or NULL for no norm (eps is then ignored);
+ *   q_out [M, K] INT8 codes; row_scale_out [M] FP32; xn_tap [M, K] FP32 or NULL.
+ * Per row: v = RMSNorm(x) (or x); a = max|v|; s = a/127; q = clamp(rint(v/s), -127,
+ * 127) with ties to even; s == 0 gives all-zero codes.  K > 0, K % 8 == 0.
+ * (PR #810 What changed: activation quantization once per row, batched over all
+ * decode rows.)  One kernel (number 0).
+ */
+a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx,
+                               const uint16_t* gamma_bf16, float eps, int64_t M,
+                               int64_t K, int8_t* q_out, float* row_scale_out,
+                               float* xn_tap, void* stream);
+
+/*
+ * One A8W8 linear on already-quantized rows.
+ *   q [M, K] INT8 codes, row_scale [M] FP32, W = {w [N, K] INT8, scale [N] FP32};
+ *   residual_bf16 [M, N] BF16 or NULL; y_bf16 [M, N] BF16 output;
+ *   acc_i32_tap [M, N] INT32 or NULL.
+ * y = rne_bf16((f32(acc) * row_scale[m]) * scale[n] [+ residual]).
+ * K % 64 == 0, 0 < K <= 131072 (INT32 accumulators cannot overflow), N % 16 == 0.
+ * y may alias residual_bf16.  One kernel (number 0).
+ */
+a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
+                        const uint16_t* residual_bf16, int64_t M, int64_t N,
+                        int64_t K, uint16_t* y_bf16, int32_t* acc_i32_tap,
+                        void* stream);
+
+/*
+ * Workspace size in bytes for a8w8_mlp_block (op = A8W8_OP_MLP_BLOCK, n_qkv ignored)
+ * or a8w8_layer_linears (op = A8W8_OP_LAYER_LINEARS).  Returns 0 for invalid
+ * arguments.  The workspace must be zero-filled before its first use (e.g. allocated
+ * with torch.zeros); every call returns its accumulator and counter region to zero,
+ * so a workspace can be reused by later calls of any size it fits.  Calls that share
+ * a workspace must not overlap in time.
+ */
+size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
+                            int split_k, int mode);
+
+/*
+ * The MLP block of one layer.
+ *   x_bf16 [M, H] BF16 input; gamma_bf16 [H] post-attention RMSNorm gain; eps;
+ *   gate, up: W [I, H]; down: W [H, I]; residual_bf16 [M, H]; out_bf16 [M, H].
+ *   split_k in {1, 2, 4, 8}: Down is computed in split_k contiguous K partitions of
+ *   I/split_k, each dequantized to its own FP32 partial (PR #810 What changed >
+ *   Decode scheduling and the CodeRabbit walkthrough row on the split Down
+ *   projection); out = rne_bf16((p_0 + p_1 + ...) + residual).
+ *   mode: A8W8_MODE_DECODE_A8W8 or A8W8_MODE_PREFILL_W8A16 (prefill ignores split_k
+ *   for its numerics: Down is one FP32-accumulated sum).
+ *   workspace: ws_bytes >= a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, ...), zero-filled
+ *   before first use.  taps: a8w8_mlp_taps or NULL.
+ * Shapes: H % 64 == 0, I % (64 * split_k) == 0, H and I <= 131072.  out may alias
+ * residual_bf16 or x_bf16.
+ * Decode kernels: 0 RMSNorm+quant, 1 Gate/Up GEMM + SiLU*up, 2 requant, 3 split-K Down
+ * + residual + RNE.
+ */
+a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, float eps,
+                           a8w8_qweight gate, a8w8_qweight up, a8w8_qweight down,
+                           const uint16_t* residual_bf16, uint16_t* out_bf16, int64_t M,
+                           int64_t H, int64_t I, int split_k, int mode, void* workspace,
+                           size_t ws_bytes, const a8w8_mlp_taps* taps, void* stream);
+
+/*
+ * All linears of one decode layer, attention replaced by identity (decode mode).
+ *   x_bf16 [M, H]; gamma_in, gamma_post [H]; qkv: W [n_qkv, H] with
+ *   n_qkv = (n_q_heads + 2 * n_kv_heads) * head_dim and n_q_heads * head_dim == H;
+ *   o: W [H, H]; gate/up/down as in a8w8_mlp_block.
+ * Steps: RMSNorm(gamma_in) -> quant -> QKV -> qkv = rne_bf16(dequant) -> the Q slice
+ * qkv[:, :H] stands in for the attention output -> quant -> O -> h1 = rne_bf16(dequant
+ * + x) -> MLP block with input h1 and residual h1.
+ *   qkv_out_bf16 [M, n_qkv] receives qkv, or NULL to keep it in the workspace;
+ *   out_bf16 [M, H]; workspace from a8w8_workspace_bytes(A8W8_OP_LAYER_LINEARS, ...).
+ * out may alias x_bf16.  Kernels: 0 RMSNorm+quant, 1 QKV GEMM, 2 quant, 3 O GEMM +
+ * residual, then 4.. the MLP block's kernels.
+ */
+a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                               const uint16_t* gamma_post_bf16, float eps,
+                               a8w8_qweight qkv, a8w8_qweight o, a8w8_qweight gate,
+                               a8w8_qweight up, a8w8_qweight down, int64_t M, int64_t H,
+                               int64_t I, int n_q_heads, int n_kv_heads, int head_dim,
+                               int split_k, uint16_t* qkv_out_bf16, uint16_t* out_bf16,
+                               void* workspace, size_t ws_bytes,
+                               const a8w8_layer_taps* taps, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* a8w8_status_string(a8w8_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int a8w8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* A8W8_H */

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every function
+that include/a8w8.h declares, and rejects invalid arguments before touching the GPU.
+
+Validation runs on the host before any HIP call, so these calls are safe without a
+device: every one of them must return an error status (or OK for an empty batch)
+without enqueueing anything.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from w8a8_quantized_decode_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "a8w8.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from w8a8_quantized_decode_amd import build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(a8w8_[a-z0-9_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"a8w8_quantize_rows", "a8w8_linear", "a8w8_mlp_block", "a8w8_layer_linears",
+            "a8w8_workspace_bytes", "a8w8_status_string", "a8w8_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in B.STATUS_NAMES.items():
+        assert B.status_string(code).startswith(name)
+    assert B.status_string(99) == "A8W8_ERR_UNKNOWN"
+    assert B.a8w8_version() >= 100
+
+
+def test_workspace_bytes(L):
+    ws = B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 1, 5120, 17408, 0, 2)
+    # at least q_x, h (FP32), q_h
+    assert ws >= 5120 + 17408 * 4 + 17408
+    ws_layer = B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 1, 5120, 17408, 7168, 2)
+    assert ws_layer > ws
+    assert B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 16, 5120, 17408, 0, 2) > ws
+    # invalid: split not in {1,2,4,8}, I not a multiple of 64*split, bad op, bad mode
+    assert B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 1, 5120, 17408, 0, 3) == 0
+    assert B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 1, 5120, 17408 + 64, 0, 2) == 0
+    assert B.a8w8_workspace_bytes(7, 1, 5120, 17408, 0, 2) == 0
+    assert B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 1, 5120, 17408, 0, 2, 9) == 0
+    assert B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 1, 5120, 17408, 7160, 2) == 0
+
+
+FAKE = 0x10000000  # 16-byte aligned, never dereferenced: validation fails first
+MIS = FAKE + 4
+QW = B.QWeight(FAKE, FAKE)
+
+
+def test_quantize_rows_validation(L):
+    f = L.a8w8_quantize_rows
+    assert f(FAKE, 64, None, 1e-6, 0, 64, FAKE, FAKE, None, None) == 0         # M == 0
+    assert f(FAKE, 64, None, 1e-6, 2, 60, FAKE, FAKE, None, None) == 2         # K % 8
+    assert f(FAKE, 32, None, 1e-6, 2, 64, FAKE, FAKE, None, None) == 2         # ldx < K
+    assert f(FAKE, 64, None, 1e-6, -1, 64, FAKE, FAKE, None, None) == 2        # M < 0
+    assert f(None, 64, None, 1e-6, 2, 64, FAKE, FAKE, None, None) == 1         # x NULL
+    assert f(FAKE, 64, None, 1e-6, 2, 64, None, FAKE, None, None) == 1         # q NULL
+    assert f(MIS, 64, None, 1e-6, 2, 64, FAKE, FAKE, None, None) == 3          # misaligned
+    assert f(FAKE, 64, MIS, 1e-6, 2, 64, FAKE, FAKE, None, None) == 3          # gamma misaligned
+
+
+def test_linear_validation(L):
+    f = L.a8w8_linear
+    assert f(FAKE, FAKE, QW, None, 0, 16, 64, FAKE, None, None) == 0            # M == 0
+    assert f(FAKE, FAKE, QW, None, 1, 16, 100, FAKE, None, None) == 2           # K % 64
+    assert f(FAKE, FAKE, QW, None, 1, 24, 64, FAKE, None, None) == 2            # N % 16
+    assert f(FAKE, FAKE, QW, None, 1, 16, 131072 + 64, FAKE, None, None) == 2   # K too large
+    assert f(FAKE, FAKE, B.QWeight(FAKE, None), None, 1, 16, 64, FAKE, None, None) == 1
+    assert f(FAKE, FAKE, QW, None, 1, 16, 64, None, None, None) == 1
+    assert f(FAKE, FAKE, B.QWeight(MIS, FAKE), None, 1, 16, 64, FAKE, None, None) == 3
+    assert f(FAKE, FAKE, QW, MIS, 1, 16, 64, FAKE, None, None) == 3
+
+
+def test_mlp_block_validation(L):
+    f = L.a8w8_mlp_block
+    ws = B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 1, 256, 768, 0, 2)
+
+    def call(M=1, H=256, I=768, split=2, mode=0, wsp=FAKE, wsb=ws, x=FAKE, gate=QW):
+        return f(x, FAKE, 1e-6, gate, QW, QW, FAKE, FAKE, M, H, I, split, mode, wsp, wsb,
+                 None, None)
+    assert call(M=0) == 0
+    assert call(H=200) == 2
+    assert call(I=768 + 64) == 2            # I % (64 * split_k)
+    assert call(split=3) == 2
+    assert call(mode=5) == 2
+    assert call(x=None) == 1
+    assert call(gate=B.QWeight(None, FAKE)) == 1
+    assert call(wsp=None) == 4
+    assert call(wsb=ws - 1) == 4
+    assert call(wsp=FAKE + 16) == 3          # workspace must be 256-byte aligned
+    assert call(x=MIS) == 3
+
+
+def test_layer_validation(L):
+    f = L.a8w8_layer_linears
+    ws = B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 1, 256, 768, 512, 2)
+
+    def call(M=1, H=256, nq=2, nkv=1, hd=128, wsb=ws):
+        return f(FAKE, FAKE, FAKE, 1e-6, QW, QW, QW, QW, QW, M, H, 768, nq, nkv, hd, 2, None,
+                 FAKE, FAKE, wsb, None, None)
+    assert call(M=0) == 0
+    assert call(nq=3) == 2                   # n_q * head_dim != H
+    assert call(hd=0) == 2
+    assert call(wsb=ws - 1) == 4
