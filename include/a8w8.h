@@ -65,11 +65,44 @@ typedef enum a8w8_op {
   A8W8_OP_LAYER_LINEARS = 1
 } a8w8_op;
 
-/* One quantized weight: w [N_out, K_in] INT8, scale [N_out] FP32. */
+/*
+ * Weight layouts.  ROWMAJOR: w[n * K + k].  TILED: the same bytes regrouped into
+ * 16-row tiles, one 1 KB block per 64-byte K step, each block in the operand order of
+ * the gfx950 INT8 matrix instruction (v_mfma_i32_16x16x64_i8):
+ *   tiled[(n / 16) * 16 * K + (k / 64) * 1024 + 16 * (n % 16 + 16 * ((k % 64) / 16))
+ *         + k % 16] = w[n * K + k].
+ * In the tiled layout every load instruction of the decode kernels reads 1 KB of
+ * consecutive bytes, which streams HBM faster than 64-byte pieces of 16 rows.  The
+ * serving loader converts checkpoint layouts once at load time (pypto-serving PR #48,
+ * loader walkthrough), which is where a8w8_pack_weight belongs.
+ */
+typedef enum a8w8_layout {
+  A8W8_LAYOUT_ROWMAJOR = 0,
+  A8W8_LAYOUT_TILED = 1
+} a8w8_layout;
+
+/* One quantized weight: w [N_out, K_in] INT8 in `layout`, scale [N_out] FP32. */
 typedef struct a8w8_qweight {
   const int8_t* w;
   const float* scale;
+  int layout; /* a8w8_layout */
 } a8w8_qweight;
+
+/*
+ * Kernel roles, for the timing hook (ev_kernel).  Which kernels a call launches depends
+ * on M: with M <= 4 rows the GEMMs quantize their inputs in their prologues (roles 1, 3,
+ * 5, 7 only); with more rows separate row-quantization kernels (0, 2, 4, 6) run first.
+ */
+typedef enum a8w8_kernel {
+  A8W8_KERNEL_QUANT_IN = 0,    /* RMSNorm(gamma_in) + quantization before QKV     */
+  A8W8_KERNEL_QKV = 1,
+  A8W8_KERNEL_QUANT_ATTN = 2,  /* quantization of the attention output before O  */
+  A8W8_KERNEL_O = 3,
+  A8W8_KERNEL_QUANT_POST = 4,  /* post-attention RMSNorm + quantization          */
+  A8W8_KERNEL_GATE_UP = 5,
+  A8W8_KERNEL_REQUANT = 6,     /* requantization of silu(g) * u before Down       */
+  A8W8_KERNEL_DOWN = 7
+} a8w8_kernel;
 
 /*
  * Diagnostic taps of the MLP block.  Every member may be NULL; a non-NULL device
@@ -85,8 +118,9 @@ typedef struct a8w8_qweight {
  *   h_bf16 [M,I] BF16; d [M,H] FP32 Down accumulator (before the residual).
  *
  * Timing hook: when ev_start and ev_stop are non-NULL hipEvent_t handles, the call
- * records ev_start right before and ev_stop right after launching its kernel number
- * ev_kernel (0-based, in launch order; see each entry point), on `stream`.
+ * records ev_start right before and ev_stop right after launching the kernel whose role
+ * (a8w8_kernel) is ev_kernel, on `stream`; nothing is recorded if the call launches no
+ * kernel of that role.
  */
 typedef struct a8w8_mlp_taps {
   float* xn;
@@ -114,8 +148,7 @@ typedef struct a8w8_mlp_taps {
  *   xn_in [M,H] FP32; q_in [M,H]; s_in [M]; acc_qkv [M,n_qkv] INT32;
  *   qkv [M,n_qkv] BF16; q_attn [M,n_q*head_dim]; s_attn [M]; acc_o [M,H] INT32;
  *   h1 [M,H] BF16 (attention-block output = MLP input and residual); mlp = MLP taps.
- * Kernel numbers for the timing hook run 0..3 for the attention side, then the MLP
- * block's kernels follow with their own numbering plus 4.
+ * The timing hook of a layer call lives in mlp.ev_start / mlp.ev_stop / mlp.ev_kernel.
  */
 typedef struct a8w8_layer_taps {
   float* xn_in;
@@ -131,6 +164,14 @@ typedef struct a8w8_layer_taps {
 } a8w8_layer_taps;
 
 /*
+ * Converts a row-major weight [N, K] into the tiled layout (see a8w8_layout) on the
+ * device.  N % 16 == 0, K % 64 == 0; w and w_tiled do not overlap.  One kernel.
+ * The scale vector is unchanged by the layout.
+ */
+a8w8_status a8w8_pack_weight(const int8_t* w, int64_t N, int64_t K, int8_t* w_tiled,
+                             void* stream);
+
+/*
  * Per-row dynamic INT8 quantization of BF16 rows, optionally after RMSNorm.
  *   x_bf16 [M, ldx] BF16 (row stride ldx elements, ldx >= K, ldx % 8 == 0);
  *   gamma_bf16 [K] BF16 RMSNorm gain, or NULL for no norm (eps is then ignored);
@@ -138,7 +179,7 @@ typedef struct a8w8_layer_taps {
  * Per row: v = RMSNorm(x) (or x); a = max|v|; s = a/127; q = clamp(rint(v/s), -127,
  * 127) with ties to even; s == 0 gives all-zero codes.  K > 0, K % 8 == 0.
  * (PR #810 What changed: activation quantization once per row, batched over all
- * decode rows.)  One kernel (number 0).
+ * decode rows.)  One kernel.
  */
 a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx,
                                const uint16_t* gamma_bf16, float eps, int64_t M,
@@ -152,7 +193,7 @@ a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx,
  *   acc_i32_tap [M, N] INT32 or NULL.
  * y = rne_bf16((f32(acc) * row_scale[m]) * scale[n] [+ residual]).
  * K % 64 == 0, 0 < K <= 131072 (INT32 accumulators cannot overflow), N % 16 == 0.
- * y may alias residual_bf16.  One kernel (number 0).
+ * y may alias residual_bf16.  One kernel.
  */
 a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
                         const uint16_t* residual_bf16, int64_t M, int64_t N,
@@ -162,10 +203,10 @@ a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
 /*
  * Workspace size in bytes for a8w8_mlp_block (op = A8W8_OP_MLP_BLOCK, n_qkv ignored)
  * or a8w8_layer_linears (op = A8W8_OP_LAYER_LINEARS).  Returns 0 for invalid
- * arguments.  The workspace must be zero-filled before its first use (e.g. allocated
- * with torch.zeros); every call returns its accumulator and counter region to zero,
- * so a workspace can be reused by later calls of any size it fits.  Calls that share
- * a workspace must not overlap in time.
+ * arguments.  The workspace is scratch: its contents on entry do not matter (each call
+ * clears the split-K accumulators it needs in its first kernel) and are unspecified
+ * on return.  A workspace can serve later calls of any size it fits; calls that share
+ * a workspace must not overlap in time.  The workspace must be 256-byte aligned.
  */
 size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
                             int split_k, int mode);
@@ -180,12 +221,11 @@ size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_q
  *   projection); out = rne_bf16((p_0 + p_1 + ...) + residual).
  *   mode: A8W8_MODE_DECODE_A8W8 or A8W8_MODE_PREFILL_W8A16 (prefill ignores split_k
  *   for its numerics: Down is one FP32-accumulated sum).
- *   workspace: ws_bytes >= a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, ...), zero-filled
- *   before first use.  taps: a8w8_mlp_taps or NULL.
+ *   workspace: ws_bytes >= a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, ...), 256-byte
+ *   aligned scratch.  taps: a8w8_mlp_taps or NULL.
  * Shapes: H % 64 == 0, I % (64 * split_k) == 0, H and I <= 131072.  out may alias
- * residual_bf16 or x_bf16.
- * Decode kernels: 0 RMSNorm+quant, 1 Gate/Up GEMM + SiLU*up, 2 requant, 3 split-K Down
- * + residual + RNE.
+ * residual_bf16 or x_bf16.  Prefill mode is not implemented in this build and returns
+ * A8W8_ERR_UNSUPPORTED.
  */
 a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, float eps,
                            a8w8_qweight gate, a8w8_qweight up, a8w8_qweight down,
@@ -203,8 +243,7 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
  * + x) -> MLP block with input h1 and residual h1.
  *   qkv_out_bf16 [M, n_qkv] receives qkv, or NULL to keep it in the workspace;
  *   out_bf16 [M, H]; workspace from a8w8_workspace_bytes(A8W8_OP_LAYER_LINEARS, ...).
- * out may alias x_bf16.  Kernels: 0 RMSNorm+quant, 1 QKV GEMM, 2 quant, 3 O GEMM +
- * residual, then 4.. the MLP block's kernels.
+ * out may alias x_bf16.
  */
 a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
                                const uint16_t* gamma_post_bf16, float eps,

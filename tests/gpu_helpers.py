@@ -43,6 +43,22 @@ def zeros(shape, dtype):
     return empty(shape, dtype).zero_()
 
 
+def dev_weight(w: np.ndarray, layout: int):
+    """Uploads an INT8 [N, K] weight; in the tiled layout it is regrouped on the device by
+    the library's own pack kernel (a layout change only, checked separately)."""
+    from w8a8_quantized_decode_amd import binding as B
+    t = dev(w)
+    if layout == B.LAYOUT_ROWMAJOR:
+        return t
+    out = torch().empty_like(t)
+    B.a8w8_pack_weight(t, out)
+    return out
+
+
+def qw(w: np.ndarray, s: np.ndarray, layout: int):
+    return (dev_weight(w, layout), dev(s), layout)
+
+
 def announce(msg: str) -> None:
     """Names the GPU case on stdout before it runs (so a failure names its case)."""
     print(f"[gpu-case] {msg}", flush=True)

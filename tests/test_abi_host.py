@@ -66,7 +66,7 @@ def test_workspace_bytes(L):
 
 FAKE = 0x10000000  # 16-byte aligned, never dereferenced: validation fails first
 MIS = FAKE + 4
-QW = B.QWeight(FAKE, FAKE)
+QW = B.QWeight(FAKE, FAKE, 0)
 
 
 def test_quantize_rows_validation(L):
@@ -81,15 +81,24 @@ def test_quantize_rows_validation(L):
     assert f(FAKE, 64, MIS, 1e-6, 2, 64, FAKE, FAKE, None, None) == 3          # gamma misaligned
 
 
+def test_pack_weight_validation(L):
+    f = L.a8w8_pack_weight
+    assert f(FAKE, 24, 64, FAKE, None) == 2          # N % 16
+    assert f(FAKE, 16, 100, FAKE, None) == 2         # K % 64
+    assert f(None, 16, 64, FAKE, None) == 1
+    assert f(FAKE, 16, 64, MIS, None) == 3
+
+
 def test_linear_validation(L):
     f = L.a8w8_linear
+    assert f(FAKE, FAKE, B.QWeight(FAKE, FAKE, 7), None, 1, 16, 64, FAKE, None, None) == 2
     assert f(FAKE, FAKE, QW, None, 0, 16, 64, FAKE, None, None) == 0            # M == 0
     assert f(FAKE, FAKE, QW, None, 1, 16, 100, FAKE, None, None) == 2           # K % 64
     assert f(FAKE, FAKE, QW, None, 1, 24, 64, FAKE, None, None) == 2            # N % 16
     assert f(FAKE, FAKE, QW, None, 1, 16, 131072 + 64, FAKE, None, None) == 2   # K too large
-    assert f(FAKE, FAKE, B.QWeight(FAKE, None), None, 1, 16, 64, FAKE, None, None) == 1
+    assert f(FAKE, FAKE, B.QWeight(FAKE, None, 0), None, 1, 16, 64, FAKE, None, None) == 1
     assert f(FAKE, FAKE, QW, None, 1, 16, 64, None, None, None) == 1
-    assert f(FAKE, FAKE, B.QWeight(MIS, FAKE), None, 1, 16, 64, FAKE, None, None) == 3
+    assert f(FAKE, FAKE, B.QWeight(MIS, FAKE, 0), None, 1, 16, 64, FAKE, None, None) == 3
     assert f(FAKE, FAKE, QW, MIS, 1, 16, 64, FAKE, None, None) == 3
 
 
@@ -106,7 +115,7 @@ def test_mlp_block_validation(L):
     assert call(split=3) == 2
     assert call(mode=5) == 2
     assert call(x=None) == 1
-    assert call(gate=B.QWeight(None, FAKE)) == 1
+    assert call(gate=B.QWeight(None, FAKE, 0)) == 1
     assert call(wsp=None) == 4
     assert call(wsb=ws - 1) == 4
     assert call(wsp=FAKE + 16) == 3          # workspace must be 256-byte aligned

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_helpers import announce, assert_bf16_close, dev, empty, host, ulp_diff_f32, zeros
+from tests.gpu_helpers import (announce, assert_bf16_close, dev, empty, host, qw, ulp_diff_f32,
+                               zeros)
 from w8a8_quantized_decode_amd import binding as B
 from w8a8_quantized_decode_amd import synth
 
@@ -22,10 +23,10 @@ pytestmark = pytest.mark.gpu
 C0, C1, C2 = synth.CONFIGS[0], synth.CONFIGS[1], synth.CONFIGS[2]
 
 
-def _mlp_dev(d):
+def _mlp_dev(d, layout=B.LAYOUT_ROWMAJOR):
     return dict(x=dev(d["x"]), gamma=dev(d["gamma_post"]), res=dev(d["res"]),
-                gate=(dev(d["w_gate"]), dev(d["s_gate"])), up=(dev(d["w_up"]), dev(d["s_up"])),
-                down=(dev(d["w_down"]), dev(d["s_down"])))
+                gate=qw(d["w_gate"], d["s_gate"], layout), up=qw(d["w_up"], d["s_up"], layout),
+                down=qw(d["w_down"], d["s_down"], layout))
 
 
 def _mlp_taps(M, H, I, split_k):
@@ -58,10 +59,10 @@ def _check_mlp_taps(t, st, split_k):
                                       st["p_down"][j].view(np.uint32))
 
 
-def run_mlp(cfg, M, split_k, layer=0, taps=True, ws=None):
+def run_mlp(cfg, M, split_k, layer=0, taps=True, ws=None, layout=B.LAYOUT_TILED):
     d = synth.mlp_inputs(cfg, layer=layer, M=M)
     H, I = cfg.H, cfg.I
-    g = _mlp_dev(d)
+    g = _mlp_dev(d, layout)
     out = empty((M, H), np.uint16)
     nbytes = B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, M, H, I, 0, split_k)
     if ws is None:
@@ -75,20 +76,22 @@ def run_mlp(cfg, M, split_k, layer=0, taps=True, ws=None):
     return host(out, np.uint16), want, t, st
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 33, 64, 65])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 33, 64, 65])
 @pytest.mark.parametrize("split_k", [1, 2, 4])
-def test_mlp_toy(M, split_k):
-    announce(f"mlp toy M={M} split_k={split_k}")
-    got, want, t, st = run_mlp(C0, M, split_k)
+@pytest.mark.parametrize("layout", [B.LAYOUT_ROWMAJOR, B.LAYOUT_TILED])
+def test_mlp_toy(M, split_k, layout):
+    announce(f"mlp toy M={M} split_k={split_k} layout={layout}")
+    got, want, t, st = run_mlp(C0, M, split_k, layout=layout)
     _check_mlp_taps(t, st, split_k)
     np.testing.assert_array_equal(got, want)
     assert_bf16_close(got, want)
 
 
-@pytest.mark.parametrize("M,split_k", [(1, 2), (16, 2), (1, 8), (4, 1)])
-def test_mlp_qwen3_14b(M, split_k):
-    announce(f"mlp qwen3-14b M={M} split_k={split_k}")
-    got, want, t, st = run_mlp(C1, M, split_k)
+@pytest.mark.parametrize("M,split_k,layout", [(1, 2, 1), (1, 2, 0), (16, 2, 1), (1, 8, 1),
+                                               (4, 1, 1), (5, 4, 0)])
+def test_mlp_qwen3_14b(M, split_k, layout):
+    announce(f"mlp qwen3-14b M={M} split_k={split_k} layout={layout}")
+    got, want, t, st = run_mlp(C1, M, split_k, layout=layout)
     _check_mlp_taps(t, st, split_k)
     np.testing.assert_array_equal(got, want)
     assert_bf16_close(got, want)
@@ -100,7 +103,7 @@ def test_mlp_deterministic_and_workspace_reuse():
     big = B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 16, cfg.H, cfg.I, 0, 2)
     ws = zeros((big,), np.uint8)
     d16 = synth.mlp_inputs(cfg, M=16)
-    g = _mlp_dev(d16)
+    g = _mlp_dev(d16, B.LAYOUT_TILED)
     outs = []
     for _ in range(5):
         out = empty((16, cfg.H), np.uint16)
@@ -109,18 +112,29 @@ def test_mlp_deterministic_and_workspace_reuse():
         outs.append(host(out, np.uint16))
     for o in outs[1:]:
         np.testing.assert_array_equal(o, outs[0])
-    # the same workspace then serves a smaller call: accumulators were left at zero
+    # the same workspace then serves a smaller call (its first kernel clears the
+    # split-K accumulators at their new offsets)
     got, want, _, _ = run_mlp(cfg, 1, 2, ws=ws, taps=False)
     np.testing.assert_array_equal(got, want)
     tail = host(ws)
     assert tail.size == big
 
 
+def test_mlp_workspace_contents_do_not_matter():
+    announce("mlp garbage-filled workspace")
+    cfg, M = C1, 3
+    nbytes = B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, M, cfg.H, cfg.I, 0, 2)
+    ws = zeros((nbytes,), np.uint8)
+    ws.fill_(0xA5)
+    got, want, _, _ = run_mlp(cfg, M, 2, ws=ws, taps=False)
+    np.testing.assert_array_equal(got, want)
+
+
 def test_mlp_out_aliases_residual():
     announce("mlp out aliases residual")
     cfg, M = C0, 5
     d = synth.mlp_inputs(cfg, M=M)
-    g = _mlp_dev(d)
+    g = _mlp_dev(d, B.LAYOUT_TILED)
     ws = zeros((B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, M, cfg.H, cfg.I, 0, 2),), np.uint8)
     B.a8w8_mlp_block(g["x"], g["gamma"], cfg.eps, g["gate"], g["up"], g["down"], g["res"],
                      g["res"], ws, split_k=2)
@@ -129,15 +143,15 @@ def test_mlp_out_aliases_residual():
     np.testing.assert_array_equal(host(g["res"], np.uint16), want)
 
 
-def run_layer(cfg, M, layer=0, taps=True, x=None):
+def run_layer(cfg, M, layer=0, taps=True, x=None, layout=B.LAYOUT_TILED):
     d = synth.layer_inputs(cfg, layer=layer, M=M)
     if x is not None:
         d["x"] = x
     H, I, n_qkv = cfg.H, cfg.I, cfg.n_qkv
-    qkv = (dev(d["w_qkv"]), dev(d["s_qkv"]))
-    o = (dev(d["w_o"]), dev(d["s_o"]))
-    gate, up, down = ((dev(d["w_gate"]), dev(d["s_gate"])), (dev(d["w_up"]), dev(d["s_up"])),
-                      (dev(d["w_down"]), dev(d["s_down"])))
+    qkv = qw(d["w_qkv"], d["s_qkv"], layout)
+    o = qw(d["w_o"], d["s_o"], layout)
+    gate, up, down = (qw(d["w_gate"], d["s_gate"], layout), qw(d["w_up"], d["s_up"], layout),
+                      qw(d["w_down"], d["s_down"], layout))
     out = empty((M, H), np.uint16)
     qkv_out = empty((M, n_qkv), np.uint16)
     ws = zeros((B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, M, H, I, n_qkv, cfg.split_k),),
@@ -179,15 +193,16 @@ TOY_LAYER = synth.Config(0, "toy layer", 1, 256, 768, "layer", n_q_heads=2, n_kv
                          head_dim=128)
 
 
-@pytest.mark.parametrize("M", [1, 4, 16])
-def test_layer_toy(M):
-    announce(f"layer toy M={M}")
-    got, qkv, want, t, st = run_layer(TOY_LAYER, M)
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 16])
+@pytest.mark.parametrize("layout", [B.LAYOUT_ROWMAJOR, B.LAYOUT_TILED])
+def test_layer_toy(M, layout):
+    announce(f"layer toy M={M} layout={layout}")
+    got, qkv, want, t, st = run_layer(TOY_LAYER, M, layout=layout)
     _check_layer(got, qkv, want, t, st, TOY_LAYER.split_k)
 
 
-@pytest.mark.parametrize("M", [1, 16])
-def test_layer_qwen3_14b(M):
-    announce(f"layer qwen3-14b M={M}")
-    got, qkv, want, t, st = run_layer(C2, M)
+@pytest.mark.parametrize("M,layout", [(1, 1), (1, 0), (16, 1)])
+def test_layer_qwen3_14b(M, layout):
+    announce(f"layer qwen3-14b M={M} layout={layout}")
+    got, qkv, want, t, st = run_layer(C2, M, layout=layout)
     _check_layer(got, qkv, want, t, st, C2.split_k)

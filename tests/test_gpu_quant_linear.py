@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.gpu_helpers import announce, dev, empty, host, zeros
+from tests.gpu_helpers import announce, dev, dev_weight, empty, host, zeros
 from w8a8_quantized_decode_amd import binding as B
 from w8a8_quantized_decode_amd import synth
 
@@ -71,8 +71,9 @@ LINEAR_CASES = [(1, 16, 64), (1, 7168, 5120), (5, 48, 320), (16, 5120, 5120), (1
 
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)
 @pytest.mark.parametrize("with_res", [False, True])
-def test_linear(M, N, K, with_res):
-    announce(f"linear M={M} N={N} K={K} res={with_res}")
+@pytest.mark.parametrize("layout", [B.LAYOUT_ROWMAJOR, B.LAYOUT_TILED])
+def test_linear(M, N, K, with_res, layout):
+    announce(f"linear M={M} N={N} K={K} res={with_res} layout={layout}")
     rng = np.random.default_rng(M * 7919 + N * 31 + K)
     q = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
     w = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
@@ -82,10 +83,28 @@ def test_linear(M, N, K, with_res):
     y_want, acc_want = O.linear_decode(q, s_x, w, s_w, res)
     y = empty((M, N), np.uint16)
     acc = empty((M, N), np.int32)
-    B.a8w8_linear(dev(q), dev(s_x), dev(w), dev(s_w), y,
-                  residual=dev(res) if with_res else None, acc_tap=acc)
+    B.a8w8_linear(dev(q), dev(s_x), dev_weight(w, layout), dev(s_w), y,
+                  residual=dev(res) if with_res else None, acc_tap=acc, layout=layout)
     np.testing.assert_array_equal(host(acc), acc_want)
     np.testing.assert_array_equal(host(y, np.uint16), y_want)
+
+
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 320), (7168, 5120)])
+def test_pack_weight_layout(N, K):
+    """The tiled layout is the documented regrouping of the row-major bytes."""
+    announce(f"pack_weight N={N} K={K}")
+    rng = np.random.default_rng(N + K)
+    w = rng.integers(-128, 128, size=(N, K), dtype=np.int8)
+    t = dev(w)
+    out = dev(np.zeros_like(w))
+    B.a8w8_pack_weight(t, out)
+    got = host(out).reshape(-1)
+    n = np.arange(N)[:, None]
+    k = np.arange(K)[None, :]
+    pos = (n // 16) * 16 * K + (k // 64) * 1024 + 16 * ((n % 16) + 16 * ((k % 64) // 16)) + k % 16
+    want = np.empty(N * K, np.int8)
+    want[pos.ravel()] = w.ravel()
+    np.testing.assert_array_equal(got, want)
 
 
 def _rne_probe_values():

@@ -34,8 +34,14 @@ class A8W8Error(RuntimeError):
         super().__init__(f"{where}: {status_string(status)}")
 
 
+LAYOUT_ROWMAJOR = 0
+LAYOUT_TILED = 1
+KERNEL_QUANT_IN, KERNEL_QKV, KERNEL_QUANT_ATTN, KERNEL_O = 0, 1, 2, 3
+KERNEL_QUANT_POST, KERNEL_GATE_UP, KERNEL_REQUANT, KERNEL_DOWN = 4, 5, 6, 7
+
+
 class QWeight(ctypes.Structure):
-    _fields_ = [("w", _vp), ("scale", _vp)]
+    _fields_ = [("w", _vp), ("scale", _vp), ("layout", ctypes.c_int)]
 
 
 class MlpTaps(ctypes.Structure):
@@ -65,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.a8w8_status_string.argtypes = [ctypes.c_int]
         L.a8w8_version.restype = ctypes.c_int
         L.a8w8_version.argtypes = []
+        L.a8w8_pack_weight.restype = ctypes.c_int
+        L.a8w8_pack_weight.argtypes = [_vp, _c_i64, _c_i64, _vp, _vp]
         L.a8w8_quantize_rows.restype = ctypes.c_int
         L.a8w8_quantize_rows.argtypes = [_vp, _c_i64, _vp, ctypes.c_float, _c_i64, _c_i64,
                                          _vp, _vp, _vp, _vp]
@@ -117,8 +125,20 @@ def _stream(stream) -> Optional[int]:
     return torch.cuda.current_stream().cuda_stream
 
 
-def qweight(w, scale) -> QWeight:
-    return QWeight(_ptr(w), _ptr(scale))
+def qweight(w, scale, layout: int = LAYOUT_ROWMAJOR) -> QWeight:
+    return QWeight(_ptr(w), _ptr(scale), int(layout))
+
+
+def _qw(spec) -> QWeight:
+    """(w, scale) or (w, scale, layout) -> QWeight."""
+    return qweight(*spec)
+
+
+def a8w8_pack_weight(w, w_tiled, stream=None) -> None:
+    """w: [N, K] INT8 row-major device tensor -> w_tiled (same size) in the tiled layout."""
+    N, K = w.shape
+    st = lib().a8w8_pack_weight(_ptr(w), N, K, _ptr(w_tiled), _stream(stream))
+    _check(st, "a8w8_pack_weight")
 
 
 def _fill_taps(struct, taps: Optional[dict]):
@@ -146,11 +166,13 @@ def a8w8_quantize_rows(x, q_out, row_scale_out, gamma=None, eps: float = 1e-6,
 
 
 def a8w8_linear(q, row_scale, w, w_scale, y_out, residual=None, acc_tap=None,
-                stream=None) -> None:
+                layout: int = LAYOUT_ROWMAJOR, stream=None) -> None:
+    """w: [N, K] row-major, or its tiled form (same byte count) with layout=LAYOUT_TILED."""
     M, K = q.shape
-    N = w.shape[0]
-    st = lib().a8w8_linear(_ptr(q), _ptr(row_scale), qweight(w, w_scale), _ptr(residual), M, N,
-                           K, _ptr(y_out), _ptr(acc_tap), _stream(stream))
+    N = y_out.shape[1]
+    st = lib().a8w8_linear(_ptr(q), _ptr(row_scale), qweight(w, w_scale, layout),
+                           _ptr(residual), M, N, K, _ptr(y_out), _ptr(acc_tap),
+                           _stream(stream))
     _check(st, "a8w8_linear")
 
 
@@ -162,16 +184,16 @@ def a8w8_workspace_bytes(op: int, M: int, H: int, I: int, n_qkv: int = 0, split_
 def a8w8_mlp_block(x, gamma, eps, gate, up, down, residual, out, workspace, split_k: int = 2,
                    mode: int = MODE_DECODE_A8W8, taps: Optional[dict] = None,
                    stream=None) -> None:
-    """gate/up/down: (w, scale) pairs of device tensors; workspace: a uint8 device tensor."""
+    """gate/up/down: (w, scale[, layout]) device tensors; workspace: a uint8 device tensor."""
     M, H = x.shape
-    I = gate[0].shape[0]
+    I = gate[1].shape[0]
     t = None
     if taps:
         t = MlpTaps()
         t.ev_kernel = -1
         _fill_taps(t, taps)
-    st = lib().a8w8_mlp_block(_ptr(x), _ptr(gamma), float(eps), qweight(*gate), qweight(*up),
-                              qweight(*down), _ptr(residual), _ptr(out), M, H, I, int(split_k),
+    st = lib().a8w8_mlp_block(_ptr(x), _ptr(gamma), float(eps), _qw(gate), _qw(up),
+                              _qw(down), _ptr(residual), _ptr(out), M, H, I, int(split_k),
                               int(mode), _ptr(workspace), workspace.numel(),
                               ctypes.byref(t) if t is not None else None, _stream(stream))
     _check(st, "a8w8_mlp_block")
@@ -181,15 +203,14 @@ def a8w8_layer_linears(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out
                        n_q_heads: int, n_kv_heads: int, head_dim: int, split_k: int = 2,
                        qkv_out=None, taps: Optional[dict] = None, stream=None) -> None:
     M, H = x.shape
-    I = gate[0].shape[0]
+    I = gate[1].shape[0]
     t = None
     if taps:
         t = LayerTaps()
         t.mlp.ev_kernel = -1
         _fill_taps(t, taps)
     st = lib().a8w8_layer_linears(_ptr(x), _ptr(gamma_in), _ptr(gamma_post), float(eps),
-                                  qweight(*qkv), qweight(*o), qweight(*gate), qweight(*up),
-                                  qweight(*down), M, H, I, int(n_q_heads), int(n_kv_heads),
+                                  _qw(qkv), _qw(o), _qw(gate), _qw(up), _qw(down), M, H, I, int(n_q_heads), int(n_kv_heads),
                                   int(head_dim), int(split_k), _ptr(qkv_out), _ptr(out),
                                   _ptr(workspace), workspace.numel(),
                                   ctypes.byref(t) if t is not None else None, _stream(stream))

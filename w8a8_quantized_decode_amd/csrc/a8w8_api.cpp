@@ -1,9 +1,14 @@
 // C-ABI layer of liba8w8: argument validation, workspace carving and kernel launches.
 //
 // Every check runs on the host before anything is enqueued (the pages' serving path
-// validates its configuration before execution and guards the down-projection tiling
-// against silent truncation: pypto-serving PR #48 commit "support A8W8 online serving",
-// pypto-lib PR #810 CodeRabbit nitpick on the down-projection constants).
+// validates its configuration before execution, pypto-serving PR #48, commit "support
+// A8W8 online serving"; and the down-projection tiling is guarded against silent
+// truncation, pypto-lib PR #810, CodeRabbit nitpick on the down-projection constants).
+//
+// Launch chains.  With at most kFuseMaxRows rows every GEMM quantizes its own input in
+// its prologue, so a layer is four kernels (QKV, O, Gate/Up, Down) and the MLP block
+// two (Gate/Up, Down).  With more rows the per-row statistics would be re-derived by
+// too many workgroups, so separate row-quantization kernels run before each GEMM.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -40,13 +45,16 @@ struct Carver {
 
 bool valid_split(int s) { return s == 1 || s == 2 || s == 4 || s == 8; }
 
-// Records the caller's timing events around kernel number `k` of a call.
+// Records the caller's timing events around the kernel with role `kernel`.
 struct Timer {
   hipEvent_t start = nullptr, stop = nullptr;
   int kernel = -1;
   hipStream_t stream;
-  Timer(void* s, void* e, int k, hipStream_t st)
-      : start(static_cast<hipEvent_t>(s)), stop(static_cast<hipEvent_t>(e)), kernel(k), stream(st) {}
+  Timer(const a8w8_mlp_taps* t, hipStream_t st)
+      : start(t ? static_cast<hipEvent_t>(t->ev_start) : nullptr),
+        stop(t ? static_cast<hipEvent_t>(t->ev_stop) : nullptr),
+        kernel(t ? t->ev_kernel : -1),
+        stream(st) {}
   hipError_t before(int k) const {
     return (start && stop && k == kernel) ? hipEventRecord(start, stream) : hipSuccess;
   }
@@ -55,70 +63,85 @@ struct Timer {
   }
 };
 
-#define A8W8_HIP(call)                          \
-  do {                                          \
+#define A8W8_HIP(call)                             \
+  do {                                             \
     if ((call) != hipSuccess) return A8W8_ERR_HIP; \
   } while (0)
 
-// ------------------------------------------------------------------ MLP (decode)
-struct MlpBuffers {
-  int8_t* q_x;
-  float* s_x;
-  float* h;
-  int8_t* q_h;
-  float* s_h;
-  int32_t* acc_gu;
-  int32_t* cnt_gu;
-  int32_t* acc_d;
-  int32_t* cnt_d;
+// ------------------------------------------------------------------ plans & workspace
+struct ChainPlan {
+  bool fused;
+  DecodeGemmPlan qkv, o, gu, dn;
 };
 
-MlpBuffers carve_mlp(Carver& c, int64_t M, int64_t H, int64_t I, int split_k) {
-  MlpBuffers b{};
-  const DecodeGemmPlan gu = plan_decode_gemm(EPI_SILU, M, I, H, 1, true);
-  const DecodeGemmPlan dn = plan_decode_gemm(EPI_DOWN, M, H, I, split_k, true);
-  b.q_x = c.take<int8_t>(size_t(M) * H);
-  b.s_x = c.take<float>(size_t(M));
-  b.h = c.take<float>(size_t(M) * I);
-  b.q_h = c.take<int8_t>(size_t(M) * I);
-  b.s_h = c.take<float>(size_t(M));
-  b.acc_gu = c.take<int32_t>(gu.acc_elems);
-  b.cnt_gu = c.take<int32_t>(gu.cnt_elems);
-  b.acc_d = c.take<int32_t>(dn.acc_elems);
-  b.cnt_d = c.take<int32_t>(dn.cnt_elems);
-  return b;
+ChainPlan make_plan(int64_t M, int64_t H, int64_t I, int64_t n_qkv, int split_k, bool layer) {
+  ChainPlan c{};
+  c.fused = M <= kFuseMaxRows;
+  // The call's first GEMM keeps its K range in one workgroup when it is also the first
+  // kernel (nothing before it could clear its accumulators).
+  if (layer) {
+    c.qkv = plan_decode_gemm(EPI_BF16, M, n_qkv, H, 1, c.fused);
+    c.o = plan_decode_gemm(EPI_BF16_RES, M, H, H, 1, false);
+    c.gu = plan_decode_gemm(EPI_SILU, M, I, H, 1, false);
+  } else {
+    c.gu = plan_decode_gemm(EPI_SILU, M, I, H, 1, c.fused);
+  }
+  c.dn = plan_decode_gemm(EPI_DOWN, M, H, I, split_k, false);
+  return c;
 }
 
-struct LayerBuffers {
+// Layout: one contiguous block of split-K accumulators and arrival counters (cleared by
+// the call's first kernel), then the intermediate activations.
+struct Buffers {
+  void* zero_ptr;
+  size_t zero_bytes;
+  int32_t *cnt_qkv, *cnt_o, *cnt_gu, *cnt_d;
+  int32_t *acc_qkv, *acc_o, *acc_gu, *acc_d;
   int8_t* q_in;
   float* s_in;
   uint16_t* qkv;
   int8_t* q_a;
   float* s_a;
   uint16_t* h1;
-  int32_t* acc_qkv;
-  int32_t* cnt_qkv;
-  int32_t* acc_o;
-  int32_t* cnt_o;
-  MlpBuffers mlp;
+  int8_t* q_x;
+  float* s_x;
+  float* h;
+  float* pmax;
+  int8_t* q_h;
+  float* s_h;
 };
 
-LayerBuffers carve_layer(Carver& c, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
-                         int split_k) {
-  LayerBuffers b{};
-  const DecodeGemmPlan pq = plan_decode_gemm(EPI_BF16, M, n_qkv, H, 1, true);
-  const DecodeGemmPlan po = plan_decode_gemm(EPI_BF16_RES, M, H, H, 1, true);
-  b.q_in = c.take<int8_t>(size_t(M) * H);
-  b.s_in = c.take<float>(size_t(M));
-  b.qkv = c.take<uint16_t>(size_t(M) * n_qkv);
-  b.q_a = c.take<int8_t>(size_t(M) * H);
-  b.s_a = c.take<float>(size_t(M));
-  b.h1 = c.take<uint16_t>(size_t(M) * H);
-  b.acc_qkv = c.take<int32_t>(pq.acc_elems);
-  b.cnt_qkv = c.take<int32_t>(pq.cnt_elems);
-  b.acc_o = c.take<int32_t>(po.acc_elems);
-  b.cnt_o = c.take<int32_t>(po.cnt_elems);
-  b.mlp = carve_mlp(c, M, H, I, split_k);
+Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
+              bool layer) {
+  Buffers b{};
+  b.cnt_qkv = c.take<int32_t>(pl.qkv.cnt_elems);
+  b.cnt_o = c.take<int32_t>(pl.o.cnt_elems);
+  b.cnt_gu = c.take<int32_t>(pl.gu.cnt_elems);
+  b.cnt_d = c.take<int32_t>(pl.dn.cnt_elems);
+  b.acc_qkv = c.take<int32_t>(pl.qkv.acc_elems);
+  b.acc_o = c.take<int32_t>(pl.o.acc_elems);
+  b.acc_gu = c.take<int32_t>(pl.gu.acc_elems);
+  b.acc_d = c.take<int32_t>(pl.dn.acc_elems);
+  b.zero_ptr = c.base;
+  b.zero_bytes = c.size();
+  if (layer) {
+    if (!pl.fused) {
+      b.q_in = c.take<int8_t>(size_t(M) * H);
+      b.s_in = c.take<float>(size_t(M));
+      b.q_a = c.take<int8_t>(size_t(M) * H);
+      b.s_a = c.take<float>(size_t(M));
+    }
+    b.qkv = c.take<uint16_t>(size_t(M) * n_qkv);
+    b.h1 = c.take<uint16_t>(size_t(M) * H);
+  }
+  if (!pl.fused) {
+    b.q_x = c.take<int8_t>(size_t(M) * H);
+    b.s_x = c.take<float>(size_t(M));
+    b.q_h = c.take<int8_t>(size_t(M) * I);
+    b.s_h = c.take<float>(size_t(M));
+  }
+  b.h = c.take<float>(size_t(M) * I);
+  b.pmax = c.take<float>(size_t(I / 16) * M);
   return b;
 }
 
@@ -133,92 +156,102 @@ a8w8_status check_mlp_shapes(int64_t M, int64_t H, int64_t I, int split_k) {
 
 a8w8_status check_qweight(const a8w8_qweight& w) {
   if (!w.w || !w.scale) return A8W8_ERR_NULL;
+  if (w.layout != A8W8_LAYOUT_ROWMAJOR && w.layout != A8W8_LAYOUT_TILED) return A8W8_ERR_SHAPE;
   if (!aligned16(w.w) || !aligned16(w.scale)) return A8W8_ERR_ALIGN;
   return A8W8_OK;
 }
 
-// Enqueues the decode MLP chain; `kbase` offsets the kernel numbers for the timer.
+int layout_of(const a8w8_qweight& w) {
+  return w.layout == A8W8_LAYOUT_TILED ? LAYOUT_TILED : LAYOUT_ROWMAJOR;
+}
+
+DecodeGemmArgs gemm_args(int epi, const DecodeGemmPlan& pl, int64_t M, int64_t N, int64_t K,
+                         const a8w8_qweight& w) {
+  DecodeGemmArgs g{};
+  g.epi = epi;
+  g.layout = layout_of(w);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.parts = 1;
+  g.ranges = pl.ranges;
+  g.w0 = w.w;
+  g.sw0 = w.scale;
+  return g;
+}
+
+hipError_t quant_kernel(const void* x, int64_t ldx, int f32, const uint16_t* gamma, float eps,
+                        int64_t M, int64_t K, int8_t* q, float* s, float* xn_tap, int8_t* q_tap,
+                        float* s_tap, void* zero_ptr, size_t zero_bytes, hipStream_t st) {
+  QuantRowsArgs a{};
+  a.x = x;
+  a.ldx = ldx;
+  a.x_is_f32 = f32;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.M = M;
+  a.K = K;
+  a.q = q;
+  a.s = s;
+  a.xn_tap = xn_tap;
+  a.q_tap = q_tap;
+  a.s_tap = s_tap;
+  a.write_codes = 1;
+  a.zero_ptr = zero_ptr;
+  a.zero_bytes = zero_bytes;
+  return launch_quant_rows(a, st);
+}
+
+// Enqueues the decode MLP chain.  `zero` is set when this chain starts the call.
 a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
                            const a8w8_qweight& gate, const a8w8_qweight& up,
                            const a8w8_qweight& down, const uint16_t* res, uint16_t* out,
-                           int64_t M, int64_t H, int64_t I, int split_k,
-                           const MlpBuffers& b, const a8w8_mlp_taps* t, const Timer& tm,
-                           int kbase, hipStream_t st) {
-  // 0: RMSNorm + per-row quantization of x.
-  QuantRowsArgs q{};
-  q.x = x;
-  q.ldx = H;
-  q.gamma = gamma;
-  q.eps = eps;
-  q.M = M;
-  q.K = H;
-  q.q = b.q_x;
-  q.s = b.s_x;
-  q.xn_tap = t ? t->xn : nullptr;
-  q.q_tap = t ? t->q_x : nullptr;
-  q.s_tap = t ? t->s_x : nullptr;
-  q.write_codes = 1;
-  A8W8_HIP(tm.before(kbase + 0));
-  A8W8_HIP(launch_quant_rows(q, st));
-  A8W8_HIP(tm.after(kbase + 0));
+                           int64_t M, int64_t H, int64_t I, int split_k, const ChainPlan& pl,
+                           const Buffers& b, bool zero, const a8w8_mlp_taps* t,
+                           const Timer& tm, hipStream_t st) {
+  void* zp = zero ? b.zero_ptr : nullptr;
+  const size_t zb = zero ? b.zero_bytes : 0;
 
-  // 1: Gate/Up GEMM, dequant, SiLU(g) * u -> h (FP32).
-  const DecodeGemmPlan gu = plan_decode_gemm(EPI_SILU, M, I, H, 1, true);
-  DecodeGemmArgs g{};
-  g.epi = EPI_SILU;
-  g.a = b.q_x;
-  g.lda = H;
-  g.sa = b.s_x;
-  g.w0 = gate.w;
-  g.sw0 = gate.scale;
+  // Gate/Up GEMM (input RMSNorm + quantization fused or separate), SiLU(g) * u -> h.
+  DecodeGemmArgs g = gemm_args(EPI_SILU, pl.gu, M, I, H, gate);
   g.w1 = up.w;
   g.sw1 = up.scale;
-  g.M = M;
-  g.N = I;
-  g.K = H;
-  g.parts = 1;
-  g.ranges = gu.ranges;
   g.h = b.h;
   g.ldh = I;
+  g.pmax_out = b.pmax;
   g.wacc = b.acc_gu;
   g.wcnt = b.cnt_gu;
   g.tap_acc0 = t ? t->acc_gate : nullptr;
   g.tap_acc1 = t ? t->acc_up : nullptr;
-  A8W8_HIP(tm.before(kbase + 1));
+  g.tap_h = t ? t->h : nullptr;
+  if (pl.fused) {
+    g.prologue = PRO_QUANT_BF16;
+    g.x = x;
+    g.ldx = H;
+    g.gamma = gamma;
+    g.eps = eps;
+    g.tap_xn = t ? t->xn : nullptr;
+    g.tap_q = t ? t->q_x : nullptr;
+    g.tap_s = t ? t->s_x : nullptr;
+    g.zero_ptr = zp;
+    g.zero_bytes = zb;
+  } else {
+    A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_POST));
+    A8W8_HIP(quant_kernel(x, H, 0, gamma, eps, M, H, b.q_x, b.s_x, t ? t->xn : nullptr,
+                          t ? t->q_x : nullptr, t ? t->s_x : nullptr, zp, zb, st));
+    A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_POST));
+    g.prologue = PRO_CODES;
+    g.a = b.q_x;
+    g.lda = H;
+    g.sa = b.s_x;
+  }
+  A8W8_HIP(tm.before(A8W8_KERNEL_GATE_UP));
   A8W8_HIP(launch_decode_gemm(g, st));
-  A8W8_HIP(tm.after(kbase + 1));
+  A8W8_HIP(tm.after(A8W8_KERNEL_GATE_UP));
 
-  // 2: per-row requantization of h over the full intermediate row.
-  QuantRowsArgs rq{};
-  rq.x = b.h;
-  rq.ldx = I;
-  rq.x_is_f32 = 1;
-  rq.M = M;
-  rq.K = I;
-  rq.q = b.q_h;
-  rq.s = b.s_h;
-  rq.xn_tap = t ? t->h : nullptr;
-  rq.q_tap = t ? t->q_h : nullptr;
-  rq.s_tap = t ? t->s_h : nullptr;
-  rq.write_codes = 1;
-  A8W8_HIP(tm.before(kbase + 2));
-  A8W8_HIP(launch_quant_rows(rq, st));
-  A8W8_HIP(tm.after(kbase + 2));
-
-  // 3: split-K Down, FP32 partials, + residual, RNE to BF16.
-  const DecodeGemmPlan dn = plan_decode_gemm(EPI_DOWN, M, H, I, split_k, true);
-  DecodeGemmArgs d{};
-  d.epi = EPI_DOWN;
-  d.a = b.q_h;
-  d.lda = I;
-  d.sa = b.s_h;
-  d.w0 = down.w;
-  d.sw0 = down.scale;
-  d.M = M;
-  d.N = H;
-  d.K = I;
+  // Down: per-row requantization of h, split-K partials, + residual, RNE to BF16.
+  DecodeGemmArgs d = gemm_args(EPI_DOWN, pl.dn, M, H, I, down);
   d.parts = split_k;
-  d.ranges = dn.ranges;
   d.out = out;
   d.ldo = H;
   d.res = res;
@@ -227,9 +260,27 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
   d.wcnt = b.cnt_d;
   d.tap_acc0 = t ? t->acc_down : nullptr;
   d.tap_p = t ? t->p_down : nullptr;
-  A8W8_HIP(tm.before(kbase + 3));
+  if (pl.fused) {
+    d.prologue = PRO_REQUANT_F32;
+    d.hin = b.h;
+    d.ldhin = I;
+    d.pmax = b.pmax;
+    d.npmax = static_cast<int>(I / 16);
+    d.tap_q = t ? t->q_h : nullptr;
+    d.tap_s = t ? t->s_h : nullptr;
+  } else {
+    A8W8_HIP(tm.before(A8W8_KERNEL_REQUANT));
+    A8W8_HIP(quant_kernel(b.h, I, 1, nullptr, 0.0f, M, I, b.q_h, b.s_h, nullptr,
+                          t ? t->q_h : nullptr, t ? t->s_h : nullptr, nullptr, 0, st));
+    A8W8_HIP(tm.after(A8W8_KERNEL_REQUANT));
+    d.prologue = PRO_CODES;
+    d.a = b.q_h;
+    d.lda = I;
+    d.sa = b.s_h;
+  }
+  A8W8_HIP(tm.before(A8W8_KERNEL_DOWN));
   A8W8_HIP(launch_decode_gemm(d, st));
-  A8W8_HIP(tm.after(kbase + 3));
+  A8W8_HIP(tm.after(A8W8_KERNEL_DOWN));
   return A8W8_OK;
 }
 
@@ -250,7 +301,16 @@ const char* a8w8_status_string(a8w8_status s) {
   return "A8W8_ERR_UNKNOWN";
 }
 
-int a8w8_version(void) { return 100; }
+int a8w8_version(void) { return 200; }
+
+a8w8_status a8w8_pack_weight(const int8_t* w, int64_t N, int64_t K, int8_t* w_tiled,
+                             void* stream) {
+  if (N <= 0 || K <= 0 || N % 16 || K % 64) return A8W8_ERR_SHAPE;
+  if (!w || !w_tiled) return A8W8_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_tiled)) return A8W8_ERR_ALIGN;
+  A8W8_HIP(launch_pack_tiled(w, N, K, w_tiled, static_cast<hipStream_t>(stream)));
+  return A8W8_OK;
+}
 
 a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx, const uint16_t* gamma_bf16,
                                float eps, int64_t M, int64_t K, int8_t* q_out,
@@ -262,18 +322,8 @@ a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx, const uint16
   if (!aligned16(x_bf16) || !aligned16(q_out) || !aligned16(row_scale_out) ||
       (gamma_bf16 && !aligned16(gamma_bf16)) || (xn_tap && !aligned16(xn_tap)))
     return A8W8_ERR_ALIGN;
-  QuantRowsArgs q{};
-  q.x = x_bf16;
-  q.ldx = ldx;
-  q.gamma = gamma_bf16;
-  q.eps = eps;
-  q.M = M;
-  q.K = K;
-  q.q = q_out;
-  q.s = row_scale_out;
-  q.xn_tap = xn_tap;
-  q.write_codes = 1;
-  A8W8_HIP(launch_quant_rows(q, static_cast<hipStream_t>(stream)));
+  A8W8_HIP(quant_kernel(x_bf16, ldx, 0, gamma_bf16, eps, M, K, q_out, row_scale_out, xn_tap,
+                        nullptr, nullptr, nullptr, 0, static_cast<hipStream_t>(stream)));
   return A8W8_OK;
 }
 
@@ -288,18 +338,13 @@ a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
   if (!aligned16(q) || !aligned16(row_scale) || !aligned16(y_bf16) ||
       (residual_bf16 && !aligned16(residual_bf16)) || (acc_i32_tap && !aligned16(acc_i32_tap)))
     return A8W8_ERR_ALIGN;
-  DecodeGemmArgs g{};
-  g.epi = residual_bf16 ? EPI_BF16_RES : EPI_BF16;
+  DecodeGemmPlan one{};
+  one.ranges = 1;
+  DecodeGemmArgs g = gemm_args(residual_bf16 ? EPI_BF16_RES : EPI_BF16, one, M, N, K, W);
+  g.prologue = PRO_CODES;
   g.a = q;
   g.lda = K;
   g.sa = row_scale;
-  g.w0 = W.w;
-  g.sw0 = W.scale;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.parts = 1;
-  g.ranges = 1;
   g.out = y_bf16;
   g.ldo = N;
   g.res = residual_bf16;
@@ -312,17 +357,20 @@ a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
 size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
                             int split_k, int mode) {
   if (check_mlp_shapes(M, H, I, split_k) != A8W8_OK) return 0;
-  if (mode != A8W8_MODE_DECODE_A8W8 && mode != A8W8_MODE_PREFILL_W8A16) return 0;
-  Carver c(nullptr);
+  if (mode != A8W8_MODE_DECODE_A8W8) return 0;
+  bool layer;
   if (op == A8W8_OP_MLP_BLOCK) {
-    if (mode != A8W8_MODE_DECODE_A8W8) return 0;
-    carve_mlp(c, M, H, I, split_k);
+    layer = false;
+    n_qkv = 0;
   } else if (op == A8W8_OP_LAYER_LINEARS) {
-    if (mode != A8W8_MODE_DECODE_A8W8 || n_qkv <= 0 || n_qkv % 16) return 0;
-    carve_layer(c, M, H, I, n_qkv, split_k);
+    if (n_qkv <= 0 || n_qkv % 16) return 0;
+    layer = true;
   } else {
     return 0;
   }
+  const ChainPlan pl = make_plan(M, H, I, n_qkv, split_k, layer);
+  Carver c(nullptr);
+  carve(c, pl, M, H, I, n_qkv, layer);
   return c.size() > 0 ? c.size() : kAlign;
 }
 
@@ -344,13 +392,13 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
   const size_t need = a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, M, H, I, 0, split_k, mode);
   if (!workspace || ws_bytes < need) return A8W8_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return A8W8_ERR_ALIGN;
+  const ChainPlan pl = make_plan(M, H, I, 0, split_k, false);
   Carver c(workspace);
-  const MlpBuffers b = carve_mlp(c, M, H, I, split_k);
+  const Buffers b = carve(c, pl, M, H, I, 0, false);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const Timer tm(taps ? taps->ev_start : nullptr, taps ? taps->ev_stop : nullptr,
-                 taps ? taps->ev_kernel : -1, st);
-  return run_mlp_decode(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M,
-                        H, I, split_k, b, taps, tm, 0, st);
+  const Timer tm(taps, st);
+  return run_mlp_decode(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M, H,
+                        I, split_k, pl, b, true, taps, tm, st);
 }
 
 a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
@@ -377,87 +425,53 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
                                            A8W8_MODE_DECODE_A8W8);
   if (!workspace || ws_bytes < need) return A8W8_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return A8W8_ERR_ALIGN;
+  const ChainPlan pl = make_plan(M, H, I, n_qkv, split_k, true);
   Carver c(workspace);
-  const LayerBuffers b = carve_layer(c, M, H, I, n_qkv, split_k);
+  const Buffers b = carve(c, pl, M, H, I, n_qkv, true);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const a8w8_mlp_taps* mt = taps ? &taps->mlp : nullptr;
-  const Timer tm(mt ? mt->ev_start : nullptr, mt ? mt->ev_stop : nullptr,
-                 mt ? mt->ev_kernel : -1, st);
+  const Timer tm(mt, st);
   uint16_t* qkv_buf = qkv_out_bf16 ? qkv_out_bf16 : b.qkv;
 
-  // 0: input RMSNorm + quantization.
-  QuantRowsArgs q{};
-  q.x = x_bf16;
-  q.ldx = H;
-  q.gamma = gamma_in_bf16;
-  q.eps = eps;
-  q.M = M;
-  q.K = H;
-  q.q = b.q_in;
-  q.s = b.s_in;
-  q.xn_tap = taps ? taps->xn_in : nullptr;
-  q.q_tap = taps ? taps->q_in : nullptr;
-  q.s_tap = taps ? taps->s_in : nullptr;
-  q.write_codes = 1;
-  A8W8_HIP(tm.before(0));
-  A8W8_HIP(launch_quant_rows(q, st));
-  A8W8_HIP(tm.after(0));
-
-  // 1: QKV projection -> BF16.
-  const DecodeGemmPlan pq = plan_decode_gemm(EPI_BF16, M, n_qkv, H, 1, true);
-  DecodeGemmArgs g{};
-  g.epi = EPI_BF16;
-  g.a = b.q_in;
-  g.lda = H;
-  g.sa = b.s_in;
-  g.w0 = qkv.w;
-  g.sw0 = qkv.scale;
-  g.M = M;
-  g.N = n_qkv;
-  g.K = H;
-  g.parts = 1;
-  g.ranges = pq.ranges;
+  // QKV projection (input RMSNorm + quantization fused or separate) -> BF16.
+  DecodeGemmArgs g = gemm_args(EPI_BF16, pl.qkv, M, n_qkv, H, qkv);
   g.out = qkv_buf;
   g.ldo = n_qkv;
   g.wacc = b.acc_qkv;
   g.wcnt = b.cnt_qkv;
   g.tap_acc0 = taps ? taps->acc_qkv : nullptr;
-  A8W8_HIP(tm.before(1));
+  if (pl.fused) {
+    g.prologue = PRO_QUANT_BF16;
+    g.x = x_bf16;
+    g.ldx = H;
+    g.gamma = gamma_in_bf16;
+    g.eps = eps;
+    g.tap_xn = taps ? taps->xn_in : nullptr;
+    g.tap_q = taps ? taps->q_in : nullptr;
+    g.tap_s = taps ? taps->s_in : nullptr;
+    g.zero_ptr = b.zero_ptr;
+    g.zero_bytes = b.zero_bytes;
+  } else {
+    A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_IN));
+    A8W8_HIP(quant_kernel(x_bf16, H, 0, gamma_in_bf16, eps, M, H, b.q_in, b.s_in,
+                          taps ? taps->xn_in : nullptr, taps ? taps->q_in : nullptr,
+                          taps ? taps->s_in : nullptr, b.zero_ptr, b.zero_bytes, st));
+    A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_IN));
+    g.prologue = PRO_CODES;
+    g.a = b.q_in;
+    g.lda = H;
+    g.sa = b.s_in;
+  }
+  A8W8_HIP(tm.before(A8W8_KERNEL_QKV));
   A8W8_HIP(launch_decode_gemm(g, st));
-  A8W8_HIP(tm.after(1));
+  A8W8_HIP(tm.after(A8W8_KERNEL_QKV));
   if (taps && taps->qkv)
     A8W8_HIP(hipMemcpyAsync(taps->qkv, qkv_buf, size_t(M) * n_qkv * sizeof(uint16_t),
                             hipMemcpyDeviceToDevice, st));
 
-  // 2: identity attention: quantize the Q slice qkv[:, :H].
-  QuantRowsArgs qa{};
-  qa.x = qkv_buf;
-  qa.ldx = n_qkv;
-  qa.M = M;
-  qa.K = H;
-  qa.q = b.q_a;
-  qa.s = b.s_a;
-  qa.q_tap = taps ? taps->q_attn : nullptr;
-  qa.s_tap = taps ? taps->s_attn : nullptr;
-  qa.write_codes = 1;
-  A8W8_HIP(tm.before(2));
-  A8W8_HIP(launch_quant_rows(qa, st));
-  A8W8_HIP(tm.after(2));
-
-  // 3: O projection + layer input as residual -> h1.
-  const DecodeGemmPlan po = plan_decode_gemm(EPI_BF16_RES, M, H, H, 1, true);
-  DecodeGemmArgs og{};
-  og.epi = EPI_BF16_RES;
-  og.a = b.q_a;
-  og.lda = H;
-  og.sa = b.s_a;
-  og.w0 = o.w;
-  og.sw0 = o.scale;
-  og.M = M;
-  og.N = H;
-  og.K = H;
-  og.parts = 1;
-  og.ranges = po.ranges;
+  // Identity attention: the Q slice qkv[:, :H] is quantized and fed to O; O adds the
+  // layer input as residual -> h1.
+  DecodeGemmArgs og = gemm_args(EPI_BF16_RES, pl.o, M, H, H, o);
   og.out = b.h1;
   og.ldo = H;
   og.res = x_bf16;
@@ -465,15 +479,32 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   og.wacc = b.acc_o;
   og.wcnt = b.cnt_o;
   og.tap_acc0 = taps ? taps->acc_o : nullptr;
-  A8W8_HIP(tm.before(3));
+  if (pl.fused) {
+    og.prologue = PRO_QUANT_BF16;
+    og.x = qkv_buf;
+    og.ldx = n_qkv;
+    og.tap_q = taps ? taps->q_attn : nullptr;
+    og.tap_s = taps ? taps->s_attn : nullptr;
+  } else {
+    A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_ATTN));
+    A8W8_HIP(quant_kernel(qkv_buf, n_qkv, 0, nullptr, 0.0f, M, H, b.q_a, b.s_a, nullptr,
+                          taps ? taps->q_attn : nullptr, taps ? taps->s_attn : nullptr, nullptr,
+                          0, st));
+    A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_ATTN));
+    og.prologue = PRO_CODES;
+    og.a = b.q_a;
+    og.lda = H;
+    og.sa = b.s_a;
+  }
+  A8W8_HIP(tm.before(A8W8_KERNEL_O));
   A8W8_HIP(launch_decode_gemm(og, st));
-  A8W8_HIP(tm.after(3));
+  A8W8_HIP(tm.after(A8W8_KERNEL_O));
   if (taps && taps->h1)
     A8W8_HIP(hipMemcpyAsync(taps->h1, b.h1, size_t(M) * H * sizeof(uint16_t),
                             hipMemcpyDeviceToDevice, st));
 
   return run_mlp_decode(b.h1, gamma_post_bf16, eps, gate, up, down, b.h1, out_bf16, M, H, I,
-                        split_k, b.mlp, mt, tm, 4, st);
+                        split_k, pl, b, false, mt, tm, st);
 }
 
 }  // extern "C"
