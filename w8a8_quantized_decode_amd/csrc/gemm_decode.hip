@@ -219,7 +219,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(DecodeGemmArgs 
   extern __shared__ __align__(16) int8_t act[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  // The wave index lives in a scalar register so that every loop bound below is
+  // wave-uniform: the MFMA guards must be real branches, since a matrix instruction
+  // does not honour a partial lane mask.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
   const int row16 = lane & 15, kg = lane >> 4;
   const int R = p.ranges;
   const int tile = blockIdx.x / R, r = blockIdx.x % R;
@@ -265,23 +269,45 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(DecodeGemmArgs 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[i][mb] = i32x4{0, 0, 0, 0};
 
-  i32x4 wcur[U][NMAT], bcur[U][MB];
+  // Batches of U steps, ping-ponged between two register sets so that the next batch
+  // is in flight while the current one feeds the matrix cores.  Loads are issued
+  // unconditionally (steps past the wave's range re-read its last step, an L2 hit) and
+  // the activation operand of those steps is zero, so the loop has no data-dependent
+  // branches and the compiler can wait for exactly the batch it consumes.
+  const int nsteps = ws1 - ws0;
+  const int nb = (nsteps + U - 1) / U;
   auto load_batch = [&](i32x4 (&wv)[U][NMAT], i32x4 (&bv)[U][MB], int t) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t + u < ws1) {
+    for (int u = 0; u < U; ++u) {
+      const int tt = min(t + u, ws1 - 1);
 #pragma unroll
-        for (int i = 0; i < NMAT; ++i) wv[u][i] = ld16(wbase[i] + int64_t(t + u) * kStep);
-        if (!kFused) {
+      for (int i = 0; i < NMAT; ++i) wv[u][i] = ld16(wbase[i] + int64_t(tt) * kStep);
+      if (!kFused) {
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const i32x4 v = ld16(abase[mb] + int64_t(t + u) * 64);
-            bv[u][mb] = aval[mb] ? v : i32x4{0, 0, 0, 0};
-          }
-        }
+        for (int mb = 0; mb < MB; ++mb) bv[u][mb] = ld16(abase[mb] + int64_t(tt) * 64);
       }
+    }
   };
-  if (ws0 < ws1) load_batch(wcur, bcur, ws0);
+  auto compute = [&](const i32x4 (&wv)[U][NMAT], const i32x4 (&bv)[U][MB], int t) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = t + u < ws1;
+      const int tt = min(t + u, ws1 - 1);
+      i32x4 b[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const i32x4 v = kFused ? *reinterpret_cast<const i32x4*>(abase[mb] + tt * 64) : bv[u][mb];
+        b[mb] = (live && aval[mb]) ? v : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = mfma_i8(wv[u][i], b[mb], acc[i][mb]);
+    }
+  };
+
+  i32x4 wA[U][NMAT], bA[U][MB], wB[U][NMAT], bB[U][MB];
+  if (nb > 0) load_batch(wA, bA, ws0);
 
   // Zero the accumulators of the call's later kernels (grid-stride, 16 bytes a store).
   if (p.zero_ptr) {
@@ -296,34 +322,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(DecodeGemmArgs 
   if (kFused)
     fused_prologue<NW, PRO>(p, sm, act, act_ld, P, Kp, rs0, ns, tile == 0);
 
-  for (int t = ws0; t < ws1; t += U) {
-    i32x4 wnxt[U][NMAT], bnxt[U][MB];
-    if (t + U < ws1) load_batch(wnxt, bnxt, t + U);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t + u < ws1) {
-        i32x4 b[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          if (kFused) {
-            const i32x4 v = *reinterpret_cast<const i32x4*>(abase[mb] + (t + u) * 64);
-            b[mb] = aval[mb] ? v : i32x4{0, 0, 0, 0};
-          } else {
-            b[mb] = bcur[u][mb];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[i][mb] = mfma_i8(wcur[u][i], b[mb], acc[i][mb]);
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int i = 0; i < NMAT; ++i) wcur[u][i] = wnxt[u][i];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) bcur[u][mb] = bnxt[u][mb];
-    }
+  for (int bi = 0; bi < nb; bi += 2) {
+    const int t = ws0 + bi * U;
+    load_batch(wB, bB, t + U);
+    compute(wA, bA, t);
+    if (bi + 1 >= nb) break;
+    load_batch(wA, bA, t + 2 * U);
+    compute(wB, bB, t + U);
   }
 
 #pragma unroll
