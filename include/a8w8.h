@@ -101,7 +101,8 @@ typedef enum a8w8_kernel {
   A8W8_KERNEL_QUANT_POST = 4,  /* post-attention RMSNorm + quantization          */
   A8W8_KERNEL_GATE_UP = 5,
   A8W8_KERNEL_REQUANT = 6,     /* requantization of silu(g) * u before Down       */
-  A8W8_KERNEL_DOWN = 7
+  A8W8_KERNEL_DOWN = 7,
+  A8W8_KERNEL_REDUCE = 8       /* prefill: Down partial sums + residual -> BF16    */
 } a8w8_kernel;
 
 /*
@@ -224,8 +225,13 @@ size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_q
  *   workspace: ws_bytes >= a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, ...), 256-byte
  *   aligned scratch.  taps: a8w8_mlp_taps or NULL.
  * Shapes: H % 64 == 0, I % (64 * split_k) == 0, H and I <= 131072.  out may alias
- * residual_bf16 or x_bf16.  Prefill mode is not implemented in this build and returns
- * A8W8_ERR_UNSUPPORTED.
+ * residual_bf16 or x_bf16.
+ * Prefill mode (any M; built for M in the hundreds): a = rne_bf16(RMSNorm(x)); every
+ * weight tile is dequantized to W' = rne_bf16(fl32(w * s)) on the fly; Gate/Up
+ * accumulate in FP32 on BF16 matrix cores; h = rne_bf16(silu(g) * u); Down accumulates
+ * in FP32 over 4 K splits whose FP32 partials are added in order; out =
+ * rne_bf16(d + residual).  Additionally needs I % 128 == 0 and H % 256 == 0.  Kernels:
+ * QUANT_POST (norm), GATE_UP, DOWN, REDUCE.
  */
 a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, float eps,
                            a8w8_qweight gate, a8w8_qweight up, a8w8_qweight down,

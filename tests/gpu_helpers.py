@@ -82,4 +82,6 @@ def assert_bf16_close(got_bits: np.ndarray, want_bits: np.ndarray, rtol=1e-2, at
     err = np.abs(g - w)
     ok = np.where(np.abs(w) < 1.0, err <= atol, err <= rtol * np.abs(w))
     bad = np.nonzero(~ok)
-    assert ok.all(), f"{bad[0].size} BF16 outputs out of tolerance, first at {[b[:5] for b in bad]}"
+    pairs = [(tuple(int(i) for i in idx), float(g[idx]), float(w[idx]))
+             for idx in list(zip(*bad))[:5]]
+    assert ok.all(), f"{bad[0].size} BF16 outputs out of tolerance: (index, got, want) {pairs}"

@@ -37,7 +37,7 @@ class A8W8Error(RuntimeError):
 LAYOUT_ROWMAJOR = 0
 LAYOUT_TILED = 1
 KERNEL_QUANT_IN, KERNEL_QKV, KERNEL_QUANT_ATTN, KERNEL_O = 0, 1, 2, 3
-KERNEL_QUANT_POST, KERNEL_GATE_UP, KERNEL_REQUANT, KERNEL_DOWN = 4, 5, 6, 7
+KERNEL_QUANT_POST, KERNEL_GATE_UP, KERNEL_REQUANT, KERNEL_DOWN, KERNEL_REDUCE = 4, 5, 6, 7, 8
 
 
 class QWeight(ctypes.Structure):

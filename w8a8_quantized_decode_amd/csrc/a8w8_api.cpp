@@ -180,6 +180,98 @@ DecodeGemmArgs gemm_args(int epi, const DecodeGemmPlan& pl, int64_t M, int64_t N
   return g;
 }
 
+// ------------------------------------------------------------------ prefill (W8A16)
+constexpr int kPrefillDownSplits = 4;
+
+struct PrefillBuffers {
+  uint16_t* a;     // [M, H] BF16 activations rne_bf16(RMSNorm(x))
+  uint16_t* h;     // [M, I] BF16 silu(g) * u
+  float* part;     // [splits, M, H] FP32 Down partial sums
+};
+
+PrefillBuffers carve_prefill(Carver& c, int64_t M, int64_t H, int64_t I) {
+  PrefillBuffers b{};
+  b.a = c.take<uint16_t>(size_t(M) * H);
+  b.h = c.take<uint16_t>(size_t(M) * I);
+  b.part = c.take<float>(size_t(kPrefillDownSplits) * M * H);
+  return b;
+}
+
+bool prefill_shapes_ok(int64_t H, int64_t I) {
+  return I % prefill_channels_per_wg(EPI_PF_SILU) == 0 &&
+         H % prefill_channels_per_wg(EPI_PF_PARTIAL) == 0 &&
+         (I / 64) >= kPrefillDownSplits;
+}
+
+a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
+                            const a8w8_qweight& gate, const a8w8_qweight& up,
+                            const a8w8_qweight& down, const uint16_t* res, uint16_t* out,
+                            int64_t M, int64_t H, int64_t I, const PrefillBuffers& b,
+                            const a8w8_mlp_taps* t, const Timer& tm, hipStream_t st) {
+  // RMSNorm, narrowed to BF16 (the MFMA operand type).
+  QuantRowsArgs q{};
+  q.x = x;
+  q.ldx = H;
+  q.gamma = gamma;
+  q.eps = eps;
+  q.M = M;
+  q.K = H;
+  q.xn_tap = t ? t->xn : nullptr;
+  q.a_bf16 = b.a;
+  q.a_bf16_tap = t ? t->a_bf16 : nullptr;
+  q.write_codes = 0;
+  A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_POST));
+  A8W8_HIP(launch_quant_rows(q, st));
+  A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_POST));
+
+  // Gate/Up on BF16-dequantized weight tiles, FP32 accumulate, h = rne_bf16(silu(g) * u).
+  PrefillGemmArgs g{};
+  g.epi = EPI_PF_SILU;
+  g.layout = layout_of(gate);
+  g.M = M;
+  g.N = I;
+  g.K = H;
+  g.splits = 1;
+  g.act = b.a;
+  g.lda = H;
+  g.w0 = gate.w;
+  g.sw0 = gate.scale;
+  g.w1 = up.w;
+  g.sw1 = up.scale;
+  g.out_bf16 = b.h;
+  g.ldo = I;
+  g.tap_g = t ? t->g : nullptr;
+  g.tap_u = t ? t->u : nullptr;
+  A8W8_HIP(tm.before(A8W8_KERNEL_GATE_UP));
+  A8W8_HIP(launch_prefill_gemm(g, st));
+  A8W8_HIP(tm.after(A8W8_KERNEL_GATE_UP));
+  if (t && t->h_bf16)
+    A8W8_HIP(hipMemcpyAsync(t->h_bf16, b.h, size_t(M) * I * sizeof(uint16_t),
+                            hipMemcpyDeviceToDevice, st));
+
+  // Down in K splits (FP32 partials), then partials + residual -> RNE BF16.
+  PrefillGemmArgs d{};
+  d.epi = EPI_PF_PARTIAL;
+  d.layout = layout_of(down);
+  d.M = M;
+  d.N = H;
+  d.K = I;
+  d.splits = kPrefillDownSplits;
+  d.act = b.h;
+  d.lda = I;
+  d.w0 = down.w;
+  d.sw0 = down.scale;
+  d.part = b.part;
+  A8W8_HIP(tm.before(A8W8_KERNEL_DOWN));
+  A8W8_HIP(launch_prefill_gemm(d, st));
+  A8W8_HIP(tm.after(A8W8_KERNEL_DOWN));
+  A8W8_HIP(tm.before(A8W8_KERNEL_REDUCE));
+  A8W8_HIP(launch_reduce_residual(b.part, kPrefillDownSplits, M, H, res, out, t ? t->d : nullptr,
+                                  st));
+  A8W8_HIP(tm.after(A8W8_KERNEL_REDUCE));
+  return A8W8_OK;
+}
+
 hipError_t quant_kernel(const void* x, int64_t ldx, int f32, const uint16_t* gamma, float eps,
                         int64_t M, int64_t K, int8_t* q, float* s, float* xn_tap, int8_t* q_tap,
                         float* s_tap, void* zero_ptr, size_t zero_bytes, hipStream_t st) {
@@ -357,6 +449,12 @@ a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
 size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
                             int split_k, int mode) {
   if (check_mlp_shapes(M, H, I, split_k) != A8W8_OK) return 0;
+  if (mode == A8W8_MODE_PREFILL_W8A16) {
+    if (op != A8W8_OP_MLP_BLOCK || !prefill_shapes_ok(H, I)) return 0;
+    Carver c(nullptr);
+    carve_prefill(c, M, H, I);
+    return c.size() > 0 ? c.size() : kAlign;
+  }
   if (mode != A8W8_MODE_DECODE_A8W8) return 0;
   bool layer;
   if (op == A8W8_OP_MLP_BLOCK) {
@@ -388,15 +486,21 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
   if (!aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(residual_bf16) ||
       !aligned16(out_bf16))
     return A8W8_ERR_ALIGN;
-  if (mode == A8W8_MODE_PREFILL_W8A16) return A8W8_ERR_UNSUPPORTED;
+  if (mode == A8W8_MODE_PREFILL_W8A16 && !prefill_shapes_ok(H, I)) return A8W8_ERR_SHAPE;
   const size_t need = a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, M, H, I, 0, split_k, mode);
   if (!workspace || ws_bytes < need) return A8W8_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return A8W8_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Timer tm(taps, st);
+  if (mode == A8W8_MODE_PREFILL_W8A16) {
+    Carver c(workspace);
+    const PrefillBuffers pb = carve_prefill(c, M, H, I);
+    return run_mlp_prefill(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M,
+                           H, I, pb, taps, tm, st);
+  }
   const ChainPlan pl = make_plan(M, H, I, 0, split_k, false);
   Carver c(workspace);
   const Buffers b = carve(c, pl, M, H, I, 0, false);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const Timer tm(taps, st);
   return run_mlp_decode(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M, H,
                         I, split_k, pl, b, true, taps, tm, st);
 }

@@ -119,4 +119,34 @@ DecodeGemmPlan plan_decode_gemm(int epi, int64_t M, int64_t N, int64_t K, int pa
                                 bool first);
 hipError_t launch_decode_gemm(const DecodeGemmArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- prefill GEMM
+enum PrefillEpilogue : int {
+  EPI_PF_SILU = 10,     // two weights: h = rne_bf16(silu(g) * u) -> out_bf16
+  EPI_PF_PARTIAL = 11   // one weight, K split `splits` ways: FP32 partials -> part
+};
+
+struct PrefillGemmArgs {
+  int epi, layout;
+  int64_t M, N, K;
+  int splits;               // K splits (EPI_PF_PARTIAL), else 1
+  const uint16_t* act;      // [M, lda] BF16 activations
+  int64_t lda;
+  const int8_t* w0;
+  const float* sw0;
+  const int8_t* w1;         // EPI_PF_SILU: the Up weight
+  const float* sw1;
+  uint16_t* out_bf16;       // EPI_PF_SILU: [M, ldo]
+  int64_t ldo;
+  float* part;              // EPI_PF_PARTIAL: [splits, M, N]
+  float* tap_g;             // EPI_PF_SILU taps: [M, N] FP32 accumulators or nullptr
+  float* tap_u;
+};
+// Output channels one workgroup covers (N must be a multiple of it).
+int prefill_channels_per_wg(int epi);
+hipError_t launch_prefill_gemm(const PrefillGemmArgs& a, hipStream_t stream);
+// out = rne_bf16(sum_s part[s] + res) over [M, N] (M * N % 4 == 0); tap_d gets the sum.
+hipError_t launch_reduce_residual(const float* part, int splits, int64_t M, int64_t N,
+                                  const uint16_t* res, uint16_t* out, float* tap_d,
+                                  hipStream_t stream);
+
 }  // namespace a8w8
