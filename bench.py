@@ -30,7 +30,10 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/layer and INT8-weight HBM GB/s (% of peak), A8W8 decode linears at batch 1"
 HBM_PEAK_GBS = 8000.0
 GATEUP_KERNEL = 5     # kernel number of the Gate/Up GEMM inside a8w8_layer_linears
+GATEUP_NAME = "decode_gemm_kernel<2, 2,"   # its symbol in rocprofv3 counter tables
+PACK_NAME = "pack_tiled_kernel"            # plain permuting copy: the counter calibration
 PMC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_pmc.json")
+PMC_MD = os.path.join(ROOT, "profiles", "layer_linears_m1_pmc.md")
 
 
 def parse():
@@ -42,6 +45,11 @@ def parse():
     p.add_argument("--config", type=int, default=2, help="2: layer M=1; 3: 40-layer M=16 stack")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="summarise two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then "
+                        "WRITE_SIZE, csv output) into the profiles/ traffic files; no GPU use")
+    p.add_argument("--pmc-commands", nargs=2, default=("?", "?"),
+                   help="the two rocprofv3 command lines, recorded in the summary")
     return p.parse_args()
 
 
@@ -64,6 +72,75 @@ def measured_traffic(launch_bytes_alg: float):
     if pmc.get("kernel_source_hash") != kernel_source_hash():
         return None
     return pmc.get("hbm_bytes_per_dispatch")
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, commands, cfg) -> None:
+    """Turn two rocprofv3 counter tables of this bench into HBM bytes per dispatch.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by the factor that
+    makes them agree with the known size of the weight-packing copy the bench runs at
+    start-up (it reads and writes N*K bytes once), then averaged per kernel."""
+    import csv
+    from collections import defaultdict
+
+    H, I, n_qkv = cfg.H, cfg.I, cfg.n_qkv
+    pack_sizes = {n_qkv * H, H * H, I * H}
+
+    def load(path, counter):
+        per_kernel, pack_alg, pack_cnt = defaultdict(list), 0.0, 0.0
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                kib = float(r["Counter_Value"])
+                name = r["Kernel_Name"]
+                if PACK_NAME in name:
+                    nbytes = int(r["Grid_Size"]) * 16      # one thread per 16-byte chunk
+                    if nbytes not in pack_sizes:
+                        raise SystemExit(f"pack dispatch of {nbytes} bytes is not a weight")
+                    pack_alg += nbytes
+                    pack_cnt += kib * 1024
+                per_kernel[name].append(kib)
+        if pack_cnt == 0:
+            raise SystemExit(f"no {PACK_NAME} dispatch in {path}: nothing to calibrate on")
+        return per_kernel, pack_alg / pack_cnt
+
+    fetch, f_fetch = load(fetch_csv, "FETCH_SIZE")
+    write, f_write = load(write_csv, "WRITE_SIZE")
+    rows, gu = [], None
+    for name in sorted(set(fetch) & set(write), key=lambda n: -np.mean(fetch[n])):
+        fk, wk = float(np.mean(fetch[name])), float(np.mean(write[name]))
+        hbm = fk * 1024 * f_fetch + wk * 1024 * f_write
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")[:90]
+        rows.append((short, len(fetch[name]), fk, wk, hbm))
+        if GATEUP_NAME in name:
+            gu = dict(fetch_kib=fk, write_kib=wk, hbm_bytes_per_dispatch=round(hbm))
+    if gu is None:
+        raise SystemExit(f"no {GATEUP_NAME} dispatch in the counter tables")
+    gu_alg = 2 * I * H + 2 * I * 4 + H + 4 + I * 4
+    summary = dict(kernel=GATEUP_NAME, workload=cfg.name, kernel_source_hash=kernel_source_hash(),
+                   fetch_factor=round(f_fetch, 5), write_factor=round(f_write, 5),
+                   algorithmic_bytes_per_dispatch=gu_alg,
+                   traffic_over_algorithmic=round(gu["hbm_bytes_per_dispatch"] / gu_alg, 4),
+                   commands=list(commands), **gu)
+    with open(PMC_FILE, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    lines = [f"# HBM traffic per dispatch, {cfg.name}", "",
+             "Two rocprofv3 counter passes over the same bench run:", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", f"Summarised by `python bench.py --pmc-summary <fetch csv> <write csv>`.",
+              f"Calibration on the weight-packing copy (reads and writes N*K bytes once): "
+              f"FETCH_SIZE x {f_fetch:.4f}, WRITE_SIZE x {f_write:.4f}.", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) |",
+              "|---|---|---|---|---|"]
+    lines += [f"| `{n}` | {c} | {fk:.1f} | {wk:.1f} | {hbm / 1e6:.2f} MB |" for n, c, fk, wk, hbm in rows]
+    lines += ["", f"Gate/Up GEMM: {gu['hbm_bytes_per_dispatch'] / 1e6:.2f} MB per dispatch against "
+              f"{gu_alg / 1e6:.2f} MB algorithmic ({summary['traffic_over_algorithmic']:.4f}x).",
+              f"Kernel source hash: {summary['kernel_source_hash']}.", ""]
+    with open(PMC_MD, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(summary))
 
 
 def cpu_baseline(cfg, seconds: float):
@@ -97,6 +174,10 @@ def cpu_baseline(cfg, seconds: float):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        from w8a8_quantized_decode_amd import synth
+        pmc_summary(*args.pmc_summary, args.pmc_commands, synth.CONFIGS[args.config])
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(multi-GPU sharding is described in DESIGN.md, not built)"}))
