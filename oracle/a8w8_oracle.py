@@ -29,7 +29,9 @@ round to nearest-even); ``fl32(.)`` is one FP32 operation.
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against brute force,
 closed forms, invariants or error bounds.  The end-to-end compositions
 (``mlp_block_decode``, ``layer_linears_decode``, ``prefill_mlp``) are pinned only
-through their stage pins plus an error bound against exact (unquantized) FP64 math.
+through their stage pins plus an error bound against exact (unquantized) FP64 math:
+the pages print no worked example of a whole block, so as compositions they are
+"parity unpinned" beyond those stage pins.
 """
 
 from __future__ import annotations
