@@ -11,8 +11,11 @@
 // too many workgroups, so separate row-quantization kernels run before each GEMM.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdint>
 #include <cstring>
+#include <random>
 
 #include "../../include/a8w8.h"
 #include "internal.h"
@@ -71,32 +74,40 @@ struct Timer {
 // ------------------------------------------------------------------ plans & workspace
 struct ChainPlan {
   bool fused;
-  DecodeGemmPlan qkv, o, gu, dn;
+  StreamKPlan qkv, o, gu, dn;
 };
 
-ChainPlan make_plan(int64_t M, int64_t H, int64_t I, int64_t n_qkv, int split_k, bool layer) {
+ChainPlan plans_for(int64_t M, int64_t H, int64_t I, int64_t n_qkv, int split_k, bool layer,
+                    bool fused) {
   ChainPlan c{};
-  c.fused = M <= kFuseMaxRows;
-  // The call's first GEMM keeps its K range in one workgroup when it is also the first
-  // kernel (nothing before it could clear its accumulators).
+  c.fused = fused;
   if (layer) {
-    c.qkv = plan_decode_gemm(EPI_BF16, M, n_qkv, H, 1, c.fused);
-    c.o = plan_decode_gemm(EPI_BF16_RES, M, H, H, 1, false);
-    c.gu = plan_decode_gemm(EPI_SILU, M, I, H, 1, false);
-  } else {
-    c.gu = plan_decode_gemm(EPI_SILU, M, I, H, 1, c.fused);
+    c.qkv = plan_streamk(EPI_BF16, M, n_qkv, H, 1, fused);
+    c.o = plan_streamk(EPI_BF16_RES, M, H, H, 1, fused);
   }
-  c.dn = plan_decode_gemm(EPI_DOWN, M, H, I, split_k, false);
+  c.gu = plan_streamk(EPI_SILU, M, I, H, 1, fused);
+  c.dn = plan_streamk(EPI_DOWN, M, H, I, split_k, fused);
   return c;
 }
 
-// Layout: one contiguous block of split-K accumulators and arrival counters (cleared by
-// the call's first kernel), then the intermediate activations.
+// Every GEMM quantizes its own input in its prologue when the rows are few and each
+// plan fits the prologue's LDS and register budget; otherwise row-quantization kernels
+// run before the GEMMs.
+ChainPlan make_plan(int64_t M, int64_t H, int64_t I, int64_t n_qkv, int split_k, bool layer) {
+  ChainPlan c = plans_for(M, H, I, n_qkv, split_k, layer, true);
+  bool ok = M <= kFuseMaxRows && streamk_fusable(c.gu, M, H, true) &&
+            streamk_fusable(c.dn, M, I, false);
+  if (layer) ok = ok && streamk_fusable(c.qkv, M, H, true) && streamk_fusable(c.o, M, H, true);
+  return ok ? c : plans_for(M, H, I, n_qkv, split_k, layer, false);
+}
+
+// Layout: piece flags, done words and partial-sum slots, shared by the GEMMs (they run
+// one after another on the stream; flags and done words carry the GEMM's number), then
+// the intermediate activations.
 struct Buffers {
-  void* zero_ptr;
-  size_t zero_bytes;
-  int32_t *cnt_qkv, *cnt_o, *cnt_gu, *cnt_d;
-  int32_t *acc_qkv, *acc_o, *acc_gu, *acc_d;
+  int32_t* slots;
+  uint64_t* flags;
+  uint64_t* dones;
   int8_t* q_in;
   float* s_in;
   uint16_t* qkv;
@@ -114,16 +125,21 @@ struct Buffers {
 Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
               bool layer) {
   Buffers b{};
-  b.cnt_qkv = c.take<int32_t>(pl.qkv.cnt_elems);
-  b.cnt_o = c.take<int32_t>(pl.o.cnt_elems);
-  b.cnt_gu = c.take<int32_t>(pl.gu.cnt_elems);
-  b.cnt_d = c.take<int32_t>(pl.dn.cnt_elems);
-  b.acc_qkv = c.take<int32_t>(pl.qkv.acc_elems);
-  b.acc_o = c.take<int32_t>(pl.o.acc_elems);
-  b.acc_gu = c.take<int32_t>(pl.gu.acc_elems);
-  b.acc_d = c.take<int32_t>(pl.dn.acc_elems);
-  b.zero_ptr = c.base;
-  b.zero_bytes = c.size();
+  size_t slot_elems = pl.gu.slot_elems, flag_elems = pl.gu.flag_elems;
+  size_t done_elems = pl.gu.done_elems;
+  auto widen = [&](const StreamKPlan& q) {
+    if (q.slot_elems > slot_elems) slot_elems = q.slot_elems;
+    if (q.flag_elems > flag_elems) flag_elems = q.flag_elems;
+    if (q.done_elems > done_elems) done_elems = q.done_elems;
+  };
+  widen(pl.dn);
+  if (layer) {
+    widen(pl.qkv);
+    widen(pl.o);
+  }
+  b.flags = c.take<uint64_t>(flag_elems);
+  b.dones = c.take<uint64_t>(done_elems);
+  b.slots = c.take<int32_t>(slot_elems);
   if (layer) {
     if (!pl.fused) {
       b.q_in = c.take<int8_t>(size_t(M) * H);
@@ -143,6 +159,20 @@ Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, i
   b.h = c.take<float>(size_t(M) * I);
   b.pmax = c.take<float>(size_t(I / 16) * M);
   return b;
+}
+
+// Tag of one call, in bits 63..24.  Consecutive calls get consecutive 40-bit tags from
+// a start drawn once per process, so a tagged word left by
+// any earlier call (or never written) carries another tag.
+uint64_t next_call_tag() {
+  static std::atomic<uint64_t> next{[] {
+    std::random_device rd;
+    uint64_t v = (uint64_t(rd()) << 32) ^ uint64_t(rd());
+    v ^= uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+    return v;
+  }()};
+  const uint64_t n = next.fetch_add(1, std::memory_order_relaxed);
+  return (n & ((uint64_t(1) << 40) - 1)) << 24;
 }
 
 a8w8_status check_mlp_shapes(int64_t M, int64_t H, int64_t I, int split_k) {
@@ -165,18 +195,23 @@ int layout_of(const a8w8_qweight& w) {
   return w.layout == A8W8_LAYOUT_TILED ? LAYOUT_TILED : LAYOUT_ROWMAJOR;
 }
 
-DecodeGemmArgs gemm_args(int epi, const DecodeGemmPlan& pl, int64_t M, int64_t N, int64_t K,
-                         const a8w8_qweight& w) {
-  DecodeGemmArgs g{};
+StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int64_t K,
+                      const a8w8_qweight& w, const Buffers& b, uint64_t tag) {
+  StreamKArgs g{};
   g.epi = epi;
   g.layout = layout_of(w);
   g.M = M;
   g.N = N;
   g.K = K;
   g.parts = 1;
-  g.ranges = pl.ranges;
+  g.g = pl.geom;
+  g.act_chunks = pl.act_chunks;
+  g.tag = tag;
   g.w0 = w.w;
   g.sw0 = w.scale;
+  g.slots = b.slots;
+  g.flags = b.flags;
+  g.dones = b.dones;
   return g;
 }
 
@@ -274,7 +309,7 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
 
 hipError_t quant_kernel(const void* x, int64_t ldx, int f32, const uint16_t* gamma, float eps,
                         int64_t M, int64_t K, int8_t* q, float* s, float* xn_tap, int8_t* q_tap,
-                        float* s_tap, void* zero_ptr, size_t zero_bytes, hipStream_t st) {
+                        float* s_tap, hipStream_t st) {
   QuantRowsArgs a{};
   a.x = x;
   a.ldx = ldx;
@@ -289,30 +324,23 @@ hipError_t quant_kernel(const void* x, int64_t ldx, int f32, const uint16_t* gam
   a.q_tap = q_tap;
   a.s_tap = s_tap;
   a.write_codes = 1;
-  a.zero_ptr = zero_ptr;
-  a.zero_bytes = zero_bytes;
   return launch_quant_rows(a, st);
 }
 
-// Enqueues the decode MLP chain.  `zero` is set when this chain starts the call.
+// Enqueues the decode MLP chain (Gate/Up, then Down) under the call's tag.
 a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
                            const a8w8_qweight& gate, const a8w8_qweight& up,
                            const a8w8_qweight& down, const uint16_t* res, uint16_t* out,
                            int64_t M, int64_t H, int64_t I, int split_k, const ChainPlan& pl,
-                           const Buffers& b, bool zero, const a8w8_mlp_taps* t,
+                           const Buffers& b, uint64_t tag, const a8w8_mlp_taps* t,
                            const Timer& tm, hipStream_t st) {
-  void* zp = zero ? b.zero_ptr : nullptr;
-  const size_t zb = zero ? b.zero_bytes : 0;
-
   // Gate/Up GEMM (input RMSNorm + quantization fused or separate), SiLU(g) * u -> h.
-  DecodeGemmArgs g = gemm_args(EPI_SILU, pl.gu, M, I, H, gate);
+  StreamKArgs g = gemm_args(EPI_SILU, pl.gu, M, I, H, gate, b, tag);
   g.w1 = up.w;
   g.sw1 = up.scale;
   g.h = b.h;
   g.ldh = I;
   g.pmax_out = b.pmax;
-  g.wacc = b.acc_gu;
-  g.wcnt = b.cnt_gu;
   g.tap_acc0 = t ? t->acc_gate : nullptr;
   g.tap_acc1 = t ? t->acc_up : nullptr;
   g.tap_h = t ? t->h : nullptr;
@@ -325,12 +353,10 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
     g.tap_xn = t ? t->xn : nullptr;
     g.tap_q = t ? t->q_x : nullptr;
     g.tap_s = t ? t->s_x : nullptr;
-    g.zero_ptr = zp;
-    g.zero_bytes = zb;
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_POST));
     A8W8_HIP(quant_kernel(x, H, 0, gamma, eps, M, H, b.q_x, b.s_x, t ? t->xn : nullptr,
-                          t ? t->q_x : nullptr, t ? t->s_x : nullptr, zp, zb, st));
+                          t ? t->q_x : nullptr, t ? t->s_x : nullptr, st));
     A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_POST));
     g.prologue = PRO_CODES;
     g.a = b.q_x;
@@ -338,32 +364,31 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
     g.sa = b.s_x;
   }
   A8W8_HIP(tm.before(A8W8_KERNEL_GATE_UP));
-  A8W8_HIP(launch_decode_gemm(g, st));
+  A8W8_HIP(launch_streamk(g, pl.gu, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_GATE_UP));
 
   // Down: per-row requantization of h, split-K partials, + residual, RNE to BF16.
-  DecodeGemmArgs d = gemm_args(EPI_DOWN, pl.dn, M, H, I, down);
+  StreamKArgs d = gemm_args(EPI_DOWN, pl.dn, M, H, I, down, b, tag);
   d.parts = split_k;
   d.out = out;
   d.ldo = H;
   d.res = res;
   d.ldr = H;
-  d.wacc = b.acc_d;
-  d.wcnt = b.cnt_d;
   d.tap_acc0 = t ? t->acc_down : nullptr;
   d.tap_p = t ? t->p_down : nullptr;
+  d.once = out == res ? 1 : 0;
   if (pl.fused) {
     d.prologue = PRO_REQUANT_F32;
     d.hin = b.h;
     d.ldhin = I;
     d.pmax = b.pmax;
-    d.npmax = static_cast<int>(I / 16);
+    d.npmax = I / 16;
     d.tap_q = t ? t->q_h : nullptr;
     d.tap_s = t ? t->s_h : nullptr;
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_REQUANT));
     A8W8_HIP(quant_kernel(b.h, I, 1, nullptr, 0.0f, M, I, b.q_h, b.s_h, nullptr,
-                          t ? t->q_h : nullptr, t ? t->s_h : nullptr, nullptr, 0, st));
+                          t ? t->q_h : nullptr, t ? t->s_h : nullptr, st));
     A8W8_HIP(tm.after(A8W8_KERNEL_REQUANT));
     d.prologue = PRO_CODES;
     d.a = b.q_h;
@@ -371,7 +396,7 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
     d.sa = b.s_h;
   }
   A8W8_HIP(tm.before(A8W8_KERNEL_DOWN));
-  A8W8_HIP(launch_decode_gemm(d, st));
+  A8W8_HIP(launch_streamk(d, pl.dn, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_DOWN));
   return A8W8_OK;
 }
@@ -393,7 +418,7 @@ const char* a8w8_status_string(a8w8_status s) {
   return "A8W8_ERR_UNKNOWN";
 }
 
-int a8w8_version(void) { return 200; }
+int a8w8_version(void) { return 300; }
 
 a8w8_status a8w8_pack_weight(const int8_t* w, int64_t N, int64_t K, int8_t* w_tiled,
                              void* stream) {
@@ -415,7 +440,7 @@ a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx, const uint16
       (gamma_bf16 && !aligned16(gamma_bf16)) || (xn_tap && !aligned16(xn_tap)))
     return A8W8_ERR_ALIGN;
   A8W8_HIP(quant_kernel(x_bf16, ldx, 0, gamma_bf16, eps, M, K, q_out, row_scale_out, xn_tap,
-                        nullptr, nullptr, nullptr, 0, static_cast<hipStream_t>(stream)));
+                        nullptr, nullptr, static_cast<hipStream_t>(stream)));
   return A8W8_OK;
 }
 
@@ -430,19 +455,23 @@ a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
   if (!aligned16(q) || !aligned16(row_scale) || !aligned16(y_bf16) ||
       (residual_bf16 && !aligned16(residual_bf16)) || (acc_i32_tap && !aligned16(acc_i32_tap)))
     return A8W8_ERR_ALIGN;
-  DecodeGemmPlan one{};
-  one.ranges = 1;
-  DecodeGemmArgs g = gemm_args(residual_bf16 ? EPI_BF16_RES : EPI_BF16, one, M, N, K, W);
-  g.prologue = PRO_CODES;
+  LinearArgs g{};
+  g.epi = residual_bf16 ? EPI_BF16_RES : EPI_BF16;
+  g.layout = layout_of(W);
+  g.M = M;
+  g.N = N;
+  g.K = K;
   g.a = q;
   g.lda = K;
   g.sa = row_scale;
+  g.w0 = W.w;
+  g.sw0 = W.scale;
   g.out = y_bf16;
   g.ldo = N;
   g.res = residual_bf16;
   g.ldr = N;
   g.tap_acc0 = acc_i32_tap;
-  A8W8_HIP(launch_decode_gemm(g, static_cast<hipStream_t>(stream)));
+  A8W8_HIP(launch_linear(g, static_cast<hipStream_t>(stream)));
   return A8W8_OK;
 }
 
@@ -502,7 +531,7 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
   Carver c(workspace);
   const Buffers b = carve(c, pl, M, H, I, 0, false);
   return run_mlp_decode(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M, H,
-                        I, split_k, pl, b, true, taps, tm, st);
+                        I, split_k, pl, b, next_call_tag(), taps, tm, st);
 }
 
 a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
@@ -537,12 +566,12 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   const Timer tm(mt, st);
   uint16_t* qkv_buf = qkv_out_bf16 ? qkv_out_bf16 : b.qkv;
 
+  const uint64_t tag = next_call_tag();
+
   // QKV projection (input RMSNorm + quantization fused or separate) -> BF16.
-  DecodeGemmArgs g = gemm_args(EPI_BF16, pl.qkv, M, n_qkv, H, qkv);
+  StreamKArgs g = gemm_args(EPI_BF16, pl.qkv, M, n_qkv, H, qkv, b, tag);
   g.out = qkv_buf;
   g.ldo = n_qkv;
-  g.wacc = b.acc_qkv;
-  g.wcnt = b.cnt_qkv;
   g.tap_acc0 = taps ? taps->acc_qkv : nullptr;
   if (pl.fused) {
     g.prologue = PRO_QUANT_BF16;
@@ -553,13 +582,11 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
     g.tap_xn = taps ? taps->xn_in : nullptr;
     g.tap_q = taps ? taps->q_in : nullptr;
     g.tap_s = taps ? taps->s_in : nullptr;
-    g.zero_ptr = b.zero_ptr;
-    g.zero_bytes = b.zero_bytes;
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_IN));
     A8W8_HIP(quant_kernel(x_bf16, H, 0, gamma_in_bf16, eps, M, H, b.q_in, b.s_in,
                           taps ? taps->xn_in : nullptr, taps ? taps->q_in : nullptr,
-                          taps ? taps->s_in : nullptr, b.zero_ptr, b.zero_bytes, st));
+                          taps ? taps->s_in : nullptr, st));
     A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_IN));
     g.prologue = PRO_CODES;
     g.a = b.q_in;
@@ -567,7 +594,7 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
     g.sa = b.s_in;
   }
   A8W8_HIP(tm.before(A8W8_KERNEL_QKV));
-  A8W8_HIP(launch_decode_gemm(g, st));
+  A8W8_HIP(launch_streamk(g, pl.qkv, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_QKV));
   if (taps && taps->qkv)
     A8W8_HIP(hipMemcpyAsync(taps->qkv, qkv_buf, size_t(M) * n_qkv * sizeof(uint16_t),
@@ -575,13 +602,11 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
 
   // Identity attention: the Q slice qkv[:, :H] is quantized and fed to O; O adds the
   // layer input as residual -> h1.
-  DecodeGemmArgs og = gemm_args(EPI_BF16_RES, pl.o, M, H, H, o);
+  StreamKArgs og = gemm_args(EPI_BF16_RES, pl.o, M, H, H, o, b, tag);
   og.out = b.h1;
   og.ldo = H;
   og.res = x_bf16;
   og.ldr = H;
-  og.wacc = b.acc_o;
-  og.wcnt = b.cnt_o;
   og.tap_acc0 = taps ? taps->acc_o : nullptr;
   if (pl.fused) {
     og.prologue = PRO_QUANT_BF16;
@@ -592,8 +617,7 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_ATTN));
     A8W8_HIP(quant_kernel(qkv_buf, n_qkv, 0, nullptr, 0.0f, M, H, b.q_a, b.s_a, nullptr,
-                          taps ? taps->q_attn : nullptr, taps ? taps->s_attn : nullptr, nullptr,
-                          0, st));
+                          taps ? taps->q_attn : nullptr, taps ? taps->s_attn : nullptr, st));
     A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_ATTN));
     og.prologue = PRO_CODES;
     og.a = b.q_a;
@@ -601,14 +625,14 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
     og.sa = b.s_a;
   }
   A8W8_HIP(tm.before(A8W8_KERNEL_O));
-  A8W8_HIP(launch_decode_gemm(og, st));
+  A8W8_HIP(launch_streamk(og, pl.o, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_O));
   if (taps && taps->h1)
     A8W8_HIP(hipMemcpyAsync(taps->h1, b.h1, size_t(M) * H * sizeof(uint16_t),
                             hipMemcpyDeviceToDevice, st));
 
   return run_mlp_decode(b.h1, gamma_post_bf16, eps, gate, up, down, b.h1, out_bf16, M, H, I,
-                        split_k, pl, b, false, mt, tm, st);
+                        split_k, pl, b, tag, mt, tm, st);
 }
 
 }  // extern "C"

@@ -60,4 +60,116 @@ __device__ __forceinline__ int32_t atomic_add_dev(int32_t* p, int32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------ INT8 matrix-core helpers
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x4 ld16(const int8_t* p) {
+  return *reinterpret_cast<const i32x4*>(p);
+}
+
+// Dequantized value: fl32(fl32(f(acc) * sa) * sw).
+__device__ __forceinline__ float dq(int32_t acc, float sa, float sw) {
+  return (static_cast<float>(acc) * sa) * sw;
+}
+
+// silu(g) * u with silu(g) = g / (1 + exp(-g)), exp evaluated in FP64 and rounded once.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = static_cast<float>(exp(-static_cast<double>(g)));
+  const float den = 1.0f + e;
+  return (g / den) * u;
+}
+
+__device__ __forceinline__ void load8_bf16(const uint16_t* p, float (&v)[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(w[i]);
+    v[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+__device__ __forceinline__ void load8_f32(const float* p, float (&v)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
+// Eight INT8 codes of v under row scale s, packed little-endian (all zero when s == 0).
+__device__ __forceinline__ u32x2 codes8(const float (&v)[8], float s) {
+  uint32_t lo = 0, hi = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= (uint32_t(quant_code(v[i], s)) & 0xFFu) << (8 * i);
+      hi |= (uint32_t(quant_code(v[4 + i], s)) & 0xFFu) << (8 * i);
+    }
+  }
+  return u32x2{lo, hi};
+}
+
+// Workgroup barrier that orders LDS only.  A full __syncthreads also waits for every
+// outstanding global load of the wave, which would drain a weight stream's prefetch.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup reductions over LDS slots: each wave reduces, lane 0 posts, and after one
+// barrier every thread combines the slots in wave order (same bits in every thread).
+template <int NW>
+__device__ __forceinline__ double block_sum_f64(double v, double* slots) {
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = v;
+  lds_barrier();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += slots[w];
+  return s;
+}
+
+template <int NW>
+__device__ __forceinline__ float block_max_f32(float v, float* slots) {
+  v = wave_max_f32(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = v;
+  lds_barrier();
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s = fmaxf(s, slots[w]);
+  return s;
+}
+
+// Agent-coherent 16-byte store and load (two relaxed 64-bit device-scope atomics each):
+// they go to the coherence point shared by all XCDs, so data passed between workgroups
+// this way needs no L2 write-back or invalidation.
+__device__ __forceinline__ void store_coherent(int32_t* p, i32x4 v) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(p);
+  const uint64_t lo = uint64_t(uint32_t(v[0])) | (uint64_t(uint32_t(v[1])) << 32);
+  const uint64_t hi = uint64_t(uint32_t(v[2])) | (uint64_t(uint32_t(v[3])) << 32);
+  __hip_atomic_store(d, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ i32x4 load_coherent(const int32_t* p) {
+  const uint64_t* d = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return i32x4{int32_t(uint32_t(lo)), int32_t(uint32_t(lo >> 32)), int32_t(uint32_t(hi)),
+               int32_t(uint32_t(hi >> 32))};
+}
+
+// Waits until every memory operation this wave has issued has completed (vmcnt = 0),
+// with compiler barriers so that no memory access moves across it.
+__device__ __forceinline__ void wait_memory_done() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt unconstrained
+  __asm__ __volatile__("" ::: "memory");
+}
+
 }  // namespace a8w8

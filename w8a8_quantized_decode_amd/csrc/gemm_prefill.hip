@@ -57,12 +57,6 @@ __device__ __forceinline__ void dequant16(u32x4 raw, float s, bf16x8& lo, bf16x8
   }
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float e = static_cast<float>(exp(-static_cast<double>(g)));
-  const float den = 1.0f + e;
-  return (g / den) * u;
-}
-
 template <int EPI, int NMAT, int CB, int LAYOUT>
 __global__ __launch_bounds__(kPfWaves * kWave) void prefill_gemm_kernel(PrefillGemmArgs p) {
   __shared__ __align__(16) int8_t bsm[2][kPfStage];

@@ -1,0 +1,810 @@
+// Stream-K INT8 x INT8 -> INT32 decode GEMM on gfx950 matrix cores, with fused
+// activation quantization (prologue) and fused dequant / SiLU / residual / split-K
+// epilogues.  It serves the MLP block and the layer chain.
+//
+// Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
+// paths", What changed > Gate/Up INT8 path (INT8 x INT8 -> INT32 Gate/Up matmuls, the
+// activation-row and weight-channel scales applied at dequantization, the
+// post-attention RMSNorm output quantized once per row) and > Decode scheduling (Down
+// split two ways along K into independent accumulators), plus the CodeRabbit
+// walkthrough row "Split down projection accumulation" (FP32 partials summed and
+// narrowed together with the residual).  QKV and O reuse the same pattern.
+//
+// At decode batch sizes the weights are the traffic: every weight byte is read from HBM
+// once and the kernel is a weight stream.
+//   * The unit of work is a 64-byte K step of a 16-channel tile: one
+//     v_mfma_i32_16x16x64_i8 with the weights as A (lane l feeds channel l%16 with the
+//     16 bytes at k-offset 16*(l/16)) and the activation codes as B (one column per
+//     decode row, zeros for missing rows).  Lane l's result holds channels 4*(l/16)+r of
+//     row l%16.
+//   * All steps of the problem form one sequence ordered by K chunk, tile, step.  In the
+//     tiled weight layout a (chunk, tile) segment is one contiguous run of bytes.  The
+//     sequence is dealt out in order and evenly (to one step) to every wave of a grid
+//     sized to the machine, so all waves stream the same number of bytes and finish
+//     together.  A wave keeps two batches of weight loads in flight in two register sets.
+//   * When its range is done a wave leaves the INT32 partial sums of the (at most two)
+//     segments it touched in LDS; the workgroup then adds its waves' partials per
+//     segment.  A tile held by one workgroup alone goes straight to the epilogue; for
+//     the others each workgroup stores its piece to a slot of its own and sets the
+//     piece's flag to the call's tag, and a wave that finds every flag of the tile set
+//     adds the slots and runs the epilogue.  Integer addition is exact, so the result
+//     does not depend on the split.  A flag holding another call's tag counts as unset,
+//     so nothing needs clearing between calls, and no address is contended.
+//   * Fused prologue: every workgroup re-derives the row statistics (RMSNorm sum of
+//     squares and absolute maximum, or the maximum of per-tile partial maxima for the
+//     requantized Down input) and writes the codes of the K chunks its waves consume to
+//     LDS.  Its first batch of weight loads is issued before it.
+//   * No wait in the streaming loop covers more than the batch being consumed: loads are
+//     unconditional with clamped addresses, dead steps multiply a zero operand, and the
+//     workgroup barriers order LDS only.
+#include "device_common.h"
+#include "internal.h"
+
+namespace a8w8 {
+
+// First step of wave w (w = W gives the total).
+__host__ __device__ inline int32_t sk_wave_start(const StreamKGeom& g, int32_t w) {
+  return w * g.q + (w < g.r ? w : g.r);
+}
+
+// Wave whose range holds step f.
+__host__ __device__ inline int32_t sk_owner(const StreamKGeom& g, int32_t f) {
+  const int32_t cut = g.r * (g.q + 1);
+  return f < cut ? static_cast<int32_t>(g.by_q1.div(static_cast<uint32_t>(f)))
+                 : g.r + static_cast<int32_t>(g.by_q.div(static_cast<uint32_t>(f - cut)));
+}
+
+// K chunks [c0, c1] of the steps dealt to workgroup b (waves b*NW .. b*NW+NW-1).
+__host__ __device__ inline void sk_wg_chunks(const StreamKGeom& g, int32_t b, int32_t NW,
+                                             int32_t& c0, int32_t& c1) {
+  const int32_t wl = (b + 1) * NW < g.waves ? (b + 1) * NW : g.waves;
+  const int32_t A = sk_wave_start(g, b * NW), B = sk_wave_start(g, wl);
+  c0 = static_cast<int32_t>(g.by_tiles.div(g.by_seg.div(static_cast<uint32_t>(A))));
+  c1 = B > A ? static_cast<int32_t>(g.by_tiles.div(g.by_seg.div(static_cast<uint32_t>(B - 1)))) : c0;
+}
+
+namespace {
+
+constexpr int kSkWaves = 8;
+constexpr int64_t kSkTargetWgs = 512;      // two 8-wave workgroups per CU
+constexpr int64_t kSkSmallWgs = 256;       // one per CU for GEMMs under kSkSmallSteps
+constexpr int64_t kSkSmallSteps = 65536;
+constexpr int64_t kSkMinSteps = 4;         // at least 4 KB of weights per wave
+constexpr int kPV = 2;                     // prologue vectors of 8 values per thread
+constexpr int64_t kPrologueMax = int64_t(kPV) * 8 * kSkWaves * kWave;  // 8192 values
+constexpr size_t kSkMaxLds = 64 * 1024;
+
+template <int NW>
+struct SkSmem {
+  double sum_slots[kFuseMaxRows][NW];
+  float max_slots[kFuseMaxRows][NW];
+  float row_scale[kFuseMaxRows];
+};
+
+// Row 0's BF16 prologue inputs, fetched before the first weight batch: a wait for them
+// then never covers weight loads (the memory counter completes in order).  Raw 16-byte
+// registers (8 BF16 of x and of the gain) loaded unconditionally from clamped
+// addresses; elements past the row are discarded where they are used.
+struct PrologueRegs {
+  u32x4 a[kPV];  // x[k..k+8) as BF16
+  u32x4 b[kPV];  // gain[k..k+8) as BF16
+};
+
+template <int NW, int PRO>
+__device__ __forceinline__ void sk_prologue_fetch(const StreamKArgs& p, int64_t klo, int64_t len,
+                                                  PrologueRegs& r) {
+  static_assert(PRO == PRO_QUANT_BF16, "only the BF16 prologue prefetches");
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kPV; ++j) {
+    const int64_t e = int64_t(j) * NT * 8 + tid * 8;
+    const int64_t k = e < p.K ? e : p.K - 8;
+    r.a[j] = *reinterpret_cast<const u32x4*>(p.x + k);
+    r.b[j] = *reinterpret_cast<const u32x4*>((p.gamma ? p.gamma : p.x) + k);
+  }
+}
+
+// BF16 prologue, one row: RMSNorm (when a gain is given), row scale into
+// sm.row_scale[m], codes of K values [klo, klo + len) into act[m * act_ld + (k - klo)].
+// The row is held in registers (K <= kPrologueMax, checked by the planner).  Row 0
+// comes from the prefetched registers (FIRST, no load on its path); later rows are
+// loaded here.
+template <int NW, int PRO, bool FIRST, typename SM>
+__device__ __forceinline__ void sk_prologue_row(const StreamKArgs& p, SM& sm, int8_t* act,
+                                                int64_t act_ld, int64_t klo, int64_t len,
+                                                bool taps, const PrologueRegs& pre, int m) {
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x;
+  float v[kPV][8];
+  float s;
+  int64_t vbase;  // K index of element (j, i) is vbase + j * NT * 8 + tid * 8 + i
+  static_assert(PRO == PRO_QUANT_BF16, "the BF16 row prologue");
+  {
+    // RMSNorm statistics over the whole row, then the absolute maximum.
+    vbase = 0;
+    float g[kPV][8];
+    const uint16_t* xr = p.x + int64_t(m) * p.ldx;
+#pragma unroll
+    for (int j = 0; j < kPV; ++j) {
+      const int64_t k = int64_t(j) * NT * 8 + tid * 8;
+      const bool in = k < p.K;
+      u32x4 xa = pre.a[j], ga = pre.b[j];
+      if constexpr (!FIRST) {
+        const int64_t kc = in ? k : p.K - 8;
+        xa = *reinterpret_cast<const u32x4*>(xr + kc);
+        ga = *reinterpret_cast<const u32x4*>((p.gamma ? p.gamma : xr) + kc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[j][2 * i] = in ? bf16_lo(xa[i]) : 0.0f;
+        v[j][2 * i + 1] = in ? bf16_hi(xa[i]) : 0.0f;
+        g[j][2 * i] = bf16_lo(ga[i]);
+        g[j][2 * i + 1] = bf16_hi(ga[i]);
+      }
+    }
+    if (p.gamma) {
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < kPV; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += double(v[j][i]) * double(v[j][i]);
+      const double S = block_sum_f64<NW>(ss, sm.sum_slots[m]);
+      const float ms = static_cast<float>(S / static_cast<double>(p.K));
+      const float t = ms + p.eps;
+      const float r = 1.0f / __builtin_sqrtf(t);
+#pragma unroll
+      for (int j = 0; j < kPV; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][i] = (v[j][i] * r) * g[j][i];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPV; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+    amax = block_max_f32<NW>(amax, sm.max_slots[m]);
+    s = amax / 127.0f;
+  }
+  if (tid == 0) {
+    sm.row_scale[m] = s;
+    if (taps && p.tap_s) p.tap_s[m] = s;
+  }
+#pragma unroll
+  for (int j = 0; j < kPV; ++j) {
+    const int64_t k = vbase + int64_t(j) * NT * 8 + tid * 8;
+    if (k >= klo && k < klo + len) {
+      const u32x2 c = codes8(v[j], s);
+      *reinterpret_cast<u32x2*>(act + m * act_ld + (k - klo)) = c;
+      if (taps && p.tap_q) *reinterpret_cast<u32x2*>(p.tap_q + int64_t(m) * p.K + k) = c;
+      if (taps && p.tap_xn) {
+        f32x4* tx = reinterpret_cast<f32x4*>(p.tap_xn + int64_t(m) * p.K + k);
+        tx[0] = f32x4{v[j][0], v[j][1], v[j][2], v[j][3]};
+        tx[1] = f32x4{v[j][4], v[j][5], v[j][6], v[j][7]};
+      }
+    } else if (taps && k < p.K) {
+      // Taps cover the whole row; workgroup 0 writes them.
+      const u32x2 c = codes8(v[j], s);
+      if (p.tap_q) *reinterpret_cast<u32x2*>(p.tap_q + int64_t(m) * p.K + k) = c;
+      if (p.tap_xn) {
+        f32x4* tx = reinterpret_cast<f32x4*>(p.tap_xn + int64_t(m) * p.K + k);
+        tx[0] = f32x4{v[j][0], v[j][1], v[j][2], v[j][3]};
+        tx[1] = f32x4{v[j][4], v[j][5], v[j][6], v[j][7]};
+      }
+    }
+  }
+}
+
+// Fused prologue for rows 0..M-1, then one barrier for the codes in LDS.
+template <int NW, int PRO, typename SM>
+__device__ void sk_prologue(const StreamKArgs& p, SM& sm, int8_t* act, int64_t act_ld,
+                            int64_t klo, int64_t len, bool taps, const PrologueRegs& pre) {
+  sk_prologue_row<NW, PRO, true>(p, sm, act, act_ld, klo, len, taps, pre, 0);
+  for (int m = 1; m < p.M; ++m)
+    sk_prologue_row<NW, PRO, false>(p, sm, act, act_ld, klo, len, taps, pre, m);
+  lds_barrier();
+}
+
+// Requantization prologue (Down input): the row scale comes from the per-tile partial
+// maxima, so the K values [klo, klo + len) are quantized straight into LDS in a loop.
+// It runs before any weight load is issued, so none of its waits covers weight loads.
+template <int NW, typename SM>
+__device__ void sk_requant_prologue(const StreamKArgs& p, SM& sm, int8_t* act, int64_t act_ld,
+                                    int64_t klo, int64_t len, bool taps) {
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x;
+  for (int m = 0; m < p.M; ++m) {
+    float amax = 0.0f;
+    for (int64_t k = tid; k < p.npmax; k += NT) amax = fmaxf(amax, p.pmax[k * p.M + m]);
+    amax = block_max_f32<NW>(amax, sm.max_slots[m]);
+    const float s = amax / 127.0f;
+    if (tid == 0) {
+      sm.row_scale[m] = s;
+      if (taps && p.tap_s) p.tap_s[m] = s;
+    }
+    const float* hr = p.hin + int64_t(m) * p.ldhin + klo;
+    for (int64_t e = int64_t(tid) * 8; e < len; e += int64_t(NT) * 8) {
+      float v[8];
+      load8_f32(hr + e, v);
+      *reinterpret_cast<u32x2*>(act + m * act_ld + e) = codes8(v, s);
+    }
+  }
+  lds_barrier();
+}
+
+// Codes taps of the requantized Down input cover the whole row; workgroup 0 writes them
+// in a separate pass (a debugging path only).
+template <int NW>
+__device__ void sk_requant_taps(const StreamKArgs& p, const float* row_scale) {
+  constexpr int NT = NW * kWave;
+  for (int m = 0; m < p.M; ++m)
+    for (int64_t k = int64_t(threadIdx.x) * 8; k < p.K; k += NT * 8) {
+      float v[8];
+      load8_f32(p.hin + int64_t(m) * p.ldhin + k, v);
+      *reinterpret_cast<u32x2*>(p.tap_q + int64_t(m) * p.K + k) = codes8(v, row_scale[m]);
+    }
+}
+
+// EPI: epilogue, NMAT: weights per tile (2 for Gate/Up), NW: waves per workgroup, MB:
+// 16-row blocks (1 with a fused prologue), LAYOUT: weight layout, PRO: prologue.
+template <int EPI, int NMAT, int NW, int MB, int LAYOUT, int PRO>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+void streamk_kernel(StreamKArgs p) {
+  constexpr bool kFused = PRO != PRO_CODES;
+  constexpr int kU0 = kFused ? (NMAT == 2 ? 4 : 6) : 4 / (NMAT * MB);
+  constexpr int U = kU0 > 0 ? kU0 : 1;         // k steps per load batch
+  constexpr int kSlot = NMAT * MB * 4 * kWave;  // INT32 per slot
+  __shared__ SkSmem<NW> sm;
+  extern __shared__ __align__(16) int8_t act[];
+
+  const int tid = threadIdx.x;
+  // The wave index lives in a scalar register so that every branch around a matrix
+  // instruction is wave-uniform (a matrix instruction ignores a partial lane mask).
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int row16 = lane & 15, kg = lane >> 4;
+  const StreamKGeom& G = p.g;
+  const int32_t T = G.tiles, St = G.steps_tile, Ss = G.steps_seg, C = G.chunks;
+  const int32_t wv = static_cast<int32_t>(blockIdx.x) * NW + wave;
+  const int32_t w0 = sk_wave_start(G, wv), w1 = sk_wave_start(G, wv + 1);
+  const bool has = w1 > w0;
+  // A wave without steps (only when there are fewer steps than waves) addresses step 0
+  // and never has a live step, so every wave issues the same unconditional loads.
+  const int32_t f0 = has ? w0 : 0, f1 = has ? w1 : 1;
+  const int32_t flive = has ? w1 : 0;
+  const int64_t m0 = int64_t(blockIdx.y) * MB * 16;
+
+  // Activation operand rows; lanes of missing rows read row 0 and feed zeros.
+  bool aval[MB];
+  int64_t aoff[MB];
+  int64_t klo = 0, act_ld = 0, alen = 0;
+  if constexpr (kFused) {
+    int32_t c0, c1;
+    sk_wg_chunks(G, static_cast<int32_t>(blockIdx.x), NW, c0, c1);
+    klo = int64_t(c0) * Ss * 64;
+    alen = int64_t(c1 - c0 + 1) * Ss * 64;
+    act_ld = int64_t(p.act_chunks) * Ss * 64;
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t m = m0 + mb * 16 + row16;
+    aval[mb] = m < p.M;
+    aoff[mb] = kFused ? (aval[mb] ? row16 : 0) * act_ld - klo + kg * 16
+                      : (aval[mb] ? m : 0) * p.lda + kg * 16;
+  }
+
+  // The range [f0, f1) covers at most two segments (the planner deals at least one
+  // wave per segment): steps f < fx belong to segment segA, the others to segA + 1.
+  // Within a segment, steps are consecutive 1 KB blocks (tiled layout) or consecutive
+  // 64-byte groups of 16 rows (row-major), so each operand address is a linear
+  // function of f on either side of fx: a scalar select, no per-step branches.
+  const int32_t segA = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(f0)));
+  const int32_t segN = segA + 1;
+  const int32_t fx = (segN * Ss < f1) ? segN * Ss : f1;
+  const int32_t cA = static_cast<int32_t>(G.by_tiles.div(static_cast<uint32_t>(segA)));
+  const int32_t tA = segA - cA * T;
+  const int32_t cB = static_cast<int32_t>(G.by_tiles.div(static_cast<uint32_t>(segN)));
+  const int32_t tB = segN - cB * T;
+  const int64_t kA0 = int64_t(cA) * Ss + (f0 - segA * Ss);   // K step of f0
+  const int64_t kB0 = int64_t(cB) * Ss;                      // K step of fx
+  constexpr int64_t kStep = (LAYOUT == LAYOUT_TILED) ? 1024 : 64;
+  const int64_t lane_off = (LAYOUT == LAYOUT_TILED) ? int64_t(lane) * 16
+                                                    : int64_t(row16) * p.K + kg * 16;
+  const int64_t wA0 = (LAYOUT == LAYOUT_TILED) ? (int64_t(tA) * St + kA0) * 1024
+                                                : int64_t(tA) * 16 * p.K + kA0 * 64;
+  const int64_t wB0 = (LAYOUT == LAYOUT_TILED) ? (int64_t(tB) * St + kB0) * 1024
+                                                : int64_t(tB) * 16 * p.K + kB0 * 64;
+  auto wofs = [&](int32_t f) -> int64_t {
+    return (f < fx) ? wA0 + int64_t(f - f0) * kStep : wB0 + int64_t(f - fx) * kStep;
+  };
+  auto kstep = [&](int32_t f) -> int64_t { return (f < fx) ? kA0 + (f - f0) : kB0 + (f - fx); };
+  const int8_t* w0l = p.w0 + lane_off;
+  const int8_t* w1l = (NMAT == 2) ? p.w1 + lane_off : nullptr;
+
+  // Load side: batches of U steps; past the end of the range the last step is re-read.
+  int32_t lf = f0;
+  auto load_batch = [&](i32x4 (&wv_)[U][NMAT], i32x4 (&bv)[U][MB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t f = (lf + u < f1) ? lf + u : f1 - 1;
+      const int64_t o = wofs(f);
+      wv_[u][0] = ld16(w0l + o);
+      if constexpr (NMAT == 2) wv_[u][1] = ld16(w1l + o);
+      if constexpr (!kFused) {
+        const int64_t ks = kstep(f);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) bv[u][mb] = ld16(p.a + aoff[mb] + ks * 64);
+      }
+    }
+    lf += U;
+  };
+
+  // Compute side: one matrix instruction per weight and row block per step; at fx the
+  // first segment's sums move to acc0, so no store happens inside the loop.
+  i32x4 acc[NMAT][MB], acc0[NMAT][MB];
+#pragma unroll
+  for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      acc[i][mb] = i32x4{0, 0, 0, 0};
+      acc0[i][mb] = i32x4{0, 0, 0, 0};
+    }
+  int32_t cf = f0;
+  auto compute = [&](const i32x4 (&wv_)[U][NMAT], const i32x4 (&bv)[U][MB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t f = cf + u;
+      const bool live = f < flive;
+      i32x4 b[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        i32x4 v;
+        if constexpr (kFused)
+          v = *reinterpret_cast<const i32x4*>(act + aoff[mb] + kstep(live ? f : f1 - 1) * 64);
+        else
+          v = bv[u][mb];
+        b[mb] = (live && aval[mb]) ? v : i32x4{0, 0, 0, 0};
+      }
+      if (f == fx && live) {
+#pragma unroll
+        for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            acc0[i][mb] = acc[i][mb];
+            acc[i][mb] = i32x4{0, 0, 0, 0};
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[i][mb] = mfma_i8(wv_[u][i], b[mb], acc[i][mb]);
+    }
+    cf += U;
+  };
+
+  i32x4 wA[U][NMAT], bA[U][MB], wB[U][NMAT], bB[U][MB];
+  const int32_t nb = (flive - f0 + U - 1) / U;
+  // The requantization prologue runs first, with no weight load in flight.  For the
+  // BF16 prologue, row 0 of its input is fetched first, then one weight batch, which is
+  // in flight while the prologue runs (a second would crowd its registers); the second
+  // is issued right after it.  Both unconditionally: a guard here would let the
+  // compiler assume the batches may arrive out of order.
+  const bool taps = blockIdx.x == 0;
+  if constexpr (PRO == PRO_REQUANT_F32) {
+    sk_requant_prologue<NW>(p, sm, act, act_ld, klo, alen, taps);
+    if (taps && p.tap_q) sk_requant_taps<NW>(p, sm.row_scale);
+  }
+  PrologueRegs pre;
+  if constexpr (PRO == PRO_QUANT_BF16) sk_prologue_fetch<NW, PRO>(p, klo, alen, pre);
+  __builtin_amdgcn_sched_barrier(0);
+  load_batch(wA, bA);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PRO == PRO_QUANT_BF16) sk_prologue<NW, PRO>(p, sm, act, act_ld, klo, alen, taps, pre);
+  __builtin_amdgcn_sched_barrier(0);
+  load_batch(wB, bB);
+  __builtin_amdgcn_sched_barrier(0);
+  // Pairs of batches with no branch inside the body (a branch would let the compiler
+  // sink the next batch's loads behind the other batch's compute) and scheduling
+  // barriers between the phases (so no instruction of one batch's compute is hoisted
+  // above the other's), then an odd tail.
+  int32_t bi = 0;
+  for (; bi + 1 < nb; bi += 2) {
+    compute(wA, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(wA, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wB, bB);
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(wB, bB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (bi < nb) compute(wA, bA);
+
+  // Workgroup combine.  Each wave leaves the partial sums of its (at most two) segments
+  // in LDS; after one barrier the workgroup's segments are dealt to its waves, and a
+  // wave sums the workgroup's partials of its segment.
+  constexpr int kRed = NMAT * MB * 4 * kWave;  // INT32 per (wave, segment) partial
+  int32_t* red = reinterpret_cast<int32_t*>(act + p.red_off);
+  {
+    const int32_t sb_w = has ? static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(f1 - 1))) : segA;
+    const bool crossed = sb_w > segA;
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int o = ((i * MB + mb) * kWave + lane) * 4;
+        *reinterpret_cast<i32x4*>(red + (wave * 2) * kRed + o) = crossed ? acc0[i][mb] : acc[i][mb];
+        *reinterpret_cast<i32x4*>(red + (wave * 2 + 1) * kRed + o) =
+            crossed ? acc[i][mb] : i32x4{0, 0, 0, 0};
+      }
+  }
+  lds_barrier();
+
+  const int32_t b = static_cast<int32_t>(blockIdx.x);
+  const int32_t nwg = static_cast<int32_t>(gridDim.x);
+  const int32_t wfirst = b * NW;
+  const int32_t wend = (wfirst + NW < G.waves) ? wfirst + NW : G.waves;
+  const int32_t A = sk_wave_start(G, wfirst), B = sk_wave_start(G, wend);
+  if (B <= A) return;
+  const int32_t sA = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(A)));
+  const int32_t sB = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(B - 1)));
+  int32_t* slots = p.slots + int64_t(blockIdx.y) * (int64_t(T) * C + nwg) * kSlot;
+  uint64_t* flags = p.flags + int64_t(blockIdx.y) * (int64_t(T) * C + nwg);
+  uint64_t* dones = p.dones + int64_t(blockIdx.y) * T;
+  const uint64_t want = p.tag | uint64_t(EPI + 1);
+
+  // The pieces of tile t in chunks [ca, cb) are the slots (c*T + t) + g for the
+  // workgroups g touching segment c*T + t, a contiguous run per chunk.  `visit` walks
+  // them in groups of eight: the eight slot indices first (scalar work), then all eight
+  // loads at once, then their use, so a group costs one memory round trip.
+  auto wg_of = [&](int32_t f) { return sk_owner(G, f) / NW; };
+  auto visit = [&](int32_t t, int32_t ca, int32_t cb, auto&& load, auto&& use) {
+    int32_t n = 0;
+    for (int32_t c = ca; c < cb; ++c) {
+      const int32_t s0 = (c * T + t) * Ss;
+      n += wg_of(s0 + Ss - 1) - wg_of(s0) + 1;
+    }
+    int32_t ic = ca;
+    int32_t ig = wg_of((ca * T + t) * Ss);
+    int32_t igb = wg_of((ca * T + t) * Ss + Ss - 1);
+    for (int32_t i0 = 0; i0 < n; i0 += 8) {
+      int32_t idx[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        idx[k] = ic * T + t + ig;
+        if (i0 + k + 1 < n) {
+          if (ig < igb) {
+            ++ig;
+          } else {
+            ++ic;
+            const int32_t s0 = (ic * T + t) * Ss;
+            ig = wg_of(s0);
+            igb = wg_of(s0 + Ss - 1);
+          }
+        }
+      }
+      decltype(load(0)) v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = load(idx[k]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (i0 + k < n) use(v[k]);
+    }
+  };
+
+  for (int32_t sg = sA + wave; sg <= sB; sg += NW) {
+    const int32_t t = sg - static_cast<int32_t>(G.by_tiles.div(static_cast<uint32_t>(sg))) * T;
+    i32x4 part[NMAT][MB];
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) part[i][mb] = i32x4{0, 0, 0, 0};
+    for (int32_t j = 0; j < wend - wfirst; ++j) {
+      const int32_t a0 = sk_wave_start(G, wfirst + j), a1 = sk_wave_start(G, wfirst + j + 1);
+      if (a1 <= a0) continue;
+      const int32_t ja = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(a0)));
+      const int32_t jb = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(a1 - 1)));
+      const int slot = (ja == sg) ? 0 : ((jb == sg) ? 1 : -1);
+      if (slot < 0) continue;
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          part[i][mb] += *reinterpret_cast<const i32x4*>(
+              red + (j * 2 + slot) * kRed + ((i * MB + mb) * kWave + lane) * 4);
+    }
+    // Epilogue inputs (channel scales, residual) are fetched now, so their latency
+    // overlaps the exchange below.  Lane l owns channels en..en+3 of row em.
+    const int64_t en = t * 16 + 4 * kg;
+    const f32x4 sw0v = *reinterpret_cast<const f32x4*>(p.sw0 + en);
+    const f32x4 sw1v = (NMAT == 2) ? *reinterpret_cast<const f32x4*>(p.sw1 + en) : sw0v;
+    u32x2 resv[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t em = m0 + mb * 16 + row16;
+      resv[mb] = u32x2{0u, 0u};
+      if constexpr (EPI == EPI_BF16_RES || EPI == EPI_DOWN)
+        resv[mb] = *reinterpret_cast<const u32x2*>(p.res + (aval[mb] ? em : 0) * p.ldr + en);
+    }
+
+    // A tile of one chunk held by this workgroup alone needs no exchange.
+    const bool interior = C == 1 && wg_of(t * Ss) == b && wg_of(t * Ss + Ss - 1) == b;
+    if (!interior) {
+      // Publish the piece: its slot, then its flag (the call's tag and this GEMM's
+      // number), each written agent-coherently and waited for, so the flag is visible
+      // only after the slot is.
+      int32_t* sp = slots + int64_t(sg + b) * kSlot;
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          if (aval[mb]) store_coherent(sp + ((i * MB + mb) * kWave + lane) * 4, part[i][mb]);
+      wait_memory_done();
+      if (lane == 0)
+        __hip_atomic_store(flags + (sg + b), want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_memory_done();
+      // The epilogue runs in a wave that finds every piece's flag set: at least the one
+      // whose flag became visible last finds them all.
+      bool all = true;
+      visit(t, 0, C,
+            [&](int32_t i) { return __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
+            [&](uint64_t f) { all = all && (f == want); });
+      if (!__builtin_amdgcn_readfirstlane(all ? 1 : 0)) continue;
+      if (p.once) {
+        // Several waves can find them all set; when the output overwrites the residual
+        // it reads, exactly one (the first to swap the tile's done word to this call's
+        // tag) runs the epilogue.  Otherwise a repeated epilogue writes the same values.
+        uint64_t prev = 0;
+        if (lane == 0)
+          prev = __hip_atomic_exchange(dones + t, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t plo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev));
+        const uint32_t phi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev >> 32));
+        if (((uint64_t(phi) << 32) | plo) == want) continue;
+      }
+    }
+
+    // Sum of the pieces of chunks [ca, cb) of tile t, per weight and row block.
+    auto gather = [&](i32x4 (&s)[NMAT][MB], int32_t ca, int32_t cb) {
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) s[i][mb] = interior ? part[i][mb] : i32x4{0, 0, 0, 0};
+      if (interior) return;
+      struct Piece {
+        i32x4 v[NMAT][MB];
+      };
+      visit(t, ca, cb,
+            [&](int32_t i) {
+              Piece pc;
+              const int32_t* q = slots + int64_t(i) * kSlot;
+#pragma unroll
+              for (int j = 0; j < NMAT; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                  pc.v[j][mb] = aval[mb] ? load_coherent(q + ((j * MB + mb) * kWave + lane) * 4)
+                                         : i32x4{0, 0, 0, 0};
+              return pc;
+            },
+            [&](const Piece& pc) {
+#pragma unroll
+              for (int j = 0; j < NMAT; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) s[j][mb] += pc.v[j][mb];
+            });
+    };
+    float sa[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t em = m0 + mb * 16 + row16;
+      sa[mb] = aval[mb] ? (kFused ? sm.row_scale[em] : p.sa[em]) : 0.0f;
+    }
+
+    if constexpr (EPI == EPI_BF16 || EPI == EPI_BF16_RES) {
+      i32x4 s[NMAT][MB];
+      gather(s, 0, C);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if (!aval[mb]) continue;
+        const int64_t em = m0 + mb * 16 + row16;
+        if (p.tap_acc0) *reinterpret_cast<i32x4*>(p.tap_acc0 + em * p.N + en) = s[0][mb];
+        float y[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) y[c] = dq(s[0][mb][c], sa[mb], sw0v[c]);
+        if constexpr (EPI == EPI_BF16_RES) {
+          const u32x2 rr = resv[mb];
+          y[0] = y[0] + bf16_lo(rr[0]);
+          y[1] = y[1] + bf16_hi(rr[0]);
+          y[2] = y[2] + bf16_lo(rr[1]);
+          y[3] = y[3] + bf16_hi(rr[1]);
+        }
+        u32x2 o;
+        o[0] = uint32_t(f32_to_bf16_rne(y[0])) | (uint32_t(f32_to_bf16_rne(y[1])) << 16);
+        o[1] = uint32_t(f32_to_bf16_rne(y[2])) | (uint32_t(f32_to_bf16_rne(y[3])) << 16);
+        *reinterpret_cast<u32x2*>(p.out + em * p.ldo + en) = o;
+      }
+    } else if constexpr (EPI == EPI_SILU) {
+      i32x4 s[NMAT][MB];
+      gather(s, 0, C);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int64_t em = m0 + mb * 16 + row16;
+        f32x4 h = {0.f, 0.f, 0.f, 0.f};
+        if (aval[mb]) {
+          if (p.tap_acc0) *reinterpret_cast<i32x4*>(p.tap_acc0 + em * p.N + en) = s[0][mb];
+          if (p.tap_acc1) *reinterpret_cast<i32x4*>(p.tap_acc1 + em * p.N + en) = s[NMAT - 1][mb];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float g = dq(s[0][mb][c], sa[mb], sw0v[c]);
+            const float u = dq(s[NMAT - 1][mb][c], sa[mb], sw1v[c]);
+            h[c] = silu_mul(g, u);
+          }
+          *reinterpret_cast<f32x4*>(p.h + em * p.ldh + en) = h;
+          if (p.tap_h) *reinterpret_cast<f32x4*>(p.tap_h + em * p.N + en) = h;
+        }
+        // Absolute maximum of the tile's 16 channels of row em (the four lanes sharing
+        // l % 16 hold them), for the requantization scale of the next GEMM.
+        float mx = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        if (p.pmax_out && aval[mb] && kg == 0) p.pmax_out[t * p.M + em] = mx;
+      }
+    } else {  // EPI_DOWN: partitions summed in order, then the residual
+      const int64_t MN = p.M * p.N;
+      const int32_t cpp = C / p.parts;  // chunks per partition
+      float tot[MB][4];
+      for (int32_t part = 0; part < p.parts; ++part) {
+        i32x4 s[NMAT][MB];
+        gather(s, part * cpp, (part + 1) * cpp);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          if (!aval[mb]) continue;
+          const int64_t em = m0 + mb * 16 + row16;
+          if (p.tap_acc0)
+            *reinterpret_cast<i32x4*>(p.tap_acc0 + part * MN + em * p.N + en) = s[0][mb];
+          f32x4 pv;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) pv[c] = dq(s[0][mb][c], sa[mb], sw0v[c]);
+          if (p.tap_p) *reinterpret_cast<f32x4*>(p.tap_p + part * MN + em * p.N + en) = pv;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) tot[mb][c] = (part == 0) ? pv[c] : tot[mb][c] + pv[c];
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if (!aval[mb]) continue;
+        const int64_t em = m0 + mb * 16 + row16;
+        const u32x2 rr = resv[mb];
+        const float o0 = tot[mb][0] + bf16_lo(rr[0]);
+        const float o1 = tot[mb][1] + bf16_hi(rr[0]);
+        const float o2 = tot[mb][2] + bf16_lo(rr[1]);
+        const float o3 = tot[mb][3] + bf16_hi(rr[1]);
+        u32x2 o;
+        o[0] = uint32_t(f32_to_bf16_rne(o0)) | (uint32_t(f32_to_bf16_rne(o1)) << 16);
+        o[1] = uint32_t(f32_to_bf16_rne(o2)) | (uint32_t(f32_to_bf16_rne(o3)) << 16);
+        *reinterpret_cast<u32x2*>(p.out + em * p.ldo + en) = o;
+      }
+    }
+  }
+}
+
+template <int EPI, int NMAT, int MB, int LAYOUT, int PRO>
+hipError_t launch_one(const StreamKArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  const auto kern = streamk_kernel<EPI, NMAT, kSkWaves, MB, LAYOUT, PRO>;
+  if (lds > 64 * 1024) {
+    // Above the default dynamic LDS limit (only the wide row blocks need it).
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, grid, dim3(kSkWaves * kWave), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int EPI, int NMAT, int MB, int PRO>
+hipError_t launch_layout(const StreamKArgs& a, dim3 grid, size_t lds, hipStream_t s) {
+  if (a.layout == LAYOUT_TILED) return launch_one<EPI, NMAT, MB, LAYOUT_TILED, PRO>(a, grid, lds, s);
+  return launch_one<EPI, NMAT, MB, LAYOUT_ROWMAJOR, PRO>(a, grid, lds, s);
+}
+
+template <int EPI, int NMAT, int PROF>
+hipError_t launch_epi(const StreamKArgs& a, const StreamKPlan& pl, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(pl.wgs), static_cast<unsigned>(pl.mgroups));
+  if (a.prologue != PRO_CODES) return launch_layout<EPI, NMAT, 1, PROF>(a, grid, pl.lds, s);
+  switch (pl.mb) {
+    case 1: return launch_layout<EPI, NMAT, 1, PRO_CODES>(a, grid, pl.lds, s);
+    case 2: return launch_layout<EPI, NMAT, 2, PRO_CODES>(a, grid, pl.lds, s);
+    default: return launch_layout<EPI, NMAT, 4, PRO_CODES>(a, grid, pl.lds, s);
+  }
+}
+
+}  // namespace
+
+StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bool fused) {
+  StreamKPlan pl{};
+  pl.waves = kSkWaves;
+  const int P = (epi == EPI_DOWN) ? parts : 1;
+  const int64_t T = N / 16, St = K / 64;
+  // One chunk per K partition, so a tile inside one workgroup needs no exchange; more
+  // for a fused requantized Down input while the codes of two chunks (a workgroup's
+  // steps span at most two) would not fit LDS beside the combine area.
+  int64_t cpp = 1;
+  const int nmat = (epi == EPI_SILU) ? 2 : 1;
+  if (epi == EPI_DOWN && fused) {
+    const int64_t red = int64_t(kSkWaves) * 2 * nmat * 4 * kWave * 4;
+    while ((St / P) % (2 * cpp) == 0 && M * 2 * (St / (P * cpp)) * 64 + red > int64_t(kSkMaxLds))
+      cpp *= 2;
+  }
+  const int64_t C = P * cpp, Ss = St / C, Tot = T * St;
+  // Smaller GEMMs stream a little faster with fewer, longer ranges (measured on the
+  // 5120 x 5120 and 7168 x 5120 projections); the large ones with two per CU.
+  int64_t wgs = Tot / (int64_t(kSkWaves) * kSkMinSteps);
+  const int64_t target = Tot < kSkSmallSteps ? kSkSmallWgs : kSkTargetWgs;
+  if (wgs > target) wgs = target;
+  // At least one wave per segment: a wave's range (at most ceil(Tot / W) <= Ss + 1
+  // steps) then spans at most two segments, which the kernel relies on.
+  const int64_t per_seg = (T * C + kSkWaves - 1) / kSkWaves;
+  if (wgs < per_seg) wgs = per_seg;
+  if (wgs < 1) wgs = 1;
+  pl.wgs = static_cast<int>(wgs);
+  const int64_t W = wgs * kSkWaves;
+  StreamKGeom& g = pl.geom;
+  g.tiles = static_cast<int32_t>(T);
+  g.steps_tile = static_cast<int32_t>(St);
+  g.steps_seg = static_cast<int32_t>(Ss);
+  g.chunks = static_cast<int32_t>(C);
+  g.total = static_cast<int32_t>(Tot);
+  g.waves = static_cast<int32_t>(W);
+  g.q = static_cast<int32_t>(Tot / W);
+  g.r = static_cast<int32_t>(Tot % W);
+  g.by_seg = FastDiv(static_cast<uint32_t>(Ss));
+  g.by_tiles = FastDiv(static_cast<uint32_t>(T));
+  g.by_q = FastDiv(static_cast<uint32_t>(g.q > 0 ? g.q : 1));
+  g.by_q1 = FastDiv(static_cast<uint32_t>(g.q + 1));
+  if (fused) {
+    pl.mgroups = 1;
+    pl.mb = 1;
+    int32_t span = 1;
+    for (int32_t b = 0; b < pl.wgs; ++b) {
+      int32_t c0, c1;
+      sk_wg_chunks(g, b, kSkWaves, c0, c1);
+      if (c1 - c0 + 1 > span) span = c1 - c0 + 1;
+    }
+    pl.act_chunks = span;
+    pl.red_off = (size_t(M) * size_t(int64_t(span) * Ss * 64) + 15) / 16 * 16;
+  } else {
+    pl.mgroups = static_cast<int>((M + 63) / 64);
+    const int64_t rows = M < 64 ? M : 64;
+    const int64_t b16 = (rows + 15) / 16;
+    pl.mb = b16 <= 1 ? 1 : (b16 <= 2 ? 2 : 4);
+    pl.act_chunks = 0;
+    pl.red_off = 0;
+  }
+  pl.lds = pl.red_off + size_t(kSkWaves) * 2 * nmat * pl.mb * 4 * kWave * sizeof(int32_t);
+  pl.slot_elems = size_t(pl.mgroups) * size_t(T * C + wgs) * size_t(nmat) * pl.mb * 4 * kWave;
+  pl.flag_elems = size_t(pl.mgroups) * size_t(T * C + wgs);
+  pl.done_elems = size_t(pl.mgroups) * size_t(T);
+  return pl;
+}
+
+bool streamk_fusable(const StreamKPlan& pl, int64_t M, int64_t K_in, bool bf16_rows) {
+  if (M > kFuseMaxRows) return false;
+  if (pl.lds > kSkMaxLds) return false;
+  // The BF16 prologue holds its rows in registers; the requantization one does not.
+  return !bf16_rows || K_in <= kPrologueMax;
+}
+
+hipError_t launch_streamk(const StreamKArgs& a_in, const StreamKPlan& pl, hipStream_t stream) {
+  if (a_in.M == 0) return hipSuccess;
+  StreamKArgs a = a_in;
+  a.red_off = static_cast<int64_t>(pl.red_off);
+  switch (a.epi) {
+    case EPI_BF16: return launch_epi<EPI_BF16, 1, PRO_QUANT_BF16>(a, pl, stream);
+    case EPI_BF16_RES: return launch_epi<EPI_BF16_RES, 1, PRO_QUANT_BF16>(a, pl, stream);
+    case EPI_SILU: return launch_epi<EPI_SILU, 2, PRO_QUANT_BF16>(a, pl, stream);
+    case EPI_DOWN: return launch_epi<EPI_DOWN, 1, PRO_REQUANT_F32>(a, pl, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace a8w8

@@ -24,11 +24,6 @@ struct QuantRowsArgs {
   uint16_t* a_bf16;         // [M, K] rne_bf16(v) or nullptr (prefill activations)
   uint16_t* a_bf16_tap;     // [M, K] or nullptr
   int write_codes;          // 0: skip the INT8 codes (prefill only needs a_bf16)
-  // Extra workgroups beyond the M row workgroups zero this region (16-byte aligned,
-  // a multiple of 16 bytes): the split-K accumulators and counters of the GEMMs that
-  // follow in the same call.
-  void* zero_ptr;
-  size_t zero_bytes;
 };
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t stream);
 
@@ -42,7 +37,7 @@ enum WeightLayout : int { LAYOUT_ROWMAJOR = 0, LAYOUT_TILED = 1 };
 hipError_t launch_pack_tiled(const int8_t* w, int64_t N, int64_t K, int8_t* out,
                              hipStream_t stream);
 
-// ---------------------------------------------------------------- decode GEMM
+// ---------------------------------------------------------------- decode GEMMs
 enum DecodeEpilogue : int {
   EPI_BF16 = 0,       // y = rne_bf16(dequant(acc))
   EPI_BF16_RES = 1,   // y = rne_bf16(dequant(acc) + res)
@@ -56,14 +51,74 @@ enum DecodePrologue : int {
   PRO_REQUANT_F32 = 2   // quantize FP32 rows hin with the scale from partial maxima
 };
 
-// Rows a fused-prologue launch handles (the prologue re-derives each row per workgroup).
+// Rows a fused-prologue launch handles (each workgroup re-derives every row).
 constexpr int kFuseMaxRows = 4;
 
-struct DecodeGemmArgs {
+// Standalone linear on given codes (a8w8_linear): one workgroup per 16-channel tile, no
+// workspace.
+struct LinearArgs {
+  int epi, layout;          // EPI_BF16 or EPI_BF16_RES
+  int64_t M, N, K;
+  const int8_t* a;          // [M, lda] INT8 codes
+  int64_t lda;
+  const float* sa;          // [M] row scales
+  const int8_t* w0;
+  const float* sw0;         // [N]
+  uint16_t* out;            // [M, ldo]
+  int64_t ldo;
+  const uint16_t* res;      // [M, ldr] or nullptr
+  int64_t ldr;
+  int32_t* tap_acc0;        // [M, N] or nullptr
+};
+hipError_t launch_linear(const LinearArgs& a, hipStream_t stream);
+
+// Division of n < 2^31 by a divisor d in [1, 2^31) fixed per launch, by multiply-high
+// and shift (the round-up method of Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+  uint32_t d, m, l;
+  FastDiv() : d(1), m(1), l(0) {}
+  explicit FastDiv(uint32_t dd) : d(dd), m(0), l(0) {
+    while ((uint64_t(1) << l) < d) ++l;
+    m = static_cast<uint32_t>(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+  }
+  __host__ __device__ uint32_t div(uint32_t n) const {
+    const uint32_t hi = static_cast<uint32_t>((uint64_t(n) * m) >> 32);
+    return static_cast<uint32_t>((uint64_t(hi) + n) >> l);
+  }
+};
+
+// Stream-K decode GEMM of the MLP block and layer chains.
+//
+// The work is the sequence of 64-byte K steps of every 16-channel tile, ordered by K
+// chunk, then tile, then step: for the tiled layout each (chunk, tile) segment is one
+// contiguous run of weight bytes.  The sequence is dealt out evenly, in order, to every
+// wave of the grid.  A wave writes the INT32 partial sums of each segment it touches to
+// its own slot and sets the piece's flag to the call's tag; a wave that finds every
+// flag of a tile set adds the slots (integer sums: exact in any order) and runs the
+// epilogue.  The tags make clearing unnecessary.
+// Geometry of the step sequence (all counts below 2^31).  Waves w < r take q + 1 steps,
+// the others q, in order: wave w starts at w * q + min(w, r).
+struct StreamKGeom {
+  int32_t tiles;            // T = N / 16
+  int32_t steps_tile;       // K / 64
+  int32_t steps_seg;        // Ss = steps_tile / chunks
+  int32_t chunks;           // C
+  int32_t total;            // T * steps_tile
+  int32_t waves;            // W, per 64-row group
+  int32_t q, r;             // total = q * W + r
+  FastDiv by_seg, by_tiles, by_q, by_q1;  // divisors Ss, T, q (1 if q == 0), q + 1
+};
+
+struct StreamKArgs {
   int epi, layout, prologue;
   int64_t M, N, K;
   int parts;                // K partitions (EPI_DOWN: split_k), else 1
-  int ranges;               // K ranges per partition spread over workgroups
+  int act_chunks;           // chunks of codes one workgroup keeps in LDS (fused prologue)
+  int64_t red_off;          // byte offset of the workgroup-combine area in dynamic LDS
+  uint64_t tag;             // call tag in bits 63..24
+  StreamKGeom g;
   // PRO_CODES
   const int8_t* a;          // [M, lda] INT8 codes
   int64_t lda;
@@ -77,7 +132,7 @@ struct DecodeGemmArgs {
   const float* hin;         // [M, ldhin] FP32
   int64_t ldhin;
   const float* pmax;        // [npmax, M] partial absolute maxima of hin's rows
-  int npmax;
+  int64_t npmax;
   // weights
   const int8_t* w0;
   const float* sw0;         // [N]
@@ -90,11 +145,11 @@ struct DecodeGemmArgs {
   int64_t ldr;
   float* h;                 // [M, ldh] FP32 (EPI_SILU)
   int64_t ldh;
-  float* pmax_out;          // EPI_SILU: [N/16, M] absolute maximum of h per 16-channel tile
-  int32_t* wacc;            // ranges > 1: [sets, M, N] INT32 accumulators, zero on entry
-  int32_t* wcnt;            // ranges > 1: [tiles * mgroups] arrival counters, zero on entry
-  void* zero_ptr;           // region this kernel zeroes for later kernels (16 B multiple)
-  size_t zero_bytes;
+  float* pmax_out;          // EPI_SILU: [N/16, M] absolute maximum of h per tile
+  int32_t* slots;           // partial-sum slots (StreamKPlan::slot_elems)
+  uint64_t* flags;          // [mgroups, tiles * chunks + workgroups] piece flags
+  uint64_t* dones;          // [mgroups, tiles] done words (used when `once`)
+  int once;                 // the output may overwrite the residual: one epilogue per tile
   // taps (nullptr = off)
   int32_t* tap_acc0;        // [M, N] (EPI_DOWN: [parts, M, N])
   int32_t* tap_acc1;        // [M, N] (EPI_SILU up accumulator)
@@ -105,19 +160,24 @@ struct DecodeGemmArgs {
   float* tap_s;             // fused prologue: [M] row scales
 };
 
-// Launch shape chosen for a problem; the host needs it to size the workspace.
-struct DecodeGemmPlan {
-  int ranges;        // K ranges per partition (1 = no cross-workgroup reduction)
-  int waves;         // waves per workgroup
-  int mgroups;       // grid.y: groups of up to 64 rows
-  int tiles;         // N / 16
-  size_t acc_elems;  // INT32 accumulator elements needed (0 when ranges == 1)
-  size_t cnt_elems;  // counters needed
+struct StreamKPlan {
+  int waves;           // waves per workgroup
+  int wgs;             // grid.x: workgroups per 64-row group
+  int mgroups;         // grid.y
+  int mb;              // 16-row blocks per group (1 with a fused prologue)
+  StreamKGeom geom;
+  int act_chunks;
+  size_t slot_elems;   // INT32 elements of partial-sum slots
+  size_t flag_elems;   // 64-bit piece flags
+  size_t done_elems;   // 64-bit done words
+  size_t red_off;      // dynamic LDS: codes first (fused), workgroup-combine area here
+  size_t lds;          // dynamic LDS bytes
 };
-// first: the call's first GEMM (its accumulators cannot be pre-zeroed, so ranges = 1).
-DecodeGemmPlan plan_decode_gemm(int epi, int64_t M, int64_t N, int64_t K, int parts,
-                                bool first);
-hipError_t launch_decode_gemm(const DecodeGemmArgs& a, hipStream_t stream);
+StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bool fused);
+// Whether a fused-prologue plan fits (rows, LDS, prologue registers); K_in is the row
+// length a BF16 prologue normalizes (bf16_rows), else the requantized row.
+bool streamk_fusable(const StreamKPlan& pl, int64_t M, int64_t K_in, bool bf16_rows);
+hipError_t launch_streamk(const StreamKArgs& a, const StreamKPlan& pl, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill GEMM
 enum PrefillEpilogue : int {

@@ -76,15 +76,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(QuantRowsArgs
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int64_t row = blockIdx.x;
-  if (row >= p.M) {
-    // Zeroing workgroups: clear the caller's accumulator region, 16 bytes per store.
-    const int64_t nz = int64_t(gridDim.x) - p.M;
-    const int64_t n16 = int64_t(p.zero_bytes / 16);
-    u32x4* z = static_cast<u32x4*>(p.zero_ptr);
-    for (int64_t i = (row - p.M) * kQuantThreads + tid; i < n16; i += nz * kQuantThreads)
-      z[i] = u32x4{0u, 0u, 0u, 0u};
-    return;
-  }
   const int64_t K = p.K;
   const char* xrow = static_cast<const char*>(p.x) +
                      row * p.ldx * (kF32In ? sizeof(float) : sizeof(uint16_t));
@@ -183,14 +174,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(QuantRowsArgs
 
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
-  // One workgroup per row, plus up to 64 workgroups that zero the accumulator region.
-  int64_t zero_wgs = 0;
-  if (a.zero_ptr && a.zero_bytes) {
-    const int64_t per_wg = int64_t(kQuantThreads) * 16 * 4;
-    zero_wgs = (int64_t(a.zero_bytes) + per_wg - 1) / per_wg;
-    if (zero_wgs > 64) zero_wgs = 64;
-  }
-  const dim3 grid(static_cast<unsigned>(a.M + zero_wgs)), block(kQuantThreads);
+  // One workgroup per row.
+  const dim3 grid(static_cast<unsigned>(a.M)), block(kQuantThreads);
   const bool rms = a.gamma != nullptr;
   if (rms && !a.x_is_f32)
     hipLaunchKernelGGL((quant_rows_kernel<true, false>), grid, block, 0, stream, a);
