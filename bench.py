@@ -220,6 +220,8 @@ def main():
         if s == 0:
             x0 = up(d["x"])
         del d
+        if nsets > 4 and (s + 1) % 5 == 0:
+            print(f"[bench] {s + 1}/{nsets} weight sets resident", file=sys.stderr, flush=True)
     wbytes_layer = (n_qkv * H + H * H + 2 * I * H + H * I)
     ws = torch.zeros(B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, M, H, I, n_qkv, cfg.split_k),
                      dtype=torch.uint8, device="cuda")
