@@ -102,7 +102,7 @@ typedef enum a8w8_kernel {
   A8W8_KERNEL_GATE_UP = 5,
   A8W8_KERNEL_REQUANT = 6,     /* requantization of silu(g) * u before Down       */
   A8W8_KERNEL_DOWN = 7,
-  A8W8_KERNEL_REDUCE = 8       /* prefill: Down partial sums + residual -> BF16    */
+  A8W8_KERNEL_REDUCE = 8       /* reserved: no current path launches this role     */
 } a8w8_kernel;
 
 /*
@@ -229,9 +229,10 @@ size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_q
  * Prefill mode (any M; built for M in the hundreds): a = rne_bf16(RMSNorm(x)); every
  * weight tile is dequantized to W' = rne_bf16(fl32(w * s)) on the fly; Gate/Up
  * accumulate in FP32 on BF16 matrix cores; h = rne_bf16(silu(g) * u); Down accumulates
- * in FP32 over 4 K splits whose FP32 partials are added in order; out =
- * rne_bf16(d + residual).  Additionally needs I % 128 == 0 and H % 256 == 0.  Kernels:
- * QUANT_POST (norm), GATE_UP, DOWN, REDUCE.
+ * in FP32 (a K range split between workgroups is added back in K order, so results
+ * are reproducible run to run); out = rne_bf16(d + residual).  Additionally needs
+ * H % 256 == 0, I % 256 == 0 and M * max(H, I) < 2^31.  Kernels: QUANT_POST (norm),
+ * GATE_UP, DOWN (with the residual add).
  */
 a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, float eps,
                            a8w8_qweight gate, a8w8_qweight up, a8w8_qweight down,

@@ -123,7 +123,7 @@ def check(d, got, want, t, st):
     assert rel <= 1e-2
 
 
-@pytest.mark.parametrize("M", [1, 16, 64, 65, 200])
+@pytest.mark.parametrize("M", [1, 16, 64, 65, 200, 300])
 @pytest.mark.parametrize("layout", [B.LAYOUT_ROWMAJOR, B.LAYOUT_TILED])
 def test_prefill_toy(M, layout):
     announce(f"prefill toy M={M} layout={layout}")

@@ -216,33 +216,42 @@ StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int6
 }
 
 // ------------------------------------------------------------------ prefill (W8A16)
-constexpr int kPrefillDownSplits = 4;
-
 struct PrefillBuffers {
-  uint16_t* a;     // [M, H] BF16 activations rne_bf16(RMSNorm(x))
-  uint16_t* h;     // [M, I] BF16 silu(g) * u
-  float* part;     // [splits, M, H] FP32 Down partial sums
+  uint16_t* a;       // [M, H] BF16 activations rne_bf16(RMSNorm(x))
+  uint16_t* h;       // [M, I] BF16 silu(g) * u
+  float* slots;      // stream-K exchange slots
+  uint64_t* flags;   // one per slot and wave
+  uint64_t* dones;   // one per tile and wave
 };
 
 PrefillBuffers carve_prefill(Carver& c, int64_t M, int64_t H, int64_t I) {
+  const PrefillPlan gu = plan_prefill(EPI_PF_SILU, M, I, H);
+  const PrefillPlan dn = plan_prefill(EPI_PF_RES, M, H, I);
+  const int64_t grid = gu.grid > dn.grid ? gu.grid : dn.grid;
+  const int64_t tiles_gu = int64_t(gu.mtiles) * gu.ntiles;
+  const int64_t tiles_dn = int64_t(dn.mtiles) * dn.ntiles;
+  const int64_t tiles = tiles_gu > tiles_dn ? tiles_gu : tiles_dn;
   PrefillBuffers b{};
   b.a = c.take<uint16_t>(size_t(M) * H);
   b.h = c.take<uint16_t>(size_t(M) * I);
-  b.part = c.take<float>(size_t(kPrefillDownSplits) * M * H);
+  b.slots = c.take<float>(size_t(2 * grid) * prefill_slot_floats());
+  b.flags = c.take<uint64_t>(size_t(2 * grid) * 4);
+  b.dones = c.take<uint64_t>(size_t(tiles) * 4);
   return b;
 }
 
-bool prefill_shapes_ok(int64_t H, int64_t I) {
-  return I % prefill_channels_per_wg(EPI_PF_SILU) == 0 &&
-         H % prefill_channels_per_wg(EPI_PF_PARTIAL) == 0 &&
-         (I / 64) >= kPrefillDownSplits;
+bool prefill_shapes_ok(int64_t M, int64_t H, int64_t I) {
+  return I % prefill_tile_channels(EPI_PF_SILU) == 0 &&
+         H % prefill_tile_channels(EPI_PF_RES) == 0 && H % 256 == 0 && I % 256 == 0 &&
+         M * (H > I ? H : I) < (int64_t(1) << 31);
 }
 
 a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
                             const a8w8_qweight& gate, const a8w8_qweight& up,
                             const a8w8_qweight& down, const uint16_t* res, uint16_t* out,
                             int64_t M, int64_t H, int64_t I, const PrefillBuffers& b,
-                            const a8w8_mlp_taps* t, const Timer& tm, hipStream_t st) {
+                            uint64_t tag, const a8w8_mlp_taps* t, const Timer& tm,
+                            hipStream_t st) {
   // RMSNorm, narrowed to BF16 (the MFMA operand type).
   QuantRowsArgs q{};
   q.x = x;
@@ -266,17 +275,20 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   g.M = M;
   g.N = I;
   g.K = H;
-  g.splits = 1;
   g.act = b.a;
   g.lda = H;
   g.w0 = gate.w;
   g.sw0 = gate.scale;
   g.w1 = up.w;
   g.sw1 = up.scale;
-  g.out_bf16 = b.h;
+  g.out = b.h;
   g.ldo = I;
   g.tap_g = t ? t->g : nullptr;
   g.tap_u = t ? t->u : nullptr;
+  g.slots = b.slots;
+  g.flags = b.flags;
+  g.dones = b.dones;
+  g.tag = tag;
   A8W8_HIP(tm.before(A8W8_KERNEL_GATE_UP));
   A8W8_HIP(launch_prefill_gemm(g, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_GATE_UP));
@@ -284,26 +296,29 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
     A8W8_HIP(hipMemcpyAsync(t->h_bf16, b.h, size_t(M) * I * sizeof(uint16_t),
                             hipMemcpyDeviceToDevice, st));
 
-  // Down in K splits (FP32 partials), then partials + residual -> RNE BF16.
+  // Down, FP32 accumulate, out = rne_bf16(d + res) in the same kernel.
   PrefillGemmArgs d{};
-  d.epi = EPI_PF_PARTIAL;
+  d.epi = EPI_PF_RES;
   d.layout = layout_of(down);
   d.M = M;
   d.N = H;
   d.K = I;
-  d.splits = kPrefillDownSplits;
   d.act = b.h;
   d.lda = I;
   d.w0 = down.w;
   d.sw0 = down.scale;
-  d.part = b.part;
+  d.out = out;
+  d.ldo = H;
+  d.res = res;
+  d.ldr = H;
+  d.tap_d = t ? t->d : nullptr;
+  d.slots = b.slots;
+  d.flags = b.flags;
+  d.dones = b.dones;
+  d.tag = tag;
   A8W8_HIP(tm.before(A8W8_KERNEL_DOWN));
   A8W8_HIP(launch_prefill_gemm(d, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_DOWN));
-  A8W8_HIP(tm.before(A8W8_KERNEL_REDUCE));
-  A8W8_HIP(launch_reduce_residual(b.part, kPrefillDownSplits, M, H, res, out, t ? t->d : nullptr,
-                                  st));
-  A8W8_HIP(tm.after(A8W8_KERNEL_REDUCE));
   return A8W8_OK;
 }
 
@@ -479,7 +494,7 @@ size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_q
                             int split_k, int mode) {
   if (check_mlp_shapes(M, H, I, split_k) != A8W8_OK) return 0;
   if (mode == A8W8_MODE_PREFILL_W8A16) {
-    if (op != A8W8_OP_MLP_BLOCK || !prefill_shapes_ok(H, I)) return 0;
+    if (op != A8W8_OP_MLP_BLOCK || !prefill_shapes_ok(M, H, I)) return 0;
     Carver c(nullptr);
     carve_prefill(c, M, H, I);
     return c.size() > 0 ? c.size() : kAlign;
@@ -515,7 +530,7 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
   if (!aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(residual_bf16) ||
       !aligned16(out_bf16))
     return A8W8_ERR_ALIGN;
-  if (mode == A8W8_MODE_PREFILL_W8A16 && !prefill_shapes_ok(H, I)) return A8W8_ERR_SHAPE;
+  if (mode == A8W8_MODE_PREFILL_W8A16 && !prefill_shapes_ok(M, H, I)) return A8W8_ERR_SHAPE;
   const size_t need = a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, M, H, I, 0, split_k, mode);
   if (!workspace || ws_bytes < need) return A8W8_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return A8W8_ERR_ALIGN;
@@ -525,7 +540,7 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
     Carver c(workspace);
     const PrefillBuffers pb = carve_prefill(c, M, H, I);
     return run_mlp_prefill(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M,
-                           H, I, pb, taps, tm, st);
+                           H, I, pb, next_call_tag(), taps, tm, st);
   }
   const ChainPlan pl = make_plan(M, H, I, 0, split_k, false);
   Carver c(workspace);

@@ -2,24 +2,40 @@
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
 // paths", What changed > Gate/Up INT8 path: prefill keeps the INT8 checkpoint weights
-// and dequantizes each weight tile to BF16 before the matrix multiply.  Here every tile
-// element becomes W' = rne_bf16(fl32(w * s[n])) in registers, the activations are BF16,
-// products accumulate in FP32 (v_mfma_f32_16x16x32_bf16).
+// and dequantizes each weight tile to BF16 before the matrix multiply.  Every weight
+// element becomes W' = rne_bf16(fl32(w * s[n])), the activations are BF16, products
+// accumulate in FP32 (v_mfma_f32_16x16x32_bf16).
 //
-// Work shape.  A workgroup of 4 waves owns 64 rows of M and 4 * 16 * CB output
-// channels; each wave owns 16 * CB channels (CB blocks of 16) of NMAT weights.
-//   * Weights come from the tiled layout: one 1 KB block = 16 channels x 64 k, lane l
-//     holding channel l%16, k-offsets 16*(l/16)..+15.  The lane dequantizes its 16
-//     bytes into two BF16 operands (k-offsets +0..7 and +8..15); each feeds one
-//     16x16x32 MFMA, and the activation operand is gathered with the same k order.
-//   * int8 -> FP32 -> x scale uses the biased byte u = w + 128 (exact in FP32) and one
-//     fused multiply-add u*s + (-128*s): the exact value is w*s, so the single rounding
-//     gives fl32(w*s) bit for bit.  The FP32 -> BF16 step is the RNE conversion.
-//   * Activations (BF16, row-major [M, K]) are staged per 64-k step through LDS in a
-//     double buffer whose rows are padded to 144 bytes, so the 16 lanes that read one
-//     column group hit 16 distinct 4-bank groups.
-//   * EPI_PF_SILU: h = rne_bf16(silu(g) * u) from the Gate and Up accumulators.
-//     EPI_PF_PARTIAL: FP32 partial sums of one K split, reduced by reduce_residual.
+// Work shape: stream-K over tiles of 256 rows of M by 16 * NCB weight channels.
+//   * Gate/Up tiles hold NCB/2 16-channel blocks of Gate and the same channels of Up,
+//     so silu(g) * u is formed from one workgroup's accumulators; Down tiles hold NCB
+//     blocks of one weight.
+//   * One unit of work is a 64-k step of one tile.  Units are ordered (tile, k) and
+//     dealt to a fixed grid of workgroups in contiguous runs of whole quads (4 steps);
+//     a workgroup runs its whole run as one software pipeline across tile boundaries.
+//   * Weights: per step each of the 256 threads loads NCB/4 16-byte chunks of the INT8
+//     tile (the chunk a matrix-core lane needs), dequantizes them and stores the BF16
+//     operands to an LDS double buffer; every wave then reads the operands of all NCB
+//     blocks from LDS.  A weight element is fetched and dequantized once per workgroup.
+//     int8 -> FP32 uses the biased byte u = w + 128 (exact) and one fused multiply-add
+//     u * s + (-128 * s), whose exact value is w * s, so its single rounding gives
+//     fl32(w * s); FP32 -> BF16 is the RNE conversion.
+//   * Activations: wave w owns rows 64w..64w+63 of the tile and loads its BF16 operands
+//     straight from global memory into registers, three steps ahead of use.
+//   * Matrix-core operands: the weights are A (lane l: channel l%16 of a block, 8
+//     k-values), the activations B (lane l: row l%16, the same 8 k-values); the 16
+//     bytes a lane holds of a tiled 64-k block (k-offsets 16*(l/16)..+15) feed two
+//     MFMAs (their first and second 8 k), and the activation operands are gathered in
+//     the same k order.  The result of lane l holds channels 4*(l/16)+r of row l%16.
+//   * A tile whose steps span several workgroups is completed by exchange: each wave
+//     leaves its FP32 partial sums in a slot of the workspace (agent-coherent) and sets
+//     its flag to the call's tag; a wave that then finds every piece's flag set claims
+//     the tile through its done word and adds the pieces in K order, so the sum does
+//     not depend on which workgroup finishes last.
+//   * EPI_PF_SILU: h = rne_bf16(silu(g) * u) (+ FP32 taps of g and u).
+//     EPI_PF_RES: out = rne_bf16(d + res) (+ FP32 tap of d).
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -27,18 +43,20 @@ namespace a8w8 {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 4;
-constexpr int kPfMt = 64;             // rows of M per workgroup
-constexpr int kPfRowBytes = 144;      // LDS row pitch (128 B of data + 16 B pad)
-constexpr int kPfStage = kPfMt * kPfRowBytes;
+constexpr int kPfRowBlocks = 4;     // 16-row blocks per wave
+constexpr int kPfTileRows = kPfWaves * kPfRowBlocks * 16;
 
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 16 INT8 weights of one channel -> two BF16 operands of 8, scaled by s.
-__device__ __forceinline__ void dequant16(u32x4 raw, float s, bf16x8& lo, bf16x8& hi) {
+// 16 INT8 weights of one channel -> two BF16 operands of 8 (first and second 8 k).
+__device__ __forceinline__ void dequant16(u32x4 raw, float s, u32x4& lo, u32x4& hi) {
   const float bias = -128.0f * s;
   float f[16];
 #pragma unroll
@@ -51,204 +69,306 @@ __device__ __forceinline__ void dequant16(u32x4 raw, float s, bf16x8& lo, bf16x8
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    lo[e] = static_cast<__bf16>(f[e]);
-    hi[e] = static_cast<__bf16>(f[8 + e]);
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{f[2 * e], f[2 * e + 1]}, bf16x2));
+    hi[e] = __builtin_bit_cast(uint32_t,
+                               __builtin_convertvector(f32x2{f[8 + 2 * e], f[9 + 2 * e]}, bf16x2));
   }
 }
 
-template <int EPI, int NMAT, int CB, int LAYOUT>
-__global__ __launch_bounds__(kPfWaves * kWave) void prefill_gemm_kernel(PrefillGemmArgs p) {
-  __shared__ __align__(16) int8_t bsm[2][kPfStage];
+template <int NCB>
+struct WStage {
+  u32x4 w[NCB / 4];
+  float s[NCB / 4];
+};
+
+struct AStage {
+  u32x4 a[kPfRowBlocks][2];
+};
+
+template <int EPI, int NMAT, int NCB, int LAYOUT>
+__global__ __launch_bounds__(kPfWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_sk_kernel(PrefillGemmArgs p) {
+  static_assert(NCB % 4 == 0 && (NMAT == 1 || NCB % 8 == 0), "tile shape");
+  constexpr int NCH = NCB / 4;                 // weight chunks per thread per step
+  constexpr int kBlkPerMat = NCB / NMAT;       // 16-channel blocks of one weight per tile
+  constexpr int kBufBytes = NCB * 2 * kWave * 16;
+  constexpr int kSlotWave = kPfRowBlocks * NCB * kWave * 4;  // floats per wave and piece
+  __shared__ __align__(16) uint8_t wsm[2][kBufBytes];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid & (kWave - 1);
   const int r16 = lane & 15, g4 = lane >> 4;
-  constexpr int kChPerWg = kPfWaves * 16 * CB;
-  const int ntile = blockIdx.x / p.splits, split = blockIdx.x % p.splits;
-  const int64_t m0 = int64_t(blockIdx.y) * kPfMt;
-  const int64_t ch0 = int64_t(ntile) * kChPerWg + wave * 16 * CB;  // this wave's first channel
-  const int steps_total = static_cast<int>(p.K / 64);
-  const int s0 = static_cast<int>(int64_t(split) * steps_total / p.splits);
-  const int s1 = static_cast<int>(int64_t(split + 1) * steps_total / p.splits);
+  const int32_t wg = static_cast<int32_t>(blockIdx.x);
+  const int32_t S = p.steps;                   // 64-k steps per tile
+  const int32_t SQ = S / 4;                    // quads per tile
+  const int32_t qa = wg * p.q + min(wg, p.r);
+  const int32_t qb = qa + p.q + (wg < p.r ? 1 : 0);
+  const int32_t glast = qb * 4 - 1;            // last step of this workgroup
+  const int64_t K = p.K;
+  const int32_t Mlast = static_cast<int32_t>(p.M - 1);
 
-  // Weight blocks and channel scales of this lane.
-  const int8_t* wblk[NMAT][CB];
-  float sc[NMAT][CB];
-#pragma unroll
-  for (int i = 0; i < NMAT; ++i)
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const int64_t tile16 = ch0 / 16 + c;
-      const int8_t* w = (i == 0) ? p.w0 : p.w1;
-      wblk[i][c] = (LAYOUT == LAYOUT_TILED) ? w + tile16 * 16 * p.K + lane * 16
-                                           : w + (tile16 * 16 + r16) * p.K + g4 * 16;
-      sc[i][c] = ((i == 0) ? p.sw0 : p.sw1)[tile16 * 16 + r16];
-    }
-
-  // Activation staging: a stage is 64 rows x 128 bytes (64 BF16); thread t moves the
-  // 32 bytes (16 BF16) at quarter t%4 of row t/4.
-  const int srow = tid >> 2, squart = tid & 3;
-  const bool srow_ok = m0 + srow < p.M;
-  const uint16_t* asrc = p.act + (srow_ok ? (m0 + srow) : 0) * p.lda + squart * 16;
-  auto stage_load = [&](int t, u32x4 (&v)[2]) {
-    const uint16_t* s = asrc + int64_t(t) * 64;
-    v[0] = *reinterpret_cast<const u32x4*>(s);
-    v[1] = *reinterpret_cast<const u32x4*>(s + 8);
-    if (!srow_ok) v[0] = v[1] = u32x4{0u, 0u, 0u, 0u};
+  // ---- operand fetch for global step g (tile g / S, step g % S), clamped by callers
+  auto tile_of = [&](int32_t g, int32_t& ks, int32_t& mt, int32_t& nt) {
+    const int32_t t = static_cast<int32_t>(p.by_steps.div(static_cast<uint32_t>(g)));
+    ks = g - t * S;
+    nt = static_cast<int32_t>(p.by_mtiles.div(static_cast<uint32_t>(t)));
+    mt = t - nt * p.mtiles;
   };
-  auto stage_store = [&](int buf, const u32x4 (&v)[2]) {
-    int8_t* d = &bsm[buf][srow * kPfRowBytes + squart * 32];
-    reinterpret_cast<u32x4*>(d)[0] = v[0];
-    reinterpret_cast<u32x4*>(d)[1] = v[1];
+  auto load_act = [&](AStage& st, int32_t g) {
+    int32_t ks, mt, nt;
+    tile_of(g, ks, mt, nt);
+#pragma unroll
+    for (int rb = 0; rb < kPfRowBlocks; ++rb) {
+      const int32_t row = min(mt * kPfTileRows + wave * 64 + rb * 16 + r16, Mlast);
+      const uint16_t* src = p.act + static_cast<uint32_t>(row * static_cast<int32_t>(p.lda)) +
+                            ks * 64 + g4 * 16;
+      st.a[rb][0] = *reinterpret_cast<const u32x4*>(src);
+      st.a[rb][1] = *reinterpret_cast<const u32x4*>(src + 8);
+    }
+  };
+  auto load_w = [&](WStage<NCB>& st, int32_t g) {
+    int32_t ks, mt, nt;
+    tile_of(g, ks, mt, nt);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int cb = 4 * c + wave;
+      const int mat = cb / kBlkPerMat;
+      const int64_t t16 = int64_t(nt) * kBlkPerMat + (cb % kBlkPerMat);
+      const int8_t* base = (NMAT == 2 && mat == 1) ? p.w1 : p.w0;
+      const float* sc = (NMAT == 2 && mat == 1) ? p.sw1 : p.sw0;
+      const int8_t* src = (LAYOUT == LAYOUT_TILED)
+                              ? base + t16 * 16 * K + int64_t(ks) * 1024 + lane * 16
+                              : base + (t16 * 16 + r16) * K + int64_t(ks) * 64 + g4 * 16;
+      st.w[c] = __builtin_bit_cast(u32x4, ld16(src));
+      st.s[c] = sc[t16 * 16 + r16];
+    }
+  };
+  auto dequant_store = [&](const WStage<NCB>& st, uint8_t* buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int cb = 4 * c + wave;
+      u32x4 lo, hi;
+      dequant16(st.w[c], st.s[c], lo, hi);
+      *reinterpret_cast<u32x4*>(buf + ((cb * 2 + 0) * kWave + lane) * 16) = lo;
+      *reinterpret_cast<u32x4*>(buf + ((cb * 2 + 1) * kWave + lane) * 16) = hi;
+    }
   };
 
-  f32x4 acc[NMAT][CB][4];
+  f32x4 acc[kPfRowBlocks][NCB];
 #pragma unroll
-  for (int i = 0; i < NMAT; ++i)
+  for (int rb = 0; rb < kPfRowBlocks; ++rb)
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[i][c][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int64_t kStep = (LAYOUT == LAYOUT_TILED) ? 1024 : 64;
-  auto load_w = [&](u32x4 (&wv)[NMAT][CB], int t) {
+  auto mma = [&](const AStage& st, const uint8_t* buf) {
 #pragma unroll
-    for (int i = 0; i < NMAT; ++i)
+    for (int cb = 0; cb < NCB; ++cb) {
+      const u32x4 wlo = *reinterpret_cast<const u32x4*>(buf + ((cb * 2 + 0) * kWave + lane) * 16);
+      const u32x4 whi = *reinterpret_cast<const u32x4*>(buf + ((cb * 2 + 1) * kWave + lane) * 16);
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
-        wv[i][c] = *reinterpret_cast<const u32x4*>(wblk[i][c] + int64_t(t) * kStep);
+      for (int rb = 0; rb < kPfRowBlocks; ++rb) acc[rb][cb] = mfma_bf16(wlo, st.a[rb][0], acc[rb][cb]);
+#pragma unroll
+      for (int rb = 0; rb < kPfRowBlocks; ++rb) acc[rb][cb] = mfma_bf16(whi, st.a[rb][1], acc[rb][cb]);
+    }
   };
-  const int nsteps = s1 - s0;
-  // One 64-k step: prefetch the next weights and activation stage, multiply the
-  // current one, then publish the next stage to LDS.
-  u32x4 sv[2];
-  auto step = [&](int it, const u32x4 (&wc)[NMAT][CB], u32x4 (&wn)[NMAT][CB]) {
-    const int cur = it & 1;
-    const bool more = it + 1 < nsteps;
-    if (more) {
-      stage_load(s0 + it + 1, sv);
-      load_w(wn, s0 + it + 1);
+
+  // ---- tile completion
+  const uint64_t want = p.tag | uint64_t(EPI + 1);
+  auto start_of = [&](int32_t w) { return w * p.q + min(w, p.r); };
+  auto owner_of = [&](int32_t quad) {
+    const int32_t cut = p.r * (p.q + 1);
+    return quad < cut ? quad / (p.q + 1) : p.r + (quad - cut) / p.q;
+  };
+  auto slot_of = [&](int32_t w, int32_t t) {
+    return 2 * w + (t != start_of(w) / SQ ? 1 : 0);
+  };
+  auto finish = [&](int32_t t) {
+    const int32_t nt = t / p.mtiles, mt = t - nt * p.mtiles;
+    const int32_t wa = owner_of(t * SQ), wb = owner_of(t * SQ + SQ - 1);
+    if (wa != wb) {
+      // Publish this wave's piece, then its flag, each agent-coherent and waited for.
+      float* mine = p.slots + (int64_t(slot_of(wg, t)) * kPfWaves + wave) * kSlotWave;
+#pragma unroll
+      for (int rb = 0; rb < kPfRowBlocks; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          store_coherent(reinterpret_cast<int32_t*>(mine + ((rb * NCB + cb) * kWave + lane) * 4),
+                         __builtin_bit_cast(i32x4, acc[rb][cb]));
+      wait_memory_done();
+      uint64_t* myflag = p.flags + int64_t(slot_of(wg, t)) * kPfWaves + wave;
+      if (lane == 0) __hip_atomic_store(myflag, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_memory_done();
+      // Every wave whose flag became visible after all others finds them all set.
+      bool all = true;
+      for (int32_t w = wa; w <= wb; ++w) {
+        const uint64_t f = __hip_atomic_load(p.flags + int64_t(slot_of(w, t)) * kPfWaves + wave,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        all = all && (f == want);
+      }
+      if (!__builtin_amdgcn_readfirstlane(all ? 1 : 0)) return;
+      // Several waves can find them all set: the first to swap the done word to this
+      // call's tag completes the tile (the output may overwrite the residual it reads).
+      uint64_t prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_exchange(p.dones + int64_t(t) * kPfWaves + wave, want,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t plo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev));
+      const uint32_t phi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev >> 32));
+      if (((uint64_t(phi) << 32) | plo) == want) return;
+      // Sum of the pieces in K order (workgroup order), all read back from the slots.
+      for (int32_t w = wa; w <= wb; ++w) {
+        const float* src = p.slots + (int64_t(slot_of(w, t)) * kPfWaves + wave) * kSlotWave;
+        f32x4 v[kPfRowBlocks][NCB];
+#pragma unroll
+        for (int rb = 0; rb < kPfRowBlocks; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            v[rb][cb] = __builtin_bit_cast(
+                f32x4, load_coherent(reinterpret_cast<const int32_t*>(
+                           src + ((rb * NCB + cb) * kWave + lane) * 4)));
+#pragma unroll
+        for (int rb = 0; rb < kPfRowBlocks; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = (w == wa) ? v[rb][cb] : acc[rb][cb] + v[rb][cb];
+      }
     }
-    bf16x8 b[4][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int8_t* rp = &bsm[cur][(mb * 16 + r16) * kPfRowBytes + g4 * 32];
-      b[mb][0] = *reinterpret_cast<const bf16x8*>(rp);
-      b[mb][1] = *reinterpret_cast<const bf16x8*>(rp + 16);
-    }
+    for (int rb = 0; rb < kPfRowBlocks; ++rb) {
+      const int64_t m = int64_t(mt) * kPfTileRows + wave * 64 + rb * 16 + r16;
+      if (m >= p.M) continue;
+      if constexpr (EPI == EPI_PF_SILU) {
 #pragma unroll
-    for (int i = 0; i < NMAT; ++i)
+        for (int cb = 0; cb < kBlkPerMat; ++cb) {
+          const int64_t n = (int64_t(nt) * kBlkPerMat + cb) * 16 + 4 * g4;
+          const f32x4 g = acc[rb][cb], u = acc[rb][kBlkPerMat + cb];
+          if (p.tap_g) *reinterpret_cast<f32x4*>(p.tap_g + m * p.N + n) = g;
+          if (p.tap_u) *reinterpret_cast<f32x4*>(p.tap_u + m * p.N + n) = u;
+          u32x2 o;
+          o[0] = uint32_t(f32_to_bf16_rne(silu_mul(g[0], u[0]))) |
+                 (uint32_t(f32_to_bf16_rne(silu_mul(g[1], u[1]))) << 16);
+          o[1] = uint32_t(f32_to_bf16_rne(silu_mul(g[2], u[2]))) |
+                 (uint32_t(f32_to_bf16_rne(silu_mul(g[3], u[3]))) << 16);
+          *reinterpret_cast<u32x2*>(p.out + m * p.ldo + n) = o;
+        }
+      } else {
 #pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        bf16x8 alo, ahi;
-        dequant16(wc[i][c], sc[i][c], alo, ahi);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          acc[i][c][mb] = mfma_bf16(alo, b[mb][0], acc[i][c][mb]);
-          acc[i][c][mb] = mfma_bf16(ahi, b[mb][1], acc[i][c][mb]);
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int64_t n = (int64_t(nt) * NCB + cb) * 16 + 4 * g4;
+          const f32x4 d = acc[rb][cb];
+          if (p.tap_d) *reinterpret_cast<f32x4*>(p.tap_d + m * p.N + n) = d;
+          const u32x2 rr = *reinterpret_cast<const u32x2*>(p.res + m * p.ldr + n);
+          u32x2 o;
+          o[0] = uint32_t(f32_to_bf16_rne(d[0] + bf16_lo(rr[0]))) |
+                 (uint32_t(f32_to_bf16_rne(d[1] + bf16_hi(rr[0]))) << 16);
+          o[1] = uint32_t(f32_to_bf16_rne(d[2] + bf16_lo(rr[1]))) |
+                 (uint32_t(f32_to_bf16_rne(d[3] + bf16_hi(rr[1]))) << 16);
+          *reinterpret_cast<u32x2*>(p.out + m * p.ldo + n) = o;
         }
       }
-    if (more) stage_store(cur ^ 1, sv);
-    __syncthreads();
+    }
   };
 
-  u32x4 wA[NMAT][CB], wB[NMAT][CB];
-  if (nsteps > 0) {
-    stage_load(s0, sv);
-    load_w(wA, s0);
-    stage_store(0, sv);
-  }
-  __syncthreads();
-  for (int it = 0; it < nsteps; it += 2) {
-    step(it, wA, wB);
-    if (it + 1 >= nsteps) break;
-    step(it + 1, wB, wA);
-  }
+  // ---- the pipeline.  Invariant at the start of step g (stage j = g % 4): A[j] holds
+  // (or is loading) the activations of step g, A[j+1], A[j+2] those of g+1, g+2;
+  // R[j+1..j+3] the raw weights of steps g+1..g+3; LDS buffer g%2 the dequantized
+  // weights of step g.  Loads past the last step re-read the last step (never used).
+  AStage A[4];
+  WStage<NCB> R[4];
+  // The prologue issues its loads in the steady state's order (the scheduling barriers
+  // keep them there): the loop head's waits are derived from every path into it, so a
+  // load issued late here would make each iteration wait for nearly all of its loads.
+  const int32_t g0 = qa * 4;
+  load_act(A[0], g0);
+  load_w(R[0], g0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(R[1], min(g0 + 1, glast));
+  __builtin_amdgcn_sched_barrier(0);
+  load_act(A[1], min(g0 + 1, glast));
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(R[2], min(g0 + 2, glast));
+  __builtin_amdgcn_sched_barrier(0);
+  load_act(A[2], min(g0 + 2, glast));
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(R[3], min(g0 + 3, glast));
+  __builtin_amdgcn_sched_barrier(0);
+  dequant_store(R[0], wsm[0]);
+  lds_barrier();
 
-  // Epilogue.  Lane l holds channels 4*(l/16)+r of row l%16 for each block.
+  auto step = [&](auto J, int32_t g) {
+    constexpr int j = decltype(J)::value;
+    load_act(A[(j + 3) & 3], min(g + 3, glast));
+    load_w(R[j], min(g + 4, glast));
+    dequant_store(R[(j + 1) & 3], wsm[(j + 1) & 1]);
+    mma(A[j], wsm[j & 1]);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int32_t Q = qa; Q < qb; ++Q) {
+    const int32_t g = Q * 4;
+    step(std::integral_constant<int, 0>{}, g);
+    step(std::integral_constant<int, 1>{}, g + 1);
+    step(std::integral_constant<int, 2>{}, g + 2);
+    step(std::integral_constant<int, 3>{}, g + 3);
+    const int32_t t = static_cast<int32_t>(p.by_steps.div(static_cast<uint32_t>(g)));
+    if (Q + 1 == qb || Q + 1 == (t + 1) * SQ) {
+      finish(t);
 #pragma unroll
-  for (int c = 0; c < CB; ++c)
+      for (int rb = 0; rb < kPfRowBlocks; ++rb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int64_t m = m0 + mb * 16 + r16;
-      if (m >= p.M) continue;
-      const int64_t n = ch0 + c * 16 + 4 * g4;
-      if constexpr (EPI == EPI_PF_SILU) {
-        const f32x4 g = acc[0][c][mb], u = acc[NMAT - 1][c][mb];
-        if (p.tap_g) *reinterpret_cast<f32x4*>(p.tap_g + m * p.N + n) = g;
-        if (p.tap_u) *reinterpret_cast<f32x4*>(p.tap_u + m * p.N + n) = u;
-        u32x2 o;
-        o[0] = uint32_t(f32_to_bf16_rne(silu_mul(g[0], u[0]))) |
-               (uint32_t(f32_to_bf16_rne(silu_mul(g[1], u[1]))) << 16);
-        o[1] = uint32_t(f32_to_bf16_rne(silu_mul(g[2], u[2]))) |
-               (uint32_t(f32_to_bf16_rne(silu_mul(g[3], u[3]))) << 16);
-        *reinterpret_cast<u32x2*>(p.out_bf16 + m * p.ldo + n) = o;
-      } else {
-        *reinterpret_cast<f32x4*>(p.part + (int64_t(split) * p.M + m) * p.N + n) = acc[0][c][mb];
-      }
+        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  }
 }
 
-// out = rne_bf16(fl32(sum_s part[s]) + res), partial sums added in split order.
-__global__ __launch_bounds__(256) void reduce_residual_kernel(const float* part, int splits,
-                                                              int64_t MN, const uint16_t* res,
-                                                              uint16_t* out, float* tap_d) {
-  for (int64_t i4 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i4 < MN / 4;
-       i4 += int64_t(gridDim.x) * blockDim.x) {
-    f32x4 s = reinterpret_cast<const f32x4*>(part)[i4];
-    for (int j = 1; j < splits; ++j) s += reinterpret_cast<const f32x4*>(part + j * MN)[i4];
-    if (tap_d) reinterpret_cast<f32x4*>(tap_d)[i4] = s;
-    const u32x2 rr = reinterpret_cast<const u32x2*>(res)[i4];
-    const float y0 = s[0] + bf16_lo(rr[0]), y1 = s[1] + bf16_hi(rr[0]);
-    const float y2 = s[2] + bf16_lo(rr[1]), y3 = s[3] + bf16_hi(rr[1]);
-    u32x2 o;
-    o[0] = uint32_t(f32_to_bf16_rne(y0)) | (uint32_t(f32_to_bf16_rne(y1)) << 16);
-    o[1] = uint32_t(f32_to_bf16_rne(y2)) | (uint32_t(f32_to_bf16_rne(y3)) << 16);
-    reinterpret_cast<u32x2*>(out)[i4] = o;
-  }
+template <int EPI, int NMAT, int NCB>
+hipError_t launch_layout(const PrefillGemmArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.grid)), block(kPfWaves * kWave);
+  if (a.layout == LAYOUT_TILED)
+    hipLaunchKernelGGL((prefill_sk_kernel<EPI, NMAT, NCB, LAYOUT_TILED>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_sk_kernel<EPI, NMAT, NCB, LAYOUT_ROWMAJOR>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-int prefill_channels_per_wg(int epi) { return kPfWaves * 16 * (epi == EPI_PF_SILU ? 2 : 4); }
+int prefill_tile_channels(int epi) { return epi == EPI_PF_SILU ? 64 : 128; }
 
-hipError_t launch_prefill_gemm(const PrefillGemmArgs& a, hipStream_t stream) {
-  if (a.M == 0) return hipSuccess;
-  const int chw = prefill_channels_per_wg(a.epi);
-  const dim3 grid(static_cast<unsigned>((a.N / chw) * a.splits),
-                  static_cast<unsigned>((a.M + kPfMt - 1) / kPfMt));
-  const dim3 block(kPfWaves * kWave);
-  const bool tiled = a.layout == LAYOUT_TILED;
-  if (a.epi == EPI_PF_SILU) {
-    if (tiled)
-      hipLaunchKernelGGL((prefill_gemm_kernel<EPI_PF_SILU, 2, 2, LAYOUT_TILED>), grid, block, 0,
-                         stream, a);
-    else
-      hipLaunchKernelGGL((prefill_gemm_kernel<EPI_PF_SILU, 2, 2, LAYOUT_ROWMAJOR>), grid, block,
-                         0, stream, a);
-  } else {
-    if (tiled)
-      hipLaunchKernelGGL((prefill_gemm_kernel<EPI_PF_PARTIAL, 1, 4, LAYOUT_TILED>), grid, block,
-                         0, stream, a);
-    else
-      hipLaunchKernelGGL((prefill_gemm_kernel<EPI_PF_PARTIAL, 1, 4, LAYOUT_ROWMAJOR>), grid,
-                         block, 0, stream, a);
+PrefillPlan plan_prefill(int epi, int64_t M, int64_t N, int64_t K) {
+  PrefillPlan pl{};
+  pl.mtiles = static_cast<int32_t>((M + kPfTileRows - 1) / kPfTileRows);
+  pl.ntiles = static_cast<int32_t>(N / prefill_tile_channels(epi));
+  pl.steps = static_cast<int32_t>(K / 64);
+  const int64_t quads = int64_t(pl.mtiles) * pl.ntiles * (pl.steps / 4);
+  pl.grid = static_cast<int32_t>(quads < kPrefillGrid ? quads : kPrefillGrid);
+  if (pl.grid > 0) {
+    pl.q = static_cast<int32_t>(quads / pl.grid);
+    pl.r = static_cast<int32_t>(quads % pl.grid);
   }
-  return hipGetLastError();
+  return pl;
 }
 
-hipError_t launch_reduce_residual(const float* part, int splits, int64_t M, int64_t N,
-                                  const uint16_t* res, uint16_t* out, float* tap_d,
-                                  hipStream_t stream) {
-  const int64_t n4 = M * N / 4;
-  if (n4 == 0) return hipSuccess;
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(reduce_residual_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     stream, part, splits, M * N, res, out, tap_d);
-  return hipGetLastError();
+size_t prefill_slot_floats() {
+  return size_t(kPfWaves) * kPfRowBlocks * 8 * kWave * 4;  // one piece of an 8-block tile
+}
+
+hipError_t launch_prefill_gemm(const PrefillGemmArgs& in, hipStream_t stream) {
+  if (in.M == 0) return hipSuccess;
+  PrefillGemmArgs a = in;
+  const PrefillPlan pl = plan_prefill(a.epi, a.M, a.N, a.K);
+  if (pl.grid <= 0) return hipSuccess;
+  a.mtiles = pl.mtiles;
+  a.steps = pl.steps;
+  a.q = pl.q;
+  a.r = pl.r;
+  a.grid = pl.grid;
+  a.by_steps = FastDiv(static_cast<uint32_t>(pl.steps));
+  a.by_mtiles = FastDiv(static_cast<uint32_t>(pl.mtiles));
+  if (a.epi == EPI_PF_SILU) return launch_layout<EPI_PF_SILU, 2, 8>(a, stream);
+  if (a.epi == EPI_PF_RES) return launch_layout<EPI_PF_RES, 1, 8>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace a8w8

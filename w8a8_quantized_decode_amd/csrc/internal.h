@@ -180,33 +180,50 @@ bool streamk_fusable(const StreamKPlan& pl, int64_t M, int64_t K_in, bool bf16_r
 hipError_t launch_streamk(const StreamKArgs& a, const StreamKPlan& pl, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill GEMM
+// Stream-K W8A16 GEMM over tiles of 256 rows x 64 (Gate/Up: 64 Gate + the same 64 Up
+// channels) or 128 (Down) channels; the (tile, 64-k step) sequence is dealt in runs of
+// whole quads (4 steps) to a grid of at most kPrefillGrid workgroups.  Needs K % 256 == 0
+// and N a multiple of prefill_tile_channels(epi).
 enum PrefillEpilogue : int {
-  EPI_PF_SILU = 10,     // two weights: h = rne_bf16(silu(g) * u) -> out_bf16
-  EPI_PF_PARTIAL = 11   // one weight, K split `splits` ways: FP32 partials -> part
+  EPI_PF_SILU = 10,     // two weights: h = rne_bf16(silu(g) * u) -> out
+  EPI_PF_RES = 11       // one weight: out = rne_bf16(acc + res)
 };
+constexpr int32_t kPrefillGrid = 256;
+
+struct PrefillPlan {
+  int32_t mtiles, ntiles, steps;  // tiles along M and N; 64-k steps per tile
+  int32_t grid, q, r;             // workgroups w < r take q + 1 quads, the others q
+};
+PrefillPlan plan_prefill(int epi, int64_t M, int64_t N, int64_t K);
+int prefill_tile_channels(int epi);
+// FP32 elements of one exchange slot; a launch uses 2 * grid slots, 4 flags per slot
+// and 4 done words per tile.
+size_t prefill_slot_floats();
 
 struct PrefillGemmArgs {
   int epi, layout;
   int64_t M, N, K;
-  int splits;               // K splits (EPI_PF_PARTIAL), else 1
-  const uint16_t* act;      // [M, lda] BF16 activations
+  const uint16_t* act;      // [M, lda] BF16 activations, M * lda < 2^31
   int64_t lda;
   const int8_t* w0;
   const float* sw0;
   const int8_t* w1;         // EPI_PF_SILU: the Up weight
   const float* sw1;
-  uint16_t* out_bf16;       // EPI_PF_SILU: [M, ldo]
+  uint16_t* out;            // [M, ldo] BF16: h (EPI_PF_SILU) or the block output
   int64_t ldo;
-  float* part;              // EPI_PF_PARTIAL: [splits, M, N]
+  const uint16_t* res;      // EPI_PF_RES: [M, ldr] BF16 residual (may alias out)
+  int64_t ldr;
   float* tap_g;             // EPI_PF_SILU taps: [M, N] FP32 accumulators or nullptr
   float* tap_u;
+  float* tap_d;             // EPI_PF_RES tap: [M, N] FP32 accumulator or nullptr
+  float* slots;             // exchange workspace (see prefill_slot_floats)
+  uint64_t* flags;
+  uint64_t* dones;
+  uint64_t tag;             // the call's tag (low 24 bits zero)
+  // Filled in by launch_prefill_gemm from plan_prefill.
+  int32_t mtiles, steps, grid, q, r;
+  FastDiv by_steps, by_mtiles;
 };
-// Output channels one workgroup covers (N must be a multiple of it).
-int prefill_channels_per_wg(int epi);
 hipError_t launch_prefill_gemm(const PrefillGemmArgs& a, hipStream_t stream);
-// out = rne_bf16(sum_s part[s] + res) over [M, N] (M * N % 4 == 0); tap_d gets the sum.
-hipError_t launch_reduce_residual(const float* part, int splits, int64_t M, int64_t N,
-                                  const uint16_t* res, uint16_t* out, float* tap_d,
-                                  hipStream_t stream);
 
 }  // namespace a8w8
