@@ -35,6 +35,14 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The prefill GEMM keeps its MFMA accumulators in architectural
+# VGPRs: its operand stages fill the accumulation registers, and with accumulators there
+# too the allocator rotates them through copies every loop iteration.
+FILE_FLAGS = {
+    "gemm_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -49,7 +57,8 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + FLAGS
+    cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + FLAGS + FILE_FLAGS.get(
+        os.path.basename(src), [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -217,8 +217,8 @@ StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int6
 
 // ------------------------------------------------------------------ prefill (W8A16)
 struct PrefillBuffers {
-  uint16_t* a;       // [M, H] BF16 activations rne_bf16(RMSNorm(x))
-  uint16_t* h;       // [M, I] BF16 silu(g) * u
+  uint16_t* a;       // BF16 activations rne_bf16(RMSNorm(x)), row-block tiled
+  uint16_t* h;       // BF16 silu(g) * u, row-block tiled
   float* slots;      // stream-K exchange slots
   uint64_t* flags;   // one per slot and wave
   uint64_t* dones;   // one per tile and wave
@@ -232,8 +232,9 @@ PrefillBuffers carve_prefill(Carver& c, int64_t M, int64_t H, int64_t I) {
   const int64_t tiles_dn = int64_t(dn.mtiles) * dn.ntiles;
   const int64_t tiles = tiles_gu > tiles_dn ? tiles_gu : tiles_dn;
   PrefillBuffers b{};
-  b.a = c.take<uint16_t>(size_t(M) * H);
-  b.h = c.take<uint16_t>(size_t(M) * I);
+  const int64_t Mp = (M + 15) / 16 * 16;  // the tiled layout pads rows to 16
+  b.a = c.take<uint16_t>(size_t(Mp) * H);
+  b.h = c.take<uint16_t>(size_t(Mp) * I);
   b.slots = c.take<float>(size_t(2 * grid) * prefill_slot_floats());
   b.flags = c.take<uint64_t>(size_t(2 * grid) * 4);
   b.dones = c.take<uint64_t>(size_t(tiles) * 4);
@@ -262,6 +263,7 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   q.K = H;
   q.xn_tap = t ? t->xn : nullptr;
   q.a_bf16 = b.a;
+  q.a_bf16_tiled = 1;
   q.a_bf16_tap = t ? t->a_bf16 : nullptr;
   q.write_codes = 0;
   A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_POST));
@@ -276,13 +278,12 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   g.N = I;
   g.K = H;
   g.act = b.a;
-  g.lda = H;
   g.w0 = gate.w;
   g.sw0 = gate.scale;
   g.w1 = up.w;
   g.sw1 = up.scale;
   g.out = b.h;
-  g.ldo = I;
+  g.tap_h = t ? t->h_bf16 : nullptr;
   g.tap_g = t ? t->g : nullptr;
   g.tap_u = t ? t->u : nullptr;
   g.slots = b.slots;
@@ -292,9 +293,6 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   A8W8_HIP(tm.before(A8W8_KERNEL_GATE_UP));
   A8W8_HIP(launch_prefill_gemm(g, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_GATE_UP));
-  if (t && t->h_bf16)
-    A8W8_HIP(hipMemcpyAsync(t->h_bf16, b.h, size_t(M) * I * sizeof(uint16_t),
-                            hipMemcpyDeviceToDevice, st));
 
   // Down, FP32 accumulate, out = rne_bf16(d + res) in the same kernel.
   PrefillGemmArgs d{};
@@ -304,7 +302,6 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   d.N = H;
   d.K = I;
   d.act = b.h;
-  d.lda = I;
   d.w0 = down.w;
   d.sw0 = down.scale;
   d.out = out;

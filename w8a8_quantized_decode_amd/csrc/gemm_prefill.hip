@@ -21,7 +21,10 @@
 //     u * s + (-128 * s), whose exact value is w * s, so its single rounding gives
 //     fl32(w * s); FP32 -> BF16 is the RNE conversion.
 //   * Activations: wave w owns rows 64w..64w+63 of the tile and loads its BF16 operands
-//     straight from global memory into registers, three steps ahead of use.
+//     straight from global memory into registers, three steps ahead of use.  They are
+//     stored row-block tiled (rowblock_tiled_index), so each load instruction reads one
+//     contiguous 1 KB (8 whole cache lines); the loads of a step are spread between its
+//     matrix-core blocks so that none waits for the address unit in front of an MFMA.
 //   * Matrix-core operands: the weights are A (lane l: channel l%16 of a block, 8
 //     k-values), the activations B (lane l: row l%16, the same 8 k-values); the 16
 //     bytes a lane holds of a tiled 64-k block (k-offsets 16*(l/16)..+15) feed two
@@ -32,7 +35,8 @@
 //     its flag to the call's tag; a wave that then finds every piece's flag set claims
 //     the tile through its done word and adds the pieces in K order, so the sum does
 //     not depend on which workgroup finishes last.
-//   * EPI_PF_SILU: h = rne_bf16(silu(g) * u) (+ FP32 taps of g and u).
+//   * EPI_PF_SILU: h = rne_bf16(silu(g) * u), row-block tiled for the Down GEMM (+ FP32
+//     taps of g and u, a row-major tap of h).
 //     EPI_PF_RES: out = rne_bf16(d + res) (+ FP32 tap of d).
 #include <type_traits>
 
@@ -107,7 +111,6 @@ void prefill_sk_kernel(PrefillGemmArgs p) {
   const int32_t qb = qa + p.q + (wg < p.r ? 1 : 0);
   const int32_t glast = qb * 4 - 1;            // last step of this workgroup
   const int64_t K = p.K;
-  const int32_t Mlast = static_cast<int32_t>(p.M - 1);
 
   // ---- operand fetch for global step g (tile g / S, step g % S), clamped by callers
   auto tile_of = [&](int32_t g, int32_t& ks, int32_t& mt, int32_t& nt) {
@@ -116,34 +119,44 @@ void prefill_sk_kernel(PrefillGemmArgs p) {
     nt = static_cast<int32_t>(p.by_mtiles.div(static_cast<uint32_t>(t)));
     mt = t - nt * p.mtiles;
   };
-  auto load_act = [&](AStage& st, int32_t g) {
+  // Loads are a wave-uniform base plus a 32-bit per-lane byte offset (the global_load
+  // saddr form), so a step's address arithmetic is almost all scalar.
+  const int32_t row_blocks = static_cast<int32_t>((p.M + 15) / 16);
+  const int64_t k_steps = K / 64;
+  const uint32_t a_lane = static_cast<uint32_t>(lane) * 16u;
+  const uint32_t w_lane = (LAYOUT == LAYOUT_TILED) ? static_cast<uint32_t>(lane) * 16u
+                                                   : static_cast<uint32_t>(r16 * K + g4 * 16);
+  // The two 1 KB operand halves of row block rb of step g (rows past M re-read the last
+  // row block; their results are never stored).
+  auto act_block = [&](int32_t g, int rb) {
     int32_t ks, mt, nt;
     tile_of(g, ks, mt, nt);
+    const int32_t R = min(mt * (kPfTileRows / 16) + wave * kPfRowBlocks + rb, row_blocks - 1);
+    return reinterpret_cast<const uint8_t*>(p.act) + (int64_t(R) * k_steps + ks) * 2048;
+  };
+  auto load_act_rb = [&](AStage& st, int rb, const uint8_t* blk) {
+    st.a[rb][0] = *reinterpret_cast<const u32x4*>(blk + a_lane);
+    st.a[rb][1] = *reinterpret_cast<const u32x4*>(blk + 1024 + a_lane);
+  };
+  auto load_act = [&](AStage& st, int32_t g) {
 #pragma unroll
-    for (int rb = 0; rb < kPfRowBlocks; ++rb) {
-      const int32_t row = min(mt * kPfTileRows + wave * 64 + rb * 16 + r16, Mlast);
-      const uint16_t* src = p.act + static_cast<uint32_t>(row * static_cast<int32_t>(p.lda)) +
-                            ks * 64 + g4 * 16;
-      st.a[rb][0] = *reinterpret_cast<const u32x4*>(src);
-      st.a[rb][1] = *reinterpret_cast<const u32x4*>(src + 8);
-    }
+    for (int rb = 0; rb < kPfRowBlocks; ++rb) load_act_rb(st, rb, act_block(g, rb));
+  };
+  auto load_w_chunk = [&](WStage<NCB>& st, int c, int32_t g) {
+    int32_t ks, mt, nt;
+    tile_of(g, ks, mt, nt);
+    const int cb = 4 * c + wave;
+    const int mat = cb / kBlkPerMat;
+    const int64_t t16 = int64_t(nt) * kBlkPerMat + (cb % kBlkPerMat);
+    const int8_t* wbase = (NMAT == 2 && mat == 1) ? p.w1 : p.w0;
+    const float* sc = (NMAT == 2 && mat == 1) ? p.sw1 : p.sw0;
+    const int8_t* blk = wbase + t16 * 16 * K + int64_t(ks) * ((LAYOUT == LAYOUT_TILED) ? 1024 : 64);
+    st.w[c] = *reinterpret_cast<const u32x4*>(blk + w_lane);
+    st.s[c] = (sc + t16 * 16)[r16];
   };
   auto load_w = [&](WStage<NCB>& st, int32_t g) {
-    int32_t ks, mt, nt;
-    tile_of(g, ks, mt, nt);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int cb = 4 * c + wave;
-      const int mat = cb / kBlkPerMat;
-      const int64_t t16 = int64_t(nt) * kBlkPerMat + (cb % kBlkPerMat);
-      const int8_t* base = (NMAT == 2 && mat == 1) ? p.w1 : p.w0;
-      const float* sc = (NMAT == 2 && mat == 1) ? p.sw1 : p.sw0;
-      const int8_t* src = (LAYOUT == LAYOUT_TILED)
-                              ? base + t16 * 16 * K + int64_t(ks) * 1024 + lane * 16
-                              : base + (t16 * 16 + r16) * K + int64_t(ks) * 64 + g4 * 16;
-      st.w[c] = __builtin_bit_cast(u32x4, ld16(src));
-      st.s[c] = sc[t16 * 16 + r16];
-    }
+    for (int c = 0; c < NCH; ++c) load_w_chunk(st, c, g);
   };
   auto dequant_store = [&](const WStage<NCB>& st, uint8_t* buf) {
 #pragma unroll
@@ -162,17 +175,7 @@ void prefill_sk_kernel(PrefillGemmArgs p) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto mma = [&](const AStage& st, const uint8_t* buf) {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const u32x4 wlo = *reinterpret_cast<const u32x4*>(buf + ((cb * 2 + 0) * kWave + lane) * 16);
-      const u32x4 whi = *reinterpret_cast<const u32x4*>(buf + ((cb * 2 + 1) * kWave + lane) * 16);
-#pragma unroll
-      for (int rb = 0; rb < kPfRowBlocks; ++rb) acc[rb][cb] = mfma_bf16(wlo, st.a[rb][0], acc[rb][cb]);
-#pragma unroll
-      for (int rb = 0; rb < kPfRowBlocks; ++rb) acc[rb][cb] = mfma_bf16(whi, st.a[rb][1], acc[rb][cb]);
-    }
-  };
+
 
   // ---- tile completion
   const uint64_t want = p.tag | uint64_t(EPI + 1);
@@ -250,7 +253,8 @@ void prefill_sk_kernel(PrefillGemmArgs p) {
                  (uint32_t(f32_to_bf16_rne(silu_mul(g[1], u[1]))) << 16);
           o[1] = uint32_t(f32_to_bf16_rne(silu_mul(g[2], u[2]))) |
                  (uint32_t(f32_to_bf16_rne(silu_mul(g[3], u[3]))) << 16);
-          *reinterpret_cast<u32x2*>(p.out + m * p.ldo + n) = o;
+          *reinterpret_cast<u32x2*>(p.out + rowblock_tiled_index(m, n, p.N)) = o;
+          if (p.tap_h) *reinterpret_cast<u32x2*>(p.tap_h + m * p.N + n) = o;
         }
       } else {
 #pragma unroll
@@ -296,29 +300,82 @@ void prefill_sk_kernel(PrefillGemmArgs p) {
   dequant_store(R[0], wsm[0]);
   lds_barrier();
 
+  // One step: per 16-channel block its 8 MFMAs, an eighth of the next step's
+  // dequantization (4 weights of one chunk) so the vector ALU works while the matrix
+  // core runs, and a share of the loads for steps g+3 (activations) and g+4 (weights);
+  // each block's weight operands are read from LDS one block ahead.  The scheduling
+  // barriers keep this order.
   auto step = [&](auto J, int32_t g) {
     constexpr int j = decltype(J)::value;
-    load_act(A[(j + 3) & 3], min(g + 3, glast));
-    load_w(R[j], min(g + 4, glast));
-    dequant_store(R[(j + 1) & 3], wsm[(j + 1) & 1]);
-    mma(A[j], wsm[j & 1]);
+    const uint8_t* rbuf = wsm[j & 1];
+    uint8_t* wbuf = wsm[(j + 1) & 1];
+    const WStage<NCB>& R1 = R[(j + 1) & 3];
+    const AStage& Aj = A[j];
+    const int32_t ga = min(g + 3, glast), gw = min(g + 4, glast);
+    u32x4 wop[2][2];
+    auto read_op = [&](int cb, u32x4 (&o)[2]) {
+      o[0] = *reinterpret_cast<const u32x4*>(rbuf + ((cb * 2 + 0) * kWave + lane) * 16);
+      o[1] = *reinterpret_cast<const u32x4*>(rbuf + ((cb * 2 + 1) * kWave + lane) * 16);
+    };
+    read_op(0, wop[0]);
+    u32x4 dq_lo, dq_hi;
+    constexpr int kPieces = 4 * NCH;  // dequantization pieces: one weight dword each
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      if (cb + 1 < NCB) read_op(cb + 1, wop[(cb + 1) & 1]);
+      // this block's share of the loads for later steps
+      if (cb < kPfRowBlocks) load_act_rb(A[(j + 3) & 3], cb, act_block(ga, cb));
+      if (cb >= kPfRowBlocks && cb < kPfRowBlocks + NCH) load_w_chunk(R[j], cb - kPfRowBlocks, gw);
+#pragma unroll
+      for (int rb = 0; rb < kPfRowBlocks; ++rb)
+        acc[rb][cb] = mfma_bf16(wop[cb & 1][0], Aj.a[rb][0], acc[rb][cb]);
+#pragma unroll
+      for (int rb = 0; rb < kPfRowBlocks; ++rb)
+        acc[rb][cb] = mfma_bf16(wop[cb & 1][1], Aj.a[rb][1], acc[rb][cb]);
+      // dequantization pieces spread evenly over the blocks
+#pragma unroll
+      for (int pc = cb * kPieces / NCB; pc < (cb + 1) * kPieces / NCB; ++pc) {
+        const int c = pc / 4, d = pc % 4;
+        const float sc = R1.s[c];
+        const float bias = -128.0f * sc;
+        const uint32_t u = R1.w[c][d] ^ 0x80808080u;  // biased bytes w + 128
+        float f[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          f[b] = __builtin_fmaf(static_cast<float>((u >> (8 * b)) & 0xFFu), sc, bias);
+        const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{f[0], f[1]}, bf16x2));
+        const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{f[2], f[3]}, bf16x2));
+        u32x4& dst = (d < 2) ? dq_lo : dq_hi;
+        dst[(d & 1) * 2] = p0;
+        dst[(d & 1) * 2 + 1] = p1;
+        if (d == 3) {
+          const int wcb = 4 * c + wave;
+          *reinterpret_cast<u32x4*>(wbuf + ((wcb * 2 + 0) * kWave + lane) * 16) = dq_lo;
+          *reinterpret_cast<u32x4*>(wbuf + ((wcb * 2 + 1) * kWave + lane) * 16) = dq_hi;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int32_t Q = qa; Q < qb; ++Q) {
-    const int32_t g = Q * 4;
-    step(std::integral_constant<int, 0>{}, g);
-    step(std::integral_constant<int, 1>{}, g + 1);
-    step(std::integral_constant<int, 2>{}, g + 2);
-    step(std::integral_constant<int, 3>{}, g + 3);
-    const int32_t t = static_cast<int32_t>(p.by_steps.div(static_cast<uint32_t>(g)));
-    if (Q + 1 == qb || Q + 1 == (t + 1) * SQ) {
-      finish(t);
-#pragma unroll
-      for (int rb = 0; rb < kPfRowBlocks; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Segments: the run of quads of one tile; the pipeline runs on across segment ends.
+  int32_t Q = qa;
+  while (Q < qb) {
+    const int32_t t = static_cast<int32_t>(p.by_steps.div(static_cast<uint32_t>(Q * 4)));
+    const int32_t qe = min(qb, (t + 1) * SQ);
+    for (; Q < qe; ++Q) {
+      const int32_t g = Q * 4;
+      step(std::integral_constant<int, 0>{}, g);
+      step(std::integral_constant<int, 1>{}, g + 1);
+      step(std::integral_constant<int, 2>{}, g + 2);
+      step(std::integral_constant<int, 3>{}, g + 3);
     }
+    finish(t);
+#pragma unroll
+    for (int rb = 0; rb < kPfRowBlocks; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 

@@ -21,7 +21,8 @@ struct QuantRowsArgs {
   float* xn_tap;            // [M, K] FP32 or nullptr
   int8_t* q_tap;            // [M, K] or nullptr (copy of q)
   float* s_tap;             // [M] or nullptr (copy of s)
-  uint16_t* a_bf16;         // [M, K] rne_bf16(v) or nullptr (prefill activations)
+  uint16_t* a_bf16;         // rne_bf16(v) or nullptr (prefill activations)
+  int a_bf16_tiled;         // a_bf16 layout: 0 row-major [M, K]; 1 row-block tiled
   uint16_t* a_bf16_tap;     // [M, K] or nullptr
   int write_codes;          // 0: skip the INT8 codes (prefill only needs a_bf16)
 };
@@ -203,14 +204,14 @@ size_t prefill_slot_floats();
 struct PrefillGemmArgs {
   int epi, layout;
   int64_t M, N, K;
-  const uint16_t* act;      // [M, lda] BF16 activations, M * lda < 2^31
-  int64_t lda;
+  const uint16_t* act;      // BF16 activations, row-block tiled, K columns, M * K < 2^31
   const int8_t* w0;
   const float* sw0;
   const int8_t* w1;         // EPI_PF_SILU: the Up weight
   const float* sw1;
-  uint16_t* out;            // [M, ldo] BF16: h (EPI_PF_SILU) or the block output
-  int64_t ldo;
+  uint16_t* out;            // EPI_PF_SILU: h, row-block tiled (N columns);
+  int64_t ldo;              // EPI_PF_RES: [M, ldo] BF16 block output
+  uint16_t* tap_h;          // EPI_PF_SILU tap: [M, N] row-major h or nullptr
   const uint16_t* res;      // EPI_PF_RES: [M, ldr] BF16 residual (may alias out)
   int64_t ldr;
   float* tap_g;             // EPI_PF_SILU taps: [M, N] FP32 accumulators or nullptr
