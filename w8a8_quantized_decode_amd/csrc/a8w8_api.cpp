@@ -217,27 +217,20 @@ StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int6
 
 // ------------------------------------------------------------------ prefill (W8A16)
 struct PrefillBuffers {
-  uint16_t* a;       // BF16 activations rne_bf16(RMSNorm(x)), row-block tiled
-  uint16_t* h;       // BF16 silu(g) * u, row-block tiled
-  float* slots;      // stream-K exchange slots
-  uint64_t* flags;   // one per slot and wave
-  uint64_t* dones;   // one per tile and wave
+  uint16_t* a;       // BF16 activations rne_bf16(RMSNorm(x)), prefill operand layout
+  uint16_t* h;       // BF16 silu(g) * u, prefill operand layout
+  float* slots;      // partial sums of split tiles
 };
 
 PrefillBuffers carve_prefill(Carver& c, int64_t M, int64_t H, int64_t I) {
   const PrefillPlan gu = plan_prefill(EPI_PF_SILU, M, I, H);
   const PrefillPlan dn = plan_prefill(EPI_PF_RES, M, H, I);
   const int64_t grid = gu.grid > dn.grid ? gu.grid : dn.grid;
-  const int64_t tiles_gu = int64_t(gu.mtiles) * gu.ntiles;
-  const int64_t tiles_dn = int64_t(dn.mtiles) * dn.ntiles;
-  const int64_t tiles = tiles_gu > tiles_dn ? tiles_gu : tiles_dn;
+  const int64_t Mp = (M + 31) / 32 * 32;  // the operand layout pads rows to 32
   PrefillBuffers b{};
-  const int64_t Mp = (M + 15) / 16 * 16;  // the tiled layout pads rows to 16
   b.a = c.take<uint16_t>(size_t(Mp) * H);
   b.h = c.take<uint16_t>(size_t(Mp) * I);
   b.slots = c.take<float>(size_t(2 * grid) * prefill_slot_floats());
-  b.flags = c.take<uint64_t>(size_t(2 * grid) * 4);
-  b.dones = c.take<uint64_t>(size_t(tiles) * 4);
   return b;
 }
 
@@ -251,8 +244,7 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
                             const a8w8_qweight& gate, const a8w8_qweight& up,
                             const a8w8_qweight& down, const uint16_t* res, uint16_t* out,
                             int64_t M, int64_t H, int64_t I, const PrefillBuffers& b,
-                            uint64_t tag, const a8w8_mlp_taps* t, const Timer& tm,
-                            hipStream_t st) {
+                            const a8w8_mlp_taps* t, const Timer& tm, hipStream_t st) {
   // RMSNorm, narrowed to BF16 (the MFMA operand type).
   QuantRowsArgs q{};
   q.x = x;
@@ -287,9 +279,6 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   g.tap_g = t ? t->g : nullptr;
   g.tap_u = t ? t->u : nullptr;
   g.slots = b.slots;
-  g.flags = b.flags;
-  g.dones = b.dones;
-  g.tag = tag;
   A8W8_HIP(tm.before(A8W8_KERNEL_GATE_UP));
   A8W8_HIP(launch_prefill_gemm(g, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_GATE_UP));
@@ -310,9 +299,6 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   d.ldr = H;
   d.tap_d = t ? t->d : nullptr;
   d.slots = b.slots;
-  d.flags = b.flags;
-  d.dones = b.dones;
-  d.tag = tag;
   A8W8_HIP(tm.before(A8W8_KERNEL_DOWN));
   A8W8_HIP(launch_prefill_gemm(d, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_DOWN));
@@ -537,7 +523,7 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
     Carver c(workspace);
     const PrefillBuffers pb = carve_prefill(c, M, H, I);
     return run_mlp_prefill(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M,
-                           H, I, pb, next_call_tag(), taps, tm, st);
+                           H, I, pb, taps, tm, st);
   }
   const ChainPlan pl = make_plan(M, H, I, 0, split_k, false);
   Carver c(workspace);

@@ -27,13 +27,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Row-block tiled BF16 activation layout of the prefill GEMMs: for each block of 16 rows
-// and 64-k step a 2 KB block, two 1 KB halves (the first and second 8 of each 16 k),
-// each in the order of the matrix-core operand (lane l = row l%16, k group l/16; 8 values
-// per lane).  Rows are padded to a multiple of 16.  Element index of (m, k) for K columns:
-__device__ __forceinline__ int64_t rowblock_tiled_index(int64_t m, int64_t k, int64_t K) {
-  return ((m >> 4) * (K >> 6) + (k >> 6)) * 1024 + ((k >> 3) & 1) * 512 +
-         ((m & 15) + 16 * ((k >> 4) & 3)) * 8 + (k & 7);
+// Prefill operand layout of BF16 activations: for each block of 32 rows and 64-k step a
+// 4 KB block of four 1 KB operands (one per 16-k substep), each in the order of the
+// 32x32x16 matrix-core operand: lane l = row l%32 and k-half l/32, 8 values per lane.
+// Rows are padded to a multiple of 32.  Element index of (m, k) for K columns:
+__device__ __forceinline__ int64_t prefill_operand_index(int64_t m, int64_t k, int64_t K) {
+  return ((m >> 5) * (K >> 6) + (k >> 6)) * 2048 + ((k >> 4) & 3) * 512 +
+         ((m & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
 }
 
 // Low / high BF16 of a packed pair.

@@ -22,7 +22,7 @@ struct QuantRowsArgs {
   int8_t* q_tap;            // [M, K] or nullptr (copy of q)
   float* s_tap;             // [M] or nullptr (copy of s)
   uint16_t* a_bf16;         // rne_bf16(v) or nullptr (prefill activations)
-  int a_bf16_tiled;         // a_bf16 layout: 0 row-major [M, K]; 1 row-block tiled
+  int a_bf16_tiled;         // a_bf16 layout: 0 row-major [M, K]; 1 prefill operand layout
   uint16_t* a_bf16_tap;     // [M, K] or nullptr
   int write_codes;          // 0: skip the INT8 codes (prefill only needs a_bf16)
 };
@@ -181,10 +181,11 @@ bool streamk_fusable(const StreamKPlan& pl, int64_t M, int64_t K_in, bool bf16_r
 hipError_t launch_streamk(const StreamKArgs& a, const StreamKPlan& pl, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill GEMM
-// Stream-K W8A16 GEMM over tiles of 256 rows x 64 (Gate/Up: 64 Gate + the same 64 Up
-// channels) or 128 (Down) channels; the (tile, 64-k step) sequence is dealt in runs of
-// whole quads (4 steps) to a grid of at most kPrefillGrid workgroups.  Needs K % 256 == 0
-// and N a multiple of prefill_tile_channels(epi).
+// W8A16 GEMM over tiles of 256 rows x 64 (Gate/Up: 64 Gate + the same 64 Up channels)
+// or 128 (Down) channels.  Each of at most kPrefillGrid workgroups first runs whole tiles
+// (tiles / grid of them); the leftover tiles' quads (4 steps of 64 k) are dealt evenly
+// over all workgroups, and a reduction kernel completes the tiles split that way.
+// Needs K % 256 == 0 and N a multiple of prefill_tile_channels(epi).
 enum PrefillEpilogue : int {
   EPI_PF_SILU = 10,     // two weights: h = rne_bf16(silu(g) * u) -> out
   EPI_PF_RES = 11       // one weight: out = rne_bf16(acc + res)
@@ -192,39 +193,39 @@ enum PrefillEpilogue : int {
 constexpr int32_t kPrefillGrid = 256;
 
 struct PrefillPlan {
-  int32_t mtiles, ntiles, steps;  // tiles along M and N; 64-k steps per tile
-  int32_t grid, q, r;             // workgroups w < r take q + 1 quads, the others q
+  int32_t mtiles, ntiles, tiles;  // tiles along M and N, and in all
+  int32_t quads;                  // quads per tile
+  int32_t grid;                   // workgroups
+  int32_t dp_per_wg, tiles_dp;    // whole tiles per workgroup; tiles run whole
+  int32_t q, r;                   // leftover quads: workgroups w < r take q + 1, others q
 };
 PrefillPlan plan_prefill(int epi, int64_t M, int64_t N, int64_t K);
 int prefill_tile_channels(int epi);
-// FP32 elements of one exchange slot; a launch uses 2 * grid slots, 4 flags per slot
-// and 4 done words per tile.
+// FP32 elements of one exchange slot; a launch uses 2 * grid slots.
 size_t prefill_slot_floats();
 
 struct PrefillGemmArgs {
   int epi, layout;
   int64_t M, N, K;
-  const uint16_t* act;      // BF16 activations, row-block tiled, K columns, M * K < 2^31
+  const uint16_t* act;      // BF16 activations, prefill operand layout, K columns
   const int8_t* w0;
   const float* sw0;
   const int8_t* w1;         // EPI_PF_SILU: the Up weight
   const float* sw1;
-  uint16_t* out;            // EPI_PF_SILU: h, row-block tiled (N columns);
+  uint16_t* out;            // EPI_PF_SILU: h, prefill operand layout (N columns);
   int64_t ldo;              // EPI_PF_RES: [M, ldo] BF16 block output
-  uint16_t* tap_h;          // EPI_PF_SILU tap: [M, N] row-major h or nullptr
   const uint16_t* res;      // EPI_PF_RES: [M, ldr] BF16 residual (may alias out)
   int64_t ldr;
+  uint16_t* tap_h;          // EPI_PF_SILU tap: [M, N] row-major h or nullptr
   float* tap_g;             // EPI_PF_SILU taps: [M, N] FP32 accumulators or nullptr
   float* tap_u;
   float* tap_d;             // EPI_PF_RES tap: [M, N] FP32 accumulator or nullptr
-  float* slots;             // exchange workspace (see prefill_slot_floats)
-  uint64_t* flags;
-  uint64_t* dones;
-  uint64_t tag;             // the call's tag (low 24 bits zero)
+  float* slots;             // partial sums of split tiles (2 * grid slots)
   // Filled in by launch_prefill_gemm from plan_prefill.
-  int32_t mtiles, steps, grid, q, r;
-  FastDiv by_steps, by_mtiles;
+  int32_t mtiles, quads, tiles, grid, dp_per_wg, tiles_dp, q, r;
+  FastDiv by_quads, by_mtiles;
 };
+// Launches the GEMM and, when tiles were split, the reduction kernel.
 hipError_t launch_prefill_gemm(const PrefillGemmArgs& a, hipStream_t stream);
 
 }  // namespace a8w8

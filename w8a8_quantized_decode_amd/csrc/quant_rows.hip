@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(QuantRowsArgs
       for (int i = 0; i < 4; ++i)
         pk[i] = uint32_t(f32_to_bf16_rne(v[2 * i])) | (uint32_t(f32_to_bf16_rne(v[2 * i + 1])) << 16);
       if (p.a_bf16)
-        *reinterpret_cast<u32x4*>(p.a_bf16 + (p.a_bf16_tiled ? rowblock_tiled_index(row, k, K)
+        *reinterpret_cast<u32x4*>(p.a_bf16 + (p.a_bf16_tiled ? prefill_operand_index(row, k, K)
                                                              : row * K + k)) = pk;
       if (p.a_bf16_tap) *reinterpret_cast<u32x4*>(p.a_bf16_tap + row * K + k) = pk;
     }
