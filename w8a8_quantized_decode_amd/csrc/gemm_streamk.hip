@@ -70,6 +70,7 @@ constexpr int64_t kSkTargetWgs = 512;      // two 8-wave workgroups per CU
 constexpr int64_t kSkSmallWgs = 256;       // one per CU for GEMMs under kSkSmallSteps
 constexpr int64_t kSkSmallSteps = 65536;
 constexpr int64_t kSkMinSteps = 4;         // at least 4 KB of weights per wave
+constexpr int64_t kSkTileWgsMin = 256;     // fewest tiles for one tile per workgroup
 constexpr int kPV = 2;                     // prologue vectors of 8 values per thread
 constexpr int64_t kPrologueMax = int64_t(kPV) * 8 * kSkWaves * kWave;  // 8192 values
 constexpr size_t kSkMaxLds = 64 * 1024;
@@ -746,6 +747,10 @@ StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bo
   const int64_t per_seg = (T * C + kSkWaves - 1) / kSkWaves;
   if (wgs < per_seg) wgs = per_seg;
   if (wgs < 1) wgs = 1;
+  // One tile per workgroup when the tiles fill the grid and split evenly over its
+  // waves: every tile is then summed within its workgroup (LDS), with no exchange
+  // between workgroups in the tail.
+  if (C == 1 && T >= kSkTileWgsMin && T <= kSkTargetWgs && St % kSkWaves == 0) wgs = T;
   pl.wgs = static_cast<int>(wgs);
   const int64_t W = wgs * kSkWaves;
   StreamKGeom& g = pl.geom;
