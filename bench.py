@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/layer and INT8-weight HBM GB/s (% of peak), A8W8 decode linears at batch 1"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 GATEUP_KERNEL = 5     # kernel number of the Gate/Up GEMM inside a8w8_layer_linears
 GATEUP_NAME = "streamk_kernel<2, 2,"       # its symbol in rocprofv3 counter tables
 PACK_NAME = "pack_tiled_kernel"            # plain permuting copy: the counter calibration
@@ -42,7 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
-    p.add_argument("--config", type=int, default=2, help="2: layer M=1; 3: 40-layer M=16 stack")
+    p.add_argument("--config", type=int, default=2,
+                   help="2: layer M=1; 3: 40-layer M=16 stack; 4: W8A16 prefill MLP M=256")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -172,6 +174,73 @@ def cpu_baseline(cfg, seconds: float):
             "us_per_layer": round(t_total / done * 1e6, 1)}
 
 
+def bench_prefill(args, cfg, torch, B) -> None:
+    """Secondary line: the W8A16 prefill MLP block (RMSNorm, Gate/Up, SiLU, Down + residual)
+    at M = 256; value in TFLOP/s of the three GEMMs, roofline of the Gate/Up GEMM (with
+    its leftover-tile reduction) against the BF16 matrix-core peak."""
+    from w8a8_quantized_decode_amd import synth
+    M, H, I = cfg.M, cfg.H, cfg.I
+    d = synth.mlp_inputs(cfg, M=M)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    def upw(w, s):
+        rm = up(w)
+        tiled = torch.empty_like(rm)
+        B.a8w8_pack_weight(rm, tiled)
+        return (tiled, up(s), B.LAYOUT_TILED)
+
+    gate, upw_, down = upw(d["w_gate"], d["s_gate"]), upw(d["w_up"], d["s_up"]), upw(d["w_down"], d["s_down"])
+    x, g, res = up(d["x"]), up(d["gamma_post"]), up(d["res"])
+    out = torch.empty_like(res)
+    ws = torch.zeros(B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, M, H, I, 0, cfg.split_k,
+                                            B.MODE_PREFILL_W8A16), dtype=torch.uint8, device="cuda")
+
+    def step(taps=None):
+        B.a8w8_mlp_block(x, g, cfg.eps, gate, upw_, down, res, out, ws, split_k=cfg.split_k,
+                         mode=B.MODE_PREFILL_W8A16, taps=taps)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    flops = 2.0 * M * 3 * H * I
+    evs = []
+    for _ in range(min(args.steps, 50)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in evs:
+        step({"ev_start": a.cuda_event, "ev_stop": b.cuda_event, "ev_kernel": GATEUP_KERNEL})
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    gu_flops = 2.0 * M * 2 * H * I
+    achieved = gu_flops / (k_ms * 1e-3) / 1e12
+    out_line = {
+        "metric": "W8A16 prefill MLP block TFLOP/s (Gate/Up + Down GEMMs), BF16 matrix cores",
+        "value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded PCG64, Qwen3-14B shapes, random INT8 weights)",
+        "config": {"workload": cfg.name, "M": M, "hidden": H, "intermediate": I},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "prefill_gemm_kernel<EPI_PF_SILU> + reduction",
+                     "kernel_us": round(k_ms * 1e3, 2), "algorithmic_flops_per_launch": gu_flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out_line))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -187,8 +256,11 @@ def main():
     from w8a8_quantized_decode_amd import synth
 
     cfg = synth.CONFIGS[args.config]
+    if cfg.kind == "prefill":
+        bench_prefill(args, cfg, torch, B)
+        return
     if cfg.kind not in ("layer", "stack"):
-        raise SystemExit("bench.py times the layer-linears configs (2 or 3)")
+        raise SystemExit("bench.py times the layer-linears configs (2, 3) or the prefill (4)")
     layers = cfg.layers if cfg.kind == "stack" else 1
     M, H, I, n_qkv = cfg.M, cfg.H, cfg.I, cfg.n_qkv
     nsets = layers if cfg.kind == "stack" else max(1, args.sets)
