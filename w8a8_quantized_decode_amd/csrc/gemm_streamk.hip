@@ -208,7 +208,7 @@ __device__ void sk_prologue(const StreamKArgs& p, SM& sm, int8_t* act, int64_t a
 
 // Requantization prologue (Down input): the row scale comes from the per-tile partial
 // maxima, so the K values [klo, klo + len) are quantized straight into LDS in a loop.
-// It runs before any weight load is issued, so none of its waits covers weight loads.
+// The GEMM's first two weight batches are issued before it and stream while it runs.
 template <int NW, typename SM>
 __device__ void sk_requant_prologue(const StreamKArgs& p, SM& sm, int8_t* act, int64_t act_ld,
                                     int64_t klo, int64_t len, bool taps) {
@@ -385,24 +385,29 @@ void streamk_kernel(StreamKArgs p) {
 
   i32x4 wA[U][NMAT], bA[U][MB], wB[U][NMAT], bB[U][MB];
   const int32_t nb = (flive - f0 + U - 1) / U;
-  // The requantization prologue runs first, with no weight load in flight.  For the
-  // BF16 prologue, row 0 of its input is fetched first, then one weight batch, which is
-  // in flight while the prologue runs (a second would crowd its registers); the second
-  // is issued right after it.  Both unconditionally: a guard here would let the
-  // compiler assume the batches may arrive out of order.
+  // Both weight batches of the requantization prologue's GEMM are issued before it, so
+  // the weights stream while it runs (its loads then wait behind them).  For the BF16
+  // prologue, row 0 of its input is fetched first, then one weight batch, which is in
+  // flight while the prologue runs (a second would crowd its registers); the second is
+  // issued right after it.  All unconditionally: a guard here would let the compiler
+  // assume the batches may arrive out of order.
   const bool taps = blockIdx.x == 0;
   if constexpr (PRO == PRO_REQUANT_F32) {
+    load_batch(wA, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(wB, bB);
+    __builtin_amdgcn_sched_barrier(0);
     sk_requant_prologue<NW>(p, sm, act, act_ld, klo, alen, taps);
     if (taps && p.tap_q) sk_requant_taps<NW>(p, sm.row_scale);
   }
   PrologueRegs pre;
   if constexpr (PRO == PRO_QUANT_BF16) sk_prologue_fetch<NW, PRO>(p, klo, alen, pre);
   __builtin_amdgcn_sched_barrier(0);
-  load_batch(wA, bA);
+  if constexpr (PRO != PRO_REQUANT_F32) load_batch(wA, bA);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (PRO == PRO_QUANT_BF16) sk_prologue<NW, PRO>(p, sm, act, act_ld, klo, alen, taps, pre);
   __builtin_amdgcn_sched_barrier(0);
-  load_batch(wB, bB);
+  if constexpr (PRO != PRO_REQUANT_F32) load_batch(wB, bB);
   __builtin_amdgcn_sched_barrier(0);
   // Pairs of batches with no branch inside the body (a branch would let the compiler
   // sink the next batch's loads behind the other batch's compute) and scheduling
