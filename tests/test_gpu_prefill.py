@@ -130,6 +130,18 @@ def test_prefill_toy(M, layout):
     check(*run_prefill(C0, M, layout))
 
 
+# A second toy shape: I = 1024 gives the Down GEMM 4 quads of K per tile (the first toy
+# shape has 3) and 8 leftover workgroups; M = 300 adds a second row tile.
+TOY_I1024 = synth.Config(0, "toy prefill, I=1024", 1, 256, 1024, "prefill",
+                         n_q_heads=2, n_kv_heads=1, head_dim=128)
+
+
+@pytest.mark.parametrize("M", [64, 300])
+def test_prefill_toy_i1024(M):
+    announce(f"prefill toy I=1024 M={M}")
+    check(*run_prefill(TOY_I1024, M, B.LAYOUT_TILED))
+
+
 def test_prefill_qwen3_14b_m256():
     announce("prefill qwen3-14b M=256")
     d, got, want, t, st = run_prefill(C4, 256, B.LAYOUT_TILED)
