@@ -101,12 +101,11 @@ ChainPlan make_plan(int64_t M, int64_t H, int64_t I, int64_t n_qkv, int split_k,
   return ok ? c : plans_for(M, H, I, n_qkv, split_k, layer, false);
 }
 
-// Layout: piece flags, done words and partial-sum slots, shared by the GEMMs (they run
-// one after another on the stream; flags and done words carry the GEMM's number), then
+// Layout: done words and tagged partial-sum slots, shared by the GEMMs (they run one
+// after another on the stream; done words and slot tags carry the GEMM's number), then
 // the intermediate activations.
 struct Buffers {
   int32_t* slots;
-  uint64_t* flags;
   uint64_t* dones;
   int8_t* q_in;
   float* s_in;
@@ -125,11 +124,10 @@ struct Buffers {
 Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
               bool layer) {
   Buffers b{};
-  size_t slot_elems = pl.gu.slot_elems, flag_elems = pl.gu.flag_elems;
+  size_t slot_elems = pl.gu.slot_elems;
   size_t done_elems = pl.gu.done_elems;
   auto widen = [&](const StreamKPlan& q) {
     if (q.slot_elems > slot_elems) slot_elems = q.slot_elems;
-    if (q.flag_elems > flag_elems) flag_elems = q.flag_elems;
     if (q.done_elems > done_elems) done_elems = q.done_elems;
   };
   widen(pl.dn);
@@ -137,7 +135,6 @@ Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, i
     widen(pl.qkv);
     widen(pl.o);
   }
-  b.flags = c.take<uint64_t>(flag_elems);
   b.dones = c.take<uint64_t>(done_elems);
   b.slots = c.take<int32_t>(slot_elems);
   if (layer) {
@@ -210,7 +207,6 @@ StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int6
   g.w0 = w.w;
   g.sw0 = w.scale;
   g.slots = b.slots;
-  g.flags = b.flags;
   g.dones = b.dones;
   return g;
 }

@@ -173,6 +173,37 @@ __device__ __forceinline__ i32x4 load_coherent(const int32_t* p) {
                int32_t(uint32_t(hi >> 32))};
 }
 
+// Tagged 16-byte slot: four 64-bit words, each an INT32 value in its low half and the
+// writer's 32-bit tag in its high half, stored and loaded as relaxed device-scope
+// atomics.  A reader that finds the expected tag in every word has the writer's values
+// (each word is written whole), so no separate ready flag is needed.
+__device__ __forceinline__ void store_tagged(uint64_t* d, i32x4 v, uint32_t tag) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    __hip_atomic_store(d + c, (uint64_t(tag) << 32) | uint32_t(v[c]), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct TaggedX4 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ TaggedX4 load_tagged(const uint64_t* d) {
+  TaggedX4 t;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) t.w[c] = __hip_atomic_load(d + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return t;
+}
+
+// Adds the values of a tagged slot to `s`; clears `ok` unless every word carries `tag`.
+__device__ __forceinline__ void add_tagged(i32x4& s, const TaggedX4& t, uint32_t tag, bool& ok) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    ok = ok && uint32_t(t.w[c] >> 32) == tag;
+    s[c] += int32_t(uint32_t(t.w[c]));
+  }
+}
+
 // Waits until every memory operation this wave has issued has completed (vmcnt = 0),
 // with compiler barriers so that no memory access moves across it.
 __device__ __forceinline__ void wait_memory_done() {

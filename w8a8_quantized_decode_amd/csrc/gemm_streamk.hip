@@ -25,11 +25,13 @@
 //   * When its range is done a wave leaves the INT32 partial sums of the (at most two)
 //     segments it touched in LDS; the workgroup then adds its waves' partials per
 //     segment.  A tile held by one workgroup alone goes straight to the epilogue; for
-//     the others each workgroup stores its piece to a slot of its own and sets the
-//     piece's flag to the call's tag, and a wave that finds every flag of the tile set
-//     adds the slots and runs the epilogue.  Integer addition is exact, so the result
-//     does not depend on the split.  A flag holding another call's tag counts as unset,
-//     so nothing needs clearing between calls, and no address is contended.
+//     the others each workgroup stores its piece to a slot of its own as 64-bit words
+//     that pair each value with the call's tag, waits until they are visible, and reads
+//     every piece of the tile; a wave that finds the call's tag in all of them adds the
+//     slots and runs the epilogue (two memory round trips).  Integer addition is exact,
+//     so the result does not depend on the split.  A word holding another call's tag
+//     counts as missing, so nothing needs clearing between calls, and no address is
+//     contended.
 //   * Fused prologue: every workgroup re-derives the row statistics (RMSNorm sum of
 //     squares and absolute maximum, or the maximum of per-tile partial maxima for the
 //     requantized Down input) and writes the codes of the K chunks its waves consume to
@@ -254,7 +256,8 @@ void streamk_kernel(StreamKArgs p) {
   constexpr bool kFused = PRO != PRO_CODES;
   constexpr int kU0 = kFused ? (NMAT == 2 ? 4 : 6) : 4 / (NMAT * MB);
   constexpr int U = kU0 > 0 ? kU0 : 1;         // k steps per load batch
-  constexpr int kSlot = NMAT * MB * 4 * kWave;  // INT32 per slot
+  constexpr int kSlot = NMAT * MB * 4 * kWave;  // tagged 64-bit words per slot
+  constexpr int kGroup = 8 / (NMAT * MB) > 0 ? 8 / (NMAT * MB) : 1;  // pieces per round trip
   __shared__ SkSmem<NW> sm;
   extern __shared__ __align__(16) int8_t act[];
 
@@ -293,6 +296,34 @@ void streamk_kernel(StreamKArgs p) {
     aoff[mb] = kFused ? (aval[mb] ? row16 : 0) * act_ld - klo + kg * 16
                       : (aval[mb] ? m : 0) * p.lda + kg * 16;
   }
+
+  // Segments sA..sB of this workgroup; after the streaming, wave w runs the epilogue of
+  // sA + w (and of every NW-th one after it).  Its channel scales and residual are
+  // fetched now, ahead of the weights, so the epilogue waits for no load.
+  const int32_t b = static_cast<int32_t>(blockIdx.x);
+  const int32_t nwg = static_cast<int32_t>(gridDim.x);
+  const int32_t wfirst = b * NW;
+  const int32_t wend = (wfirst + NW < G.waves) ? wfirst + NW : G.waves;
+  const int32_t A = sk_wave_start(G, wfirst), B = sk_wave_start(G, wend);
+  const int32_t sA = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(A)));
+  const int32_t sB = B > A ? static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(B - 1))) : sA;
+  const int32_t sg0 = sA + wave;
+  f32x4 sw0p, sw1p;
+  u32x2 resp[MB];
+  auto fetch_epilogue_inputs = [&](int32_t sg) {
+    const int32_t t = sg - static_cast<int32_t>(G.by_tiles.div(static_cast<uint32_t>(sg))) * T;
+    const int64_t en = t * 16 + 4 * kg;
+    sw0p = *reinterpret_cast<const f32x4*>(p.sw0 + en);
+    sw1p = (NMAT == 2) ? *reinterpret_cast<const f32x4*>(p.sw1 + en) : sw0p;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t em = m0 + mb * 16 + row16;
+      resp[mb] = u32x2{0u, 0u};
+      if constexpr (EPI == EPI_BF16_RES || EPI == EPI_DOWN)
+        resp[mb] = *reinterpret_cast<const u32x2*>(p.res + (aval[mb] ? em : 0) * p.ldr + en);
+    }
+  };
+  fetch_epilogue_inputs(sg0 <= sB ? sg0 : sA);
 
   // The range [f0, f1) covers at most two segments (the planner deals at least one
   // wave per segment): steps f < fx belong to segment segA, the others to segA + 1.
@@ -412,9 +443,11 @@ void streamk_kernel(StreamKArgs p) {
   // Pairs of batches with no branch inside the body (a branch would let the compiler
   // sink the next batch's loads behind the other batch's compute) and scheduling
   // barriers between the phases (so no instruction of one batch's compute is hoisted
-  // above the other's), then an odd tail.
+  // above the other's).  The last one to three batches are peeled off so that no load
+  // past the range is left in flight: the exchange's wait and the epilogue would
+  // otherwise wait for it.
   int32_t bi = 0;
-  for (; bi + 1 < nb; bi += 2) {
+  for (; bi + 3 < nb; bi += 2) {
     compute(wA, bA);
     __builtin_amdgcn_sched_barrier(0);
     load_batch(wA, bA);
@@ -424,7 +457,21 @@ void streamk_kernel(StreamKArgs p) {
     load_batch(wB, bB);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (bi < nb) compute(wA, bA);
+  if (bi + 2 < nb) {
+    compute(wA, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(wA, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wB, bB);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wA, bA);
+  } else if (bi + 1 < nb) {
+    compute(wA, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wB, bB);
+  } else if (bi < nb) {
+    compute(wA, bA);
+  }
 
   // Workgroup combine.  Each wave leaves the partial sums of its (at most two) segments
   // in LDS; after one barrier the workgroup's segments are dealt to its waves, and a
@@ -446,22 +493,18 @@ void streamk_kernel(StreamKArgs p) {
   }
   lds_barrier();
 
-  const int32_t b = static_cast<int32_t>(blockIdx.x);
-  const int32_t nwg = static_cast<int32_t>(gridDim.x);
-  const int32_t wfirst = b * NW;
-  const int32_t wend = (wfirst + NW < G.waves) ? wfirst + NW : G.waves;
-  const int32_t A = sk_wave_start(G, wfirst), B = sk_wave_start(G, wend);
   if (B <= A) return;
-  const int32_t sA = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(A)));
-  const int32_t sB = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(B - 1)));
-  int32_t* slots = p.slots + int64_t(blockIdx.y) * (int64_t(T) * C + nwg) * kSlot;
-  uint64_t* flags = p.flags + int64_t(blockIdx.y) * (int64_t(T) * C + nwg);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(p.slots) +
+                    int64_t(blockIdx.y) * (int64_t(T) * C + nwg) * kSlot;
   uint64_t* dones = p.dones + int64_t(blockIdx.y) * T;
   const uint64_t want = p.tag | uint64_t(EPI + 1);
+  // The call's tag (bits 24..55) with this GEMM's number folded into the top bits: the
+  // GEMMs of one call share the slots, and a word from another call or GEMM differs.
+  const uint32_t tag32 = uint32_t(p.tag >> 24) ^ (uint32_t(EPI + 1) << 29);
 
   // The pieces of tile t in chunks [ca, cb) are the slots (c*T + t) + g for the
   // workgroups g touching segment c*T + t, a contiguous run per chunk.  `visit` walks
-  // them in groups of eight: the eight slot indices first (scalar work), then all eight
+  // them in groups of kGroup: the slot indices first (scalar work), then all the group's
   // loads at once, then their use, so a group costs one memory round trip.
   auto wg_of = [&](int32_t f) { return sk_owner(G, f) / NW; };
   auto visit = [&](int32_t t, int32_t ca, int32_t cb, auto&& load, auto&& use) {
@@ -473,10 +516,10 @@ void streamk_kernel(StreamKArgs p) {
     int32_t ic = ca;
     int32_t ig = wg_of((ca * T + t) * Ss);
     int32_t igb = wg_of((ca * T + t) * Ss + Ss - 1);
-    for (int32_t i0 = 0; i0 < n; i0 += 8) {
-      int32_t idx[8];
+    for (int32_t i0 = 0; i0 < n; i0 += kGroup) {
+      int32_t idx[kGroup];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < kGroup; ++k) {
         idx[k] = ic * T + t + ig;
         if (i0 + k + 1 < n) {
           if (ig < igb) {
@@ -489,11 +532,11 @@ void streamk_kernel(StreamKArgs p) {
           }
         }
       }
-      decltype(load(0)) v[8];
+      decltype(load(0)) v[kGroup];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = load(idx[k]);
+      for (int k = 0; k < kGroup; ++k) v[k] = load(idx[k]);
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
+      for (int k = 0; k < kGroup; ++k)
         if (i0 + k < n) use(v[k]);
     }
   };
@@ -519,84 +562,75 @@ void streamk_kernel(StreamKArgs p) {
           part[i][mb] += *reinterpret_cast<const i32x4*>(
               red + (j * 2 + slot) * kRed + ((i * MB + mb) * kWave + lane) * 4);
     }
-    // Epilogue inputs (channel scales, residual) are fetched now, so their latency
-    // overlaps the exchange below.  Lane l owns channels en..en+3 of row em.
+    // Epilogue inputs: prefetched for the first segment; later ones (a workgroup with
+    // more segments than waves) fetch theirs here, before the exchange.  Lane l owns
+    // channels en..en+3 of row em.
+    if (sg != sg0) fetch_epilogue_inputs(sg);
     const int64_t en = t * 16 + 4 * kg;
-    const f32x4 sw0v = *reinterpret_cast<const f32x4*>(p.sw0 + en);
-    const f32x4 sw1v = (NMAT == 2) ? *reinterpret_cast<const f32x4*>(p.sw1 + en) : sw0v;
+    const f32x4 sw0v = sw0p, sw1v = sw1p;
     u32x2 resv[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int64_t em = m0 + mb * 16 + row16;
-      resv[mb] = u32x2{0u, 0u};
-      if constexpr (EPI == EPI_BF16_RES || EPI == EPI_DOWN)
-        resv[mb] = *reinterpret_cast<const u32x2*>(p.res + (aval[mb] ? em : 0) * p.ldr + en);
-    }
+    for (int mb = 0; mb < MB; ++mb) resv[mb] = resp[mb];
 
     // A tile of one chunk held by this workgroup alone needs no exchange.
     const bool interior = C == 1 && wg_of(t * Ss) == b && wg_of(t * Ss + Ss - 1) == b;
     if (!interior) {
-      // Publish the piece: its slot, then its flag (the call's tag and this GEMM's
-      // number), each written agent-coherently and waited for, so the flag is visible
-      // only after the slot is.
-      int32_t* sp = slots + int64_t(sg + b) * kSlot;
+      // Publish the piece as tagged words and wait until they are visible.  Every
+      // owner then reads all pieces of the tile: the owner whose words became visible
+      // last finds every tag, so at least one wave runs the epilogue.
+      uint64_t* sp = slots + int64_t(sg + b) * kSlot;
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          if (aval[mb]) store_coherent(sp + ((i * MB + mb) * kWave + lane) * 4, part[i][mb]);
+          if (aval[mb]) store_tagged(sp + ((i * MB + mb) * kWave + lane) * 4, part[i][mb], tag32);
       wait_memory_done();
-      if (lane == 0)
-        __hip_atomic_store(flags + (sg + b), want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_memory_done();
-      // The epilogue runs in a wave that finds every piece's flag set: at least the one
-      // whose flag became visible last finds them all.
-      bool all = true;
-      visit(t, 0, C,
-            [&](int32_t i) { return __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
-            [&](uint64_t f) { all = all && (f == want); });
-      if (!__builtin_amdgcn_readfirstlane(all ? 1 : 0)) continue;
-      if (p.once) {
-        // Several waves can find them all set; when the output overwrites the residual
-        // it reads, exactly one (the first to swap the tile's done word to this call's
-        // tag) runs the epilogue.  Otherwise a repeated epilogue writes the same values.
-        uint64_t prev = 0;
-        if (lane == 0)
-          prev = __hip_atomic_exchange(dones + t, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t plo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev));
-        const uint32_t phi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev >> 32));
-        if (((uint64_t(phi) << 32) | plo) == want) continue;
-      }
     }
 
-    // Sum of the pieces of chunks [ca, cb) of tile t, per weight and row block.
-    auto gather = [&](i32x4 (&s)[NMAT][MB], int32_t ca, int32_t cb) {
+    // Sum of the pieces of chunks [ca, cb) of tile t, per weight and row block; false
+    // (for the whole wave) when a piece is not yet visible.
+    auto gather = [&](i32x4 (&s)[NMAT][MB], int32_t ca, int32_t cb) -> bool {
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) s[i][mb] = interior ? part[i][mb] : i32x4{0, 0, 0, 0};
-      if (interior) return;
+      if (interior) return true;
       struct Piece {
-        i32x4 v[NMAT][MB];
+        TaggedX4 v[NMAT][MB];
       };
+      bool ok = true;
       visit(t, ca, cb,
             [&](int32_t i) {
               Piece pc;
-              const int32_t* q = slots + int64_t(i) * kSlot;
+              const uint64_t* q = slots + int64_t(i) * kSlot;
 #pragma unroll
               for (int j = 0; j < NMAT; ++j)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                  pc.v[j][mb] = aval[mb] ? load_coherent(q + ((j * MB + mb) * kWave + lane) * 4)
-                                         : i32x4{0, 0, 0, 0};
+                  pc.v[j][mb] = aval[mb] ? load_tagged(q + ((j * MB + mb) * kWave + lane) * 4)
+                                         : TaggedX4{{uint64_t(tag32) << 32, uint64_t(tag32) << 32,
+                                                     uint64_t(tag32) << 32, uint64_t(tag32) << 32}};
               return pc;
             },
             [&](const Piece& pc) {
 #pragma unroll
               for (int j = 0; j < NMAT; ++j)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) s[j][mb] += pc.v[j][mb];
+                for (int mb = 0; mb < MB; ++mb) add_tagged(s[j][mb], pc.v[j][mb], tag32, ok);
             });
+      return __builtin_amdgcn_ballot_w64(!ok) == 0;
+    };
+    // When the output overwrites the residual it reads, exactly one of the waves that
+    // found every piece (the first to swap the tile's done word to this call's tag)
+    // runs the epilogue.  Otherwise a repeated epilogue writes the same values.
+    auto claim = [&]() -> bool {
+      if (interior || !p.once) return true;
+      uint64_t prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_exchange(dones + t, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t plo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev));
+      const uint32_t phi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev >> 32));
+      return ((uint64_t(phi) << 32) | plo) != want;
     };
     float sa[MB];
 #pragma unroll
@@ -607,7 +641,7 @@ void streamk_kernel(StreamKArgs p) {
 
     if constexpr (EPI == EPI_BF16 || EPI == EPI_BF16_RES) {
       i32x4 s[NMAT][MB];
-      gather(s, 0, C);
+      if (!gather(s, 0, C) || !claim()) continue;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if (!aval[mb]) continue;
@@ -630,7 +664,7 @@ void streamk_kernel(StreamKArgs p) {
       }
     } else if constexpr (EPI == EPI_SILU) {
       i32x4 s[NMAT][MB];
-      gather(s, 0, C);
+      if (!gather(s, 0, C) || !claim()) continue;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int64_t em = m0 + mb * 16 + row16;
@@ -658,9 +692,11 @@ void streamk_kernel(StreamKArgs p) {
       const int64_t MN = p.M * p.N;
       const int32_t cpp = C / p.parts;  // chunks per partition
       float tot[MB][4];
-      for (int32_t part = 0; part < p.parts; ++part) {
+      bool have = true;
+      for (int32_t part = 0; part < p.parts && have; ++part) {
         i32x4 s[NMAT][MB];
-        gather(s, part * cpp, (part + 1) * cpp);
+        have = gather(s, part * cpp, (part + 1) * cpp);
+        if (!have) break;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           if (!aval[mb]) continue;
@@ -675,6 +711,7 @@ void streamk_kernel(StreamKArgs p) {
           for (int c = 0; c < 4; ++c) tot[mb][c] = (part == 0) ? pv[c] : tot[mb][c] + pv[c];
         }
       }
+      if (!have || !claim()) continue;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if (!aval[mb]) continue;
@@ -791,8 +828,8 @@ StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bo
     pl.red_off = 0;
   }
   pl.lds = pl.red_off + size_t(kSkWaves) * 2 * nmat * pl.mb * 4 * kWave * sizeof(int32_t);
-  pl.slot_elems = size_t(pl.mgroups) * size_t(T * C + wgs) * size_t(nmat) * pl.mb * 4 * kWave;
-  pl.flag_elems = size_t(pl.mgroups) * size_t(T * C + wgs);
+  // Tagged slots: one 64-bit word (two INT32 elements) per partial sum.
+  pl.slot_elems = 2 * size_t(pl.mgroups) * size_t(T * C + wgs) * size_t(nmat) * pl.mb * 4 * kWave;
   pl.done_elems = size_t(pl.mgroups) * size_t(T);
   return pl;
 }

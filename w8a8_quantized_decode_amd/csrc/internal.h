@@ -95,10 +95,10 @@ struct FastDiv {
 // The work is the sequence of 64-byte K steps of every 16-channel tile, ordered by K
 // chunk, then tile, then step: for the tiled layout each (chunk, tile) segment is one
 // contiguous run of weight bytes.  The sequence is dealt out evenly, in order, to every
-// wave of the grid.  A wave writes the INT32 partial sums of each segment it touches to
-// its own slot and sets the piece's flag to the call's tag; a wave that finds every
-// flag of a tile set adds the slots (integer sums: exact in any order) and runs the
-// epilogue.  The tags make clearing unnecessary.
+// wave of the grid.  A workgroup writes the INT32 partial sums of each shared segment
+// to its own slot, each value paired with the call's tag in one 64-bit word; a wave that
+// finds the call's tag in every word of a tile's pieces adds them (integer sums: exact
+// in any order) and runs the epilogue.  The tags make clearing unnecessary.
 // Geometry of the step sequence (all counts below 2^31).  Waves w < r take q + 1 steps,
 // the others q, in order: wave w starts at w * q + min(w, r).
 struct StreamKGeom {
@@ -147,8 +147,7 @@ struct StreamKArgs {
   float* h;                 // [M, ldh] FP32 (EPI_SILU)
   int64_t ldh;
   float* pmax_out;          // EPI_SILU: [N/16, M] absolute maximum of h per tile
-  int32_t* slots;           // partial-sum slots (StreamKPlan::slot_elems)
-  uint64_t* flags;          // [mgroups, tiles * chunks + workgroups] piece flags
+  int32_t* slots;           // tagged partial-sum slots (StreamKPlan::slot_elems INT32)
   uint64_t* dones;          // [mgroups, tiles] done words (used when `once`)
   int once;                 // the output may overwrite the residual: one epilogue per tile
   // taps (nullptr = off)
@@ -169,7 +168,6 @@ struct StreamKPlan {
   StreamKGeom geom;
   int act_chunks;
   size_t slot_elems;   // INT32 elements of partial-sum slots
-  size_t flag_elems;   // 64-bit piece flags
   size_t done_elems;   // 64-bit done words
   size_t red_off;      // dynamic LDS: codes first (fused), workgroup-combine area here
   size_t lds;          // dynamic LDS bytes
