@@ -210,15 +210,49 @@ __device__ void sk_prologue(const StreamKArgs& p, SM& sm, int8_t* act, int64_t a
 
 // Requantization prologue (Down input): the row scale comes from the per-tile partial
 // maxima, so the K values [klo, klo + len) are quantized straight into LDS in a loop.
-// The GEMM's first two weight batches are issued before it and stream while it runs.
+// Row 0's first partial maxima and values are fetched before any weight load
+// (RequantRegs), so the wait for them never covers weight loads; the rest is loaded here.
+constexpr int kReqPm = 3;  // partial maxima of row 0 per thread fetched ahead
+constexpr int kReqHv = 3;  // 8-value groups of row 0 per thread fetched ahead
+
+struct RequantRegs {
+  float pm[kReqPm];
+  f32x4 hv[kReqHv][2];
+};
+
+template <int NW>
+__device__ __forceinline__ void sk_requant_fetch(const StreamKArgs& p, int64_t klo, int64_t len,
+                                                 RequantRegs& r) {
+  constexpr int NT = NW * kWave;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kReqPm; ++j) {
+    const int64_t k = tid + int64_t(j) * NT;
+    r.pm[j] = p.pmax[(k < p.npmax ? k : 0) * p.M];
+  }
+#pragma unroll
+  for (int i = 0; i < kReqHv; ++i) {
+    const int64_t e = int64_t(tid) * 8 + int64_t(i) * NT * 8;
+    const f32x4* q = reinterpret_cast<const f32x4*>(p.hin + klo + (e < len ? e : 0));
+    r.hv[i][0] = q[0];
+    r.hv[i][1] = q[1];
+  }
+}
+
 template <int NW, typename SM>
 __device__ void sk_requant_prologue(const StreamKArgs& p, SM& sm, int8_t* act, int64_t act_ld,
-                                    int64_t klo, int64_t len, bool taps) {
+                                    int64_t klo, int64_t len, bool taps, const RequantRegs& r) {
   constexpr int NT = NW * kWave;
   const int tid = threadIdx.x;
   for (int m = 0; m < p.M; ++m) {
     float amax = 0.0f;
-    for (int64_t k = tid; k < p.npmax; k += NT) amax = fmaxf(amax, p.pmax[k * p.M + m]);
+    int64_t k = tid;
+    if (m == 0) {
+#pragma unroll
+      for (int j = 0; j < kReqPm; ++j, k += NT)
+        if (k < p.npmax) amax = fmaxf(amax, r.pm[j]);
+    }
+    for (; k < p.npmax; k += NT) amax = fmaxf(amax, p.pmax[k * p.M + m]);
     amax = block_max_f32<NW>(amax, sm.max_slots[m]);
     const float s = amax / 127.0f;
     if (tid == 0) {
@@ -226,7 +260,18 @@ __device__ void sk_requant_prologue(const StreamKArgs& p, SM& sm, int8_t* act, i
       if (taps && p.tap_s) p.tap_s[m] = s;
     }
     const float* hr = p.hin + int64_t(m) * p.ldhin + klo;
-    for (int64_t e = int64_t(tid) * 8; e < len; e += int64_t(NT) * 8) {
+    int64_t e = int64_t(tid) * 8;
+    if (m == 0) {
+#pragma unroll
+      for (int i = 0; i < kReqHv; ++i, e += int64_t(NT) * 8) {
+        if (e < len) {
+          const float v[8] = {r.hv[i][0][0], r.hv[i][0][1], r.hv[i][0][2], r.hv[i][0][3],
+                              r.hv[i][1][0], r.hv[i][1][1], r.hv[i][1][2], r.hv[i][1][3]};
+          *reinterpret_cast<u32x2*>(act + e) = codes8(v, s);
+        }
+      }
+    }
+    for (; e < len; e += int64_t(NT) * 8) {
       float v[8];
       load8_f32(hr + e, v);
       *reinterpret_cast<u32x2*>(act + m * act_ld + e) = codes8(v, s);
@@ -416,20 +461,21 @@ void streamk_kernel(StreamKArgs p) {
 
   i32x4 wA[U][NMAT], bA[U][MB], wB[U][NMAT], bB[U][MB];
   const int32_t nb = (flive - f0 + U - 1) / U;
-  // Both weight batches of the requantization prologue's GEMM are issued before it, so
-  // the weights stream while it runs (its loads then wait behind them).  For the BF16
-  // prologue, row 0 of its input is fetched first, then one weight batch, which is in
-  // flight while the prologue runs (a second would crowd its registers); the second is
-  // issued right after it.  All unconditionally: a guard here would let the compiler
-  // assume the batches may arrive out of order.
+  // Row 0 of the prologue's input is fetched first, then one weight batch, which is in
+  // flight while the prologue runs (its waits then cover no weight load); the second
+  // batch is issued right after it.  All unconditionally: a guard here would let the
+  // compiler assume the batches may arrive out of order.
   const bool taps = blockIdx.x == 0;
   if constexpr (PRO == PRO_REQUANT_F32) {
+    RequantRegs rq;
+    sk_requant_fetch<NW>(p, klo, alen, rq);
+    __builtin_amdgcn_sched_barrier(0);
     load_batch(wA, bA);
     __builtin_amdgcn_sched_barrier(0);
-    load_batch(wB, bB);
-    __builtin_amdgcn_sched_barrier(0);
-    sk_requant_prologue<NW>(p, sm, act, act_ld, klo, alen, taps);
+    sk_requant_prologue<NW>(p, sm, act, act_ld, klo, alen, taps, rq);
     if (taps && p.tap_q) sk_requant_taps<NW>(p, sm.row_scale);
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(wB, bB);
   }
   PrologueRegs pre;
   if constexpr (PRO == PRO_QUANT_BF16) sk_prologue_fetch<NW, PRO>(p, klo, alen, pre);
