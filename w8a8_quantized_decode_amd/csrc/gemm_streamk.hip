@@ -302,7 +302,7 @@ void streamk_kernel(StreamKArgs p) {
   constexpr int kU0 = kFused ? (NMAT == 2 ? 4 : 6) : 4 / (NMAT * MB);
   constexpr int U = kU0 > 0 ? kU0 : 1;         // k steps per load batch
   constexpr int kSlot = NMAT * MB * 4 * kWave;  // tagged 64-bit words per slot
-  constexpr int kGroup = 8 / (NMAT * MB) > 0 ? 8 / (NMAT * MB) : 1;  // pieces per round trip
+  constexpr int kGroup = 4 / (NMAT * MB) > 0 ? 4 / (NMAT * MB) : 1;  // pieces per round trip
   __shared__ SkSmem<NW> sm;
   extern __shared__ __align__(16) int8_t act[];
 
@@ -563,10 +563,11 @@ void streamk_kernel(StreamKArgs p) {
     int32_t ig = wg_of((ca * T + t) * Ss);
     int32_t igb = wg_of((ca * T + t) * Ss + Ss - 1);
     for (int32_t i0 = 0; i0 < n; i0 += kGroup) {
-      int32_t idx[kGroup];
+      int32_t idx[kGroup], chk[kGroup];
 #pragma unroll
       for (int k = 0; k < kGroup; ++k) {
         idx[k] = ic * T + t + ig;
+        chk[k] = ic;
         if (i0 + k + 1 < n) {
           if (ig < igb) {
             ++ig;
@@ -583,7 +584,7 @@ void streamk_kernel(StreamKArgs p) {
       for (int k = 0; k < kGroup; ++k) v[k] = load(idx[k]);
 #pragma unroll
       for (int k = 0; k < kGroup; ++k)
-        if (i0 + k < n) use(v[k]);
+        if (i0 + k < n) use(v[k], chk[k]);
     }
   };
 
@@ -633,13 +634,18 @@ void streamk_kernel(StreamKArgs p) {
       wait_memory_done();
     }
 
-    // Sum of the pieces of chunks [ca, cb) of tile t, per weight and row block; false
-    // (for the whole wave) when a piece is not yet visible.
-    auto gather = [&](i32x4 (&s)[NMAT][MB], int32_t ca, int32_t cb) -> bool {
+    // Sums of the pieces of chunks [ca, cb) of tile t, per weight and row block, into s
+    // for chunks below csplit and into s2 for the others (one round trip per group of
+    // pieces for both); false (for the whole wave) when a piece is not yet visible.
+    auto gather2 = [&](i32x4 (&s)[NMAT][MB], i32x4 (&s2)[NMAT][MB], int32_t ca, int32_t cb,
+                       int32_t csplit) -> bool {
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) s[i][mb] = interior ? part[i][mb] : i32x4{0, 0, 0, 0};
+        for (int mb = 0; mb < MB; ++mb) {
+          s[i][mb] = interior ? part[i][mb] : i32x4{0, 0, 0, 0};
+          s2[i][mb] = i32x4{0, 0, 0, 0};
+        }
       if (interior) return true;
       struct Piece {
         TaggedX4 v[NMAT][MB];
@@ -658,13 +664,22 @@ void streamk_kernel(StreamKArgs p) {
                                                      uint64_t(tag32) << 32, uint64_t(tag32) << 32}};
               return pc;
             },
-            [&](const Piece& pc) {
+            [&](const Piece& pc, int32_t c) {
+              const bool lo = c < csplit;
 #pragma unroll
               for (int j = 0; j < NMAT; ++j)
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) add_tagged(s[j][mb], pc.v[j][mb], tag32, ok);
+                for (int mb = 0; mb < MB; ++mb) {
+                  i32x4 v = {0, 0, 0, 0};
+                  add_tagged(v, pc.v[j][mb], tag32, ok);
+                  if (lo) s[j][mb] += v; else s2[j][mb] += v;
+                }
             });
       return __builtin_amdgcn_ballot_w64(!ok) == 0;
+    };
+    auto gather = [&](i32x4 (&s)[NMAT][MB], int32_t ca, int32_t cb) -> bool {
+      i32x4 unused[NMAT][MB];
+      return gather2(s, unused, ca, cb, cb);
     };
     // When the output overwrites the residual it reads, exactly one of the waves that
     // found every piece (the first to swap the tile's done word to this call's tag)
@@ -739,10 +754,18 @@ void streamk_kernel(StreamKArgs p) {
       const int32_t cpp = C / p.parts;  // chunks per partition
       float tot[MB][4];
       bool have = true;
+      // Two partitions (the usual split) are gathered together in one pass.
+      i32x4 s01[2][NMAT][MB];
+      if (p.parts == 2) have = gather2(s01[0], s01[1], 0, C, cpp);
       for (int32_t part = 0; part < p.parts && have; ++part) {
         i32x4 s[NMAT][MB];
-        have = gather(s, part * cpp, (part + 1) * cpp);
-        if (!have) break;
+        if (p.parts == 2) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) s[0][mb] = part == 0 ? s01[0][0][mb] : s01[1][0][mb];
+        } else {
+          have = gather(s, part * cpp, (part + 1) * cpp);
+          if (!have) break;
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           if (!aval[mb]) continue;
