@@ -202,7 +202,10 @@ StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int6
   g.K = K;
   g.parts = 1;
   g.g = pl.geom;
-  g.act_chunks = pl.act_chunks;
+  g.g2 = pl.geom2;
+  g.wgs1 = pl.wgs1;
+  g.toff2 = pl.toff2;
+  g.act_row = pl.act_row;
   g.tag = tag;
   g.w0 = w.w;
   g.sw0 = w.scale;

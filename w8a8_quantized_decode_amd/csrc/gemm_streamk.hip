@@ -312,9 +312,17 @@ void streamk_kernel(StreamKArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid & (kWave - 1);
   const int row16 = lane & 15, kg = lane >> 4;
-  const StreamKGeom& G = p.g;
+  // Workgroups past wgs1 run the second geometry over tiles toff2.. as its workgroup
+  // b = blockIdx.x - wgs1; tile indices below are local to the geometry (t + toff
+  // addresses weights, channels and per-tile words).
+  const bool second = static_cast<int32_t>(blockIdx.x) >= p.wgs1;
+  const StreamKGeom& G = second ? p.g2 : p.g;
+  const int32_t b = second ? static_cast<int32_t>(blockIdx.x) - p.wgs1
+                           : static_cast<int32_t>(blockIdx.x);
+  const int32_t nwg = second ? static_cast<int32_t>(gridDim.x) - p.wgs1 : p.wgs1;
+  const int32_t toff = second ? p.toff2 : 0;
   const int32_t T = G.tiles, St = G.steps_tile, Ss = G.steps_seg, C = G.chunks;
-  const int32_t wv = static_cast<int32_t>(blockIdx.x) * NW + wave;
+  const int32_t wv = b * NW + wave;
   const int32_t w0 = sk_wave_start(G, wv), w1 = sk_wave_start(G, wv + 1);
   const bool has = w1 > w0;
   // A wave without steps (only when there are fewer steps than waves) addresses step 0
@@ -329,10 +337,10 @@ void streamk_kernel(StreamKArgs p) {
   int64_t klo = 0, act_ld = 0, alen = 0;
   if constexpr (kFused) {
     int32_t c0, c1;
-    sk_wg_chunks(G, static_cast<int32_t>(blockIdx.x), NW, c0, c1);
+    sk_wg_chunks(G, b, NW, c0, c1);
     klo = int64_t(c0) * Ss * 64;
     alen = int64_t(c1 - c0 + 1) * Ss * 64;
-    act_ld = int64_t(p.act_chunks) * Ss * 64;
+    act_ld = p.act_row;
   }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -345,8 +353,6 @@ void streamk_kernel(StreamKArgs p) {
   // Segments sA..sB of this workgroup; after the streaming, wave w runs the epilogue of
   // sA + w (and of every NW-th one after it).  Its channel scales and residual are
   // fetched now, ahead of the weights, so the epilogue waits for no load.
-  const int32_t b = static_cast<int32_t>(blockIdx.x);
-  const int32_t nwg = static_cast<int32_t>(gridDim.x);
   const int32_t wfirst = b * NW;
   const int32_t wend = (wfirst + NW < G.waves) ? wfirst + NW : G.waves;
   const int32_t A = sk_wave_start(G, wfirst), B = sk_wave_start(G, wend);
@@ -357,7 +363,7 @@ void streamk_kernel(StreamKArgs p) {
   u32x2 resp[MB];
   auto fetch_epilogue_inputs = [&](int32_t sg) {
     const int32_t t = sg - static_cast<int32_t>(G.by_tiles.div(static_cast<uint32_t>(sg))) * T;
-    const int64_t en = t * 16 + 4 * kg;
+    const int64_t en = int64_t(t + toff) * 16 + 4 * kg;
     sw0p = *reinterpret_cast<const f32x4*>(p.sw0 + en);
     sw1p = (NMAT == 2) ? *reinterpret_cast<const f32x4*>(p.sw1 + en) : sw0p;
 #pragma unroll
@@ -387,10 +393,10 @@ void streamk_kernel(StreamKArgs p) {
   constexpr int64_t kStep = (LAYOUT == LAYOUT_TILED) ? 1024 : 64;
   const int64_t lane_off = (LAYOUT == LAYOUT_TILED) ? int64_t(lane) * 16
                                                     : int64_t(row16) * p.K + kg * 16;
-  const int64_t wA0 = (LAYOUT == LAYOUT_TILED) ? (int64_t(tA) * St + kA0) * 1024
-                                                : int64_t(tA) * 16 * p.K + kA0 * 64;
-  const int64_t wB0 = (LAYOUT == LAYOUT_TILED) ? (int64_t(tB) * St + kB0) * 1024
-                                                : int64_t(tB) * 16 * p.K + kB0 * 64;
+  const int64_t wA0 = (LAYOUT == LAYOUT_TILED) ? (int64_t(tA + toff) * St + kA0) * 1024
+                                                : int64_t(tA + toff) * 16 * p.K + kA0 * 64;
+  const int64_t wB0 = (LAYOUT == LAYOUT_TILED) ? (int64_t(tB + toff) * St + kB0) * 1024
+                                                : int64_t(tB + toff) * 16 * p.K + kB0 * 64;
   auto wofs = [&](int32_t f) -> int64_t {
     return (f < fx) ? wA0 + int64_t(f - f0) * kStep : wB0 + int64_t(f - fx) * kStep;
   };
@@ -540,9 +546,16 @@ void streamk_kernel(StreamKArgs p) {
   lds_barrier();
 
   if (B <= A) return;
+  // Slots per 64-row group: one per (chunk, tile) segment and one per workgroup of the
+  // first geometry, then the same for the second.
+  const int64_t slots1 = int64_t(p.g.tiles) * p.g.chunks + p.wgs1;
+  const int64_t slots_group =
+      slots1 + (static_cast<int32_t>(gridDim.x) > p.wgs1
+                    ? int64_t(p.g2.tiles) * p.g2.chunks + (static_cast<int32_t>(gridDim.x) - p.wgs1)
+                    : 0);
   uint64_t* slots = reinterpret_cast<uint64_t*>(p.slots) +
-                    int64_t(blockIdx.y) * (int64_t(T) * C + nwg) * kSlot;
-  uint64_t* dones = p.dones + int64_t(blockIdx.y) * T;
+                    (int64_t(blockIdx.y) * slots_group + (second ? slots1 : 0)) * kSlot;
+  uint64_t* dones = p.dones + int64_t(blockIdx.y) * (p.N / 16);
   const uint64_t want = p.tag | uint64_t(EPI + 1);
   // The call's tag (bits 24..55) with this GEMM's number folded into the top bits: the
   // GEMMs of one call share the slots, and a word from another call or GEMM differs.
@@ -613,7 +626,7 @@ void streamk_kernel(StreamKArgs p) {
     // more segments than waves) fetch theirs here, before the exchange.  Lane l owns
     // channels en..en+3 of row em.
     if (sg != sg0) fetch_epilogue_inputs(sg);
-    const int64_t en = t * 16 + 4 * kg;
+    const int64_t en = int64_t(t + toff) * 16 + 4 * kg;
     const f32x4 sw0v = sw0p, sw1v = sw1p;
     u32x2 resv[MB];
 #pragma unroll
@@ -688,7 +701,7 @@ void streamk_kernel(StreamKArgs p) {
       if (interior || !p.once) return true;
       uint64_t prev = 0;
       if (lane == 0)
-        prev = __hip_atomic_exchange(dones + t, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __hip_atomic_exchange(dones + toff + t, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const uint32_t plo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev));
       const uint32_t phi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(prev >> 32));
       return ((uint64_t(phi) << 32) | plo) != want;
@@ -747,7 +760,7 @@ void streamk_kernel(StreamKArgs p) {
         float mx = fmaxf(fmaxf(fabsf(h[0]), fabsf(h[1])), fmaxf(fabsf(h[2]), fabsf(h[3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        if (p.pmax_out && aval[mb] && kg == 0) p.pmax_out[t * p.M + em] = mx;
+        if (p.pmax_out && aval[mb] && kg == 0) p.pmax_out[(t + toff) * p.M + em] = mx;
       }
     } else {  // EPI_DOWN: partitions summed in order, then the residual
       const int64_t MN = p.M * p.N;
@@ -832,6 +845,23 @@ hipError_t launch_epi(const StreamKArgs& a, const StreamKPlan& pl, hipStream_t s
 
 }  // namespace
 
+// Geometry of T tiles of St steps in C chunks dealt to W waves.
+static void set_geom(StreamKGeom& g, int64_t T, int64_t St, int64_t C, int64_t W) {
+  const int64_t Tot = T * St;
+  g.tiles = static_cast<int32_t>(T);
+  g.steps_tile = static_cast<int32_t>(St);
+  g.steps_seg = static_cast<int32_t>(St / C);
+  g.chunks = static_cast<int32_t>(C);
+  g.total = static_cast<int32_t>(Tot);
+  g.waves = static_cast<int32_t>(W);
+  g.q = static_cast<int32_t>(Tot / W);
+  g.r = static_cast<int32_t>(Tot % W);
+  g.by_seg = FastDiv(static_cast<uint32_t>(St / C));
+  g.by_tiles = FastDiv(static_cast<uint32_t>(T));
+  g.by_q = FastDiv(static_cast<uint32_t>(g.q > 0 ? g.q : 1));
+  g.by_q1 = FastDiv(static_cast<uint32_t>(g.q + 1));
+}
+
 StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bool fused) {
   StreamKPlan pl{};
   pl.waves = kSkWaves;
@@ -863,37 +893,45 @@ StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bo
   // between workgroups in the tail.
   if (C == 1 && T >= kSkTileWgsMin && T <= kSkTargetWgs && St % kSkWaves == 0) wgs = T;
   pl.wgs = static_cast<int>(wgs);
-  const int64_t W = wgs * kSkWaves;
-  StreamKGeom& g = pl.geom;
-  g.tiles = static_cast<int32_t>(T);
-  g.steps_tile = static_cast<int32_t>(St);
-  g.steps_seg = static_cast<int32_t>(Ss);
-  g.chunks = static_cast<int32_t>(C);
-  g.total = static_cast<int32_t>(Tot);
-  g.waves = static_cast<int32_t>(W);
-  g.q = static_cast<int32_t>(Tot / W);
-  g.r = static_cast<int32_t>(Tot % W);
-  g.by_seg = FastDiv(static_cast<uint32_t>(Ss));
-  g.by_tiles = FastDiv(static_cast<uint32_t>(T));
-  g.by_q = FastDiv(static_cast<uint32_t>(g.q > 0 ? g.q : 1));
-  g.by_q1 = FastDiv(static_cast<uint32_t>(g.q + 1));
+  pl.wgs1 = pl.wgs;
+  pl.toff2 = 0;
+  set_geom(pl.geom, T, St, C, wgs * kSkWaves);
+  pl.geom2 = pl.geom;
+  // Two per CU, the second workgroup on a CU (blockIdx >= wgs / 2) is dispatched last
+  // and streams last.  When the tiles allow, those workgroups take k whole tiles each
+  // (summed in LDS, no exchange) and the first half runs the stream-K split of the other
+  // tiles, so the exchanges finish while the second half still streams and the kernel's
+  // tail holds no exchange.
+  if (C == 1 && wgs == kSkTargetWgs) {
+    const int64_t half = wgs / 2, k = T / wgs;
+    const int64_t T2 = half * k, T1 = T - T2;
+    if (k >= 1 && (k * St) % kSkWaves == 0 && T1 >= 1 && T1 * C <= half * kSkWaves) {
+      pl.wgs1 = static_cast<int>(half);
+      pl.toff2 = static_cast<int>(T1);
+      set_geom(pl.geom, T1, St, C, half * kSkWaves);
+      set_geom(pl.geom2, T2, St, C, half * kSkWaves);
+    }
+  }
   if (fused) {
     pl.mgroups = 1;
     pl.mb = 1;
-    int32_t span = 1;
+    int64_t row = 0;
     for (int32_t b = 0; b < pl.wgs; ++b) {
+      const bool two = b >= pl.wgs1;
+      const StreamKGeom& gb = two ? pl.geom2 : pl.geom;
       int32_t c0, c1;
-      sk_wg_chunks(g, b, kSkWaves, c0, c1);
-      if (c1 - c0 + 1 > span) span = c1 - c0 + 1;
+      sk_wg_chunks(gb, two ? b - pl.wgs1 : b, kSkWaves, c0, c1);
+      const int64_t bytes = int64_t(c1 - c0 + 1) * gb.steps_seg * 64;
+      if (bytes > row) row = bytes;
     }
-    pl.act_chunks = span;
-    pl.red_off = (size_t(M) * size_t(int64_t(span) * Ss * 64) + 15) / 16 * 16;
+    pl.act_row = row;
+    pl.red_off = (size_t(M) * size_t(row) + 15) / 16 * 16;
   } else {
     pl.mgroups = static_cast<int>((M + 63) / 64);
     const int64_t rows = M < 64 ? M : 64;
     const int64_t b16 = (rows + 15) / 16;
     pl.mb = b16 <= 1 ? 1 : (b16 <= 2 ? 2 : 4);
-    pl.act_chunks = 0;
+    pl.act_row = 0;
     pl.red_off = 0;
   }
   pl.lds = pl.red_off + size_t(kSkWaves) * 2 * nmat * pl.mb * 4 * kWave * sizeof(int32_t);

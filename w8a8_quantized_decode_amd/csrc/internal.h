@@ -116,10 +116,14 @@ struct StreamKArgs {
   int epi, layout, prologue;
   int64_t M, N, K;
   int parts;                // K partitions (EPI_DOWN: split_k), else 1
-  int act_chunks;           // chunks of codes one workgroup keeps in LDS (fused prologue)
+  int64_t act_row;          // bytes of codes per row one workgroup keeps in LDS (fused prologue)
   int64_t red_off;          // byte offset of the workgroup-combine area in dynamic LDS
   uint64_t tag;             // call tag in bits 63..24
   StreamKGeom g;
+  // Workgroups b >= wgs1 run a second geometry g2 over tiles [toff2, toff2 + g2.tiles),
+  // as workgroup b - wgs1 of it (wgs1 = grid.x: one geometry).
+  StreamKGeom g2;
+  int32_t wgs1, toff2;
   // PRO_CODES
   const int8_t* a;          // [M, lda] INT8 codes
   int64_t lda;
@@ -166,7 +170,9 @@ struct StreamKPlan {
   int mgroups;         // grid.y
   int mb;              // 16-row blocks per group (1 with a fused prologue)
   StreamKGeom geom;
-  int act_chunks;
+  StreamKGeom geom2;   // second geometry for workgroups >= wgs1 (see StreamKArgs)
+  int wgs1, toff2;
+  int64_t act_row;
   size_t slot_elems;   // INT32 elements of partial-sum slots
   size_t done_elems;   // 64-bit done words
   size_t red_off;      // dynamic LDS: codes first (fused), workgroup-combine area here
