@@ -78,6 +78,13 @@ __device__ __forceinline__ i32x4 ld16(const int8_t* p) {
   return *reinterpret_cast<const i32x4*>(p);
 }
 
+// Weight bytes are read once per call: a non-temporal load keeps the weight stream from
+// displacing the kernel's code, the activation rows and the exchange words from the
+// caches (each kernel's instruction fetches otherwise queue behind the stream).
+__device__ __forceinline__ i32x4 ld16_stream(const int8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+
 // Dequantized value: fl32(fl32(f(acc) * sa) * sw).
 __device__ __forceinline__ float dq(int32_t acc, float sa, float sw) {
   return (static_cast<float>(acc) * sa) * sw;

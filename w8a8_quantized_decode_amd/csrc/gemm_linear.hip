@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kLinWaves * kWave) void linear_kernel(LinearArgs p)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int tt = min(t + u, ws1 - 1);
-      wv[u] = ld16(wbase + int64_t(tt) * kStep);
+      wv[u] = ld16_stream(wbase + int64_t(tt) * kStep);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) bv[u][mb] = ld16(abase[mb] + int64_t(tt) * 64);
     }

@@ -411,8 +411,8 @@ void streamk_kernel(StreamKArgs p) {
     for (int u = 0; u < U; ++u) {
       const int32_t f = (lf + u < f1) ? lf + u : f1 - 1;
       const int64_t o = wofs(f);
-      wv_[u][0] = ld16(w0l + o);
-      if constexpr (NMAT == 2) wv_[u][1] = ld16(w1l + o);
+      wv_[u][0] = ld16_stream(w0l + o);
+      if constexpr (NMAT == 2) wv_[u][1] = ld16_stream(w1l + o);
       if constexpr (!kFused) {
         const int64_t ks = kstep(f);
 #pragma unroll
