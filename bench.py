@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--config", type=int, default=2,
                    help="2: layer M=1; 3: 40-layer M=16 stack; 4: W8A16 prefill MLP M=256")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", type=int, default=1,
+                   help="also time the steps replayed from one captured HIP graph (0: skip)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="summarise two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then "
@@ -331,6 +333,27 @@ def main():
     us_per_layer = ms_per_step * 1e3 / layers_per_step
     gbs = wbytes_layer * layers_per_step / (ms_per_step * 1e-3) / 1e9
 
+    # The same steps captured once in a HIP graph (one call per weight set, or the stack)
+    # and replayed: the decode GEMMs keep their exchange tags on the device, so replays
+    # are valid calls.  Reported beside the plain-launch figure, labelled.
+    graph_us = None
+    if args.graph:
+        n_cap = 1 if cfg.kind == "stack" else nsets
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(n_cap):
+                step(i)
+        for _ in range(max(1, args.warmup // n_cap)):
+            gr.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // n_cap)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            gr.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t0) / (reps * n_cap * layers_per_step) * 1e6
+        del gr
+
     # Roofline of the dominant kernel: HIP events recorded by the library right before
     # and after the Gate/Up GEMM launch, on the same stream.
     n_ev = min(args.steps, 100)
@@ -370,6 +393,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic (seeded PCG64, Qwen3-14B shapes, random INT8 weights)",
         "us_per_layer": round(us_per_layer, 2),
+        "graph_us_per_layer": round(graph_us, 2) if graph_us is not None else None,
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "config": {"workload": cfg.name, "M": M, "hidden": H, "intermediate": I,
                    "n_qkv": n_qkv, "split_k": cfg.split_k, "layers_per_step": layers_per_step,

@@ -204,10 +204,15 @@ a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
 /*
  * Workspace size in bytes for a8w8_mlp_block (op = A8W8_OP_MLP_BLOCK, n_qkv ignored)
  * or a8w8_layer_linears (op = A8W8_OP_LAYER_LINEARS).  Returns 0 for invalid
- * arguments.  The workspace is scratch: its contents on entry do not matter (each call
- * clears the split-K accumulators it needs in its first kernel) and are unspecified
- * on return.  A workspace can serve later calls of any size it fits; calls that share
- * a workspace must not overlap in time.  The workspace must be 256-byte aligned.
+ * arguments.  The workspace is scratch: its contents on entry do not matter and are
+ * unspecified on return.  Its first 256 bytes hold two tag words that the decode GEMMs
+ * advance on the device (each GEMM reads one and writes the next value to the other);
+ * partial sums exchanged between workgroups carry that tag, so nothing is cleared
+ * between calls, and a call captured into a HIP graph stays correct when replayed (the
+ * tags move on every replay).  A zero-filled workspace is the usual start; any other
+ * content works except with negligible probability (a stale word matching a 32-bit tag).
+ * A workspace can serve later calls of any size it fits; calls that share a workspace
+ * must not overlap in time.  The workspace must be 256-byte aligned.
  */
 size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_qkv,
                             int split_k, int mode);

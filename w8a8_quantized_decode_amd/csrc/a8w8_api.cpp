@@ -46,6 +46,10 @@ struct Carver {
   size_t size() const { return round_up(off, kAlign); }
 };
 
+// Every workspace layout starts with the two tag words of the decode GEMMs, so no
+// other use of the workspace overwrites them between decode calls.
+uint32_t* take_epoch(Carver& c) { return c.take<uint32_t>(2); }
+
 bool valid_split(int s) { return s == 1 || s == 2 || s == 4 || s == 8; }
 
 // Records the caller's timing events around the kernel with role `kernel`.
@@ -105,6 +109,7 @@ ChainPlan make_plan(int64_t M, int64_t H, int64_t I, int64_t n_qkv, int split_k,
 // after another on the stream; done words and slot tags carry the GEMM's number), then
 // the intermediate activations.
 struct Buffers {
+  uint32_t* epoch;          // [2] tag words, alternately read and advanced by the GEMMs
   int32_t* slots;
   uint64_t* dones;
   int8_t* q_in;
@@ -135,6 +140,7 @@ Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, i
     widen(pl.qkv);
     widen(pl.o);
   }
+  b.epoch = take_epoch(c);
   b.dones = c.take<uint64_t>(done_elems);
   b.slots = c.take<int32_t>(slot_elems);
   if (layer) {
@@ -158,20 +164,6 @@ Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, i
   return b;
 }
 
-// Tag of one call, in bits 63..24.  Consecutive calls get consecutive 40-bit tags from
-// a start drawn once per process, so a tagged word left by
-// any earlier call (or never written) carries another tag.
-uint64_t next_call_tag() {
-  static std::atomic<uint64_t> next{[] {
-    std::random_device rd;
-    uint64_t v = (uint64_t(rd()) << 32) ^ uint64_t(rd());
-    v ^= uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
-    return v;
-  }()};
-  const uint64_t n = next.fetch_add(1, std::memory_order_relaxed);
-  return (n & ((uint64_t(1) << 40) - 1)) << 24;
-}
-
 a8w8_status check_mlp_shapes(int64_t M, int64_t H, int64_t I, int split_k) {
   if (M < 0 || H <= 0 || I <= 0) return A8W8_ERR_SHAPE;
   if (!valid_split(split_k)) return A8W8_ERR_SHAPE;
@@ -192,8 +184,10 @@ int layout_of(const a8w8_qweight& w) {
   return w.layout == A8W8_LAYOUT_TILED ? LAYOUT_TILED : LAYOUT_ROWMAJOR;
 }
 
+// GEMM number g of a call (calls run an even number of them) reads tag word g % 2 and
+// advances the other one.
 StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int64_t K,
-                      const a8w8_qweight& w, const Buffers& b, uint64_t tag) {
+                      const a8w8_qweight& w, const Buffers& b, int g_in_call) {
   StreamKArgs g{};
   g.epi = epi;
   g.layout = layout_of(w);
@@ -206,7 +200,8 @@ StreamKArgs gemm_args(int epi, const StreamKPlan& pl, int64_t M, int64_t N, int6
   g.wgs1 = pl.wgs1;
   g.toff2 = pl.toff2;
   g.act_row = pl.act_row;
-  g.tag = tag;
+  g.epoch_in = b.epoch + (g_in_call & 1);
+  g.epoch_out = b.epoch + ((g_in_call + 1) & 1);
   g.w0 = w.w;
   g.sw0 = w.scale;
   g.slots = b.slots;
@@ -227,6 +222,7 @@ PrefillBuffers carve_prefill(Carver& c, int64_t M, int64_t H, int64_t I) {
   const int64_t grid = gu.grid > dn.grid ? gu.grid : dn.grid;
   const int64_t Mp = (M + 31) / 32 * 32;  // the operand layout pads rows to 32
   PrefillBuffers b{};
+  take_epoch(c);
   b.a = c.take<uint16_t>(size_t(Mp) * H);
   b.h = c.take<uint16_t>(size_t(Mp) * I);
   b.slots = c.take<float>(size_t(2 * grid) * prefill_slot_floats());
@@ -324,15 +320,15 @@ hipError_t quant_kernel(const void* x, int64_t ldx, int f32, const uint16_t* gam
   return launch_quant_rows(a, st);
 }
 
-// Enqueues the decode MLP chain (Gate/Up, then Down) under the call's tag.
+// Enqueues the decode MLP chain (Gate/Up, then Down) as GEMMs g0 and g0 + 1 of the call.
 a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
                            const a8w8_qweight& gate, const a8w8_qweight& up,
                            const a8w8_qweight& down, const uint16_t* res, uint16_t* out,
                            int64_t M, int64_t H, int64_t I, int split_k, const ChainPlan& pl,
-                           const Buffers& b, uint64_t tag, const a8w8_mlp_taps* t,
+                           const Buffers& b, int g0, const a8w8_mlp_taps* t,
                            const Timer& tm, hipStream_t st) {
   // Gate/Up GEMM (input RMSNorm + quantization fused or separate), SiLU(g) * u -> h.
-  StreamKArgs g = gemm_args(EPI_SILU, pl.gu, M, I, H, gate, b, tag);
+  StreamKArgs g = gemm_args(EPI_SILU, pl.gu, M, I, H, gate, b, g0);
   g.w1 = up.w;
   g.sw1 = up.scale;
   g.h = b.h;
@@ -365,7 +361,7 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
   A8W8_HIP(tm.after(A8W8_KERNEL_GATE_UP));
 
   // Down: per-row requantization of h, split-K partials, + residual, RNE to BF16.
-  StreamKArgs d = gemm_args(EPI_DOWN, pl.dn, M, H, I, down, b, tag);
+  StreamKArgs d = gemm_args(EPI_DOWN, pl.dn, M, H, I, down, b, g0 + 1);
   d.parts = split_k;
   d.out = out;
   d.ldo = H;
@@ -528,7 +524,7 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
   Carver c(workspace);
   const Buffers b = carve(c, pl, M, H, I, 0, false);
   return run_mlp_decode(x_bf16, gamma_bf16, eps, gate, up, down, residual_bf16, out_bf16, M, H,
-                        I, split_k, pl, b, next_call_tag(), taps, tm, st);
+                        I, split_k, pl, b, 0, taps, tm, st);
 }
 
 a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
@@ -563,10 +559,9 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   const Timer tm(mt, st);
   uint16_t* qkv_buf = qkv_out_bf16 ? qkv_out_bf16 : b.qkv;
 
-  const uint64_t tag = next_call_tag();
 
   // QKV projection (input RMSNorm + quantization fused or separate) -> BF16.
-  StreamKArgs g = gemm_args(EPI_BF16, pl.qkv, M, n_qkv, H, qkv, b, tag);
+  StreamKArgs g = gemm_args(EPI_BF16, pl.qkv, M, n_qkv, H, qkv, b, 0);
   g.out = qkv_buf;
   g.ldo = n_qkv;
   g.tap_acc0 = taps ? taps->acc_qkv : nullptr;
@@ -599,7 +594,7 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
 
   // Identity attention: the Q slice qkv[:, :H] is quantized and fed to O; O adds the
   // layer input as residual -> h1.
-  StreamKArgs og = gemm_args(EPI_BF16_RES, pl.o, M, H, H, o, b, tag);
+  StreamKArgs og = gemm_args(EPI_BF16_RES, pl.o, M, H, H, o, b, 1);
   og.out = b.h1;
   og.ldo = H;
   og.res = x_bf16;
@@ -629,7 +624,7 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
                             hipMemcpyDeviceToDevice, st));
 
   return run_mlp_decode(b.h1, gamma_post_bf16, eps, gate, up, down, b.h1, out_bf16, M, H, I,
-                        split_k, pl, b, tag, mt, tm, st);
+                        split_k, pl, b, 2, mt, tm, st);
 }
 
 }  // extern "C"

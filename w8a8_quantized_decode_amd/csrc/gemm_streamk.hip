@@ -307,6 +307,9 @@ void streamk_kernel(StreamKArgs p) {
   extern __shared__ __align__(16) int8_t act[];
 
   const int tid = threadIdx.x;
+  // This GEMM's tag; the next GEMM on the workspace reads the advanced value.
+  const uint32_t epoch = *p.epoch_in;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *p.epoch_out = epoch + 1;
   // The wave index lives in a scalar register so that every branch around a matrix
   // instruction is wave-uniform (a matrix instruction ignores a partial lane mask).
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -556,10 +559,11 @@ void streamk_kernel(StreamKArgs p) {
   uint64_t* slots = reinterpret_cast<uint64_t*>(p.slots) +
                     (int64_t(blockIdx.y) * slots_group + (second ? slots1 : 0)) * kSlot;
   uint64_t* dones = p.dones + int64_t(blockIdx.y) * (p.N / 16);
-  const uint64_t want = p.tag | uint64_t(EPI + 1);
-  // The call's tag (bits 24..55) with this GEMM's number folded into the top bits: the
-  // GEMMs of one call share the slots, and a word from another call or GEMM differs.
-  const uint32_t tag32 = uint32_t(p.tag >> 24) ^ (uint32_t(EPI + 1) << 29);
+  const uint64_t want = (uint64_t(epoch) << 24) | uint64_t(EPI + 1);
+  // The GEMM's tag with its epilogue number folded into the top bits (never zero, so a
+  // cleared word never matches): every GEMM of every call on this workspace reads a
+  // different tag word value, so a word left by another GEMM or call differs.
+  const uint32_t tag32 = epoch ^ (uint32_t(EPI + 1) << 29);
 
   // The pieces of tile t in chunks [ca, cb) are the slots (c*T + t) + g for the
   // workgroups g touching segment c*T + t, a contiguous run per chunk.  `visit` walks

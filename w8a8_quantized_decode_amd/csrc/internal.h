@@ -118,7 +118,10 @@ struct StreamKArgs {
   int parts;                // K partitions (EPI_DOWN: split_k), else 1
   int64_t act_row;          // bytes of codes per row one workgroup keeps in LDS (fused prologue)
   int64_t red_off;          // byte offset of the workgroup-combine area in dynamic LDS
-  uint64_t tag;             // call tag in bits 63..24
+  // Call tags live on the device: this GEMM's tag is *epoch_in; workgroup (0, 0)
+  // writes *epoch_in + 1 to epoch_out, the word the next GEMM of the chain reads.
+  const uint32_t* epoch_in;
+  uint32_t* epoch_out;
   StreamKGeom g;
   // Workgroups b >= wgs1 run a second geometry g2 over tiles [toff2, toff2 + g2.tiles),
   // as workgroup b - wgs1 of it (wgs1 = grid.x: one geometry).
