@@ -82,6 +82,7 @@ struct SkSmem {
   double sum_slots[kFuseMaxRows][NW];
   float max_slots[kFuseMaxRows][NW];
   float row_scale[kFuseMaxRows];
+  int32_t seg_lo[NW], seg_hi[NW];  // segments of each wave's partial sums (-1: none)
 };
 
 // Row 0's BF16 prologue inputs, fetched before the first weight batch: a wait for them
@@ -536,6 +537,10 @@ void streamk_kernel(StreamKArgs p) {
   {
     const int32_t sb_w = has ? static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(f1 - 1))) : segA;
     const bool crossed = sb_w > segA;
+    if (lane == 0) {
+      sm.seg_lo[wave] = has ? segA : -1;
+      sm.seg_hi[wave] = crossed ? sb_w : -1;
+    }
 #pragma unroll
     for (int i = 0; i < NMAT; ++i)
 #pragma unroll
@@ -612,19 +617,21 @@ void streamk_kernel(StreamKArgs p) {
     for (int i = 0; i < NMAT; ++i)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) part[i][mb] = i32x4{0, 0, 0, 0};
-    for (int32_t j = 0; j < wend - wfirst; ++j) {
-      const int32_t a0 = sk_wave_start(G, wfirst + j), a1 = sk_wave_start(G, wfirst + j + 1);
-      if (a1 <= a0) continue;
-      const int32_t ja = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(a0)));
-      const int32_t jb = static_cast<int32_t>(G.by_seg.div(static_cast<uint32_t>(a1 - 1)));
-      const int slot = (ja == sg) ? 0 : ((jb == sg) ? 1 : -1);
-      if (slot < 0) continue;
+    // Every wave's partial of segment sg (its first or second slot), read in one pass
+    // with no branch, so the LDS reads are issued together and waited for once.
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int32_t lo = sm.seg_lo[j], hi = sm.seg_hi[j];
+      const bool second_slot = hi == sg;
+      const bool use = second_slot || lo == sg;
+      const int32_t* rj = red + (j * 2 + (second_slot ? 1 : 0)) * kRed;
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          part[i][mb] += *reinterpret_cast<const i32x4*>(
-              red + (j * 2 + slot) * kRed + ((i * MB + mb) * kWave + lane) * 4);
+        for (int mb = 0; mb < MB; ++mb) {
+          const i32x4 v = *reinterpret_cast<const i32x4*>(rj + ((i * MB + mb) * kWave + lane) * 4);
+          part[i][mb] += use ? v : i32x4{0, 0, 0, 0};
+        }
     }
     // Epilogue inputs: prefetched for the first segment; later ones (a workgroup with
     // more segments than waves) fetch theirs here, before the exchange.  Lane l owns
@@ -637,7 +644,8 @@ void streamk_kernel(StreamKArgs p) {
     for (int mb = 0; mb < MB; ++mb) resv[mb] = resp[mb];
 
     // A tile of one chunk held by this workgroup alone needs no exchange.
-    const bool interior = C == 1 && wg_of(t * Ss) == b && wg_of(t * Ss + Ss - 1) == b;
+    // (Its steps [t * Ss, t * Ss + Ss) lie in the workgroup's range [A, B).)
+    const bool interior = C == 1 && t * Ss >= A && t * Ss + Ss <= B;
     if (!interior) {
       // Publish the piece as tagged words and wait until they are visible.  Every
       // owner then reads all pieces of the tile: the owner whose words became visible
