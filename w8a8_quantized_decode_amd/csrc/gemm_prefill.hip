@@ -194,7 +194,9 @@ void prefill_gemm_kernel(PrefillGemmArgs p) {
     st.a[rb][s] = *reinterpret_cast<const u32x4*>(b.act[rb] + j * 4096 + s * 1024 + a_lane);
   };
   auto load_w_chunk = [&](WStage& st, int c, const QuadBase& b, int j) {
-    st.w[c] = *reinterpret_cast<const u32x4*>(b.w[c] + j * kWStep + w_lane);
+    // Weight bytes are read once; the activation operand is re-read by every workgroup
+    // and must stay cached, so the weights are loaded non-temporally.
+    st.w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b.w[c] + j * kWStep + w_lane));
     st.s[c] = b.s[c][lane & 15];
   };
 
