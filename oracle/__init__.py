@@ -12,8 +12,10 @@ from .a8w8_oracle import (  # noqa: F401
     exp_f32,
     int_gemm,
     layer_linears_decode,
+    layer_linears_prefill,
     linear_decode,
     mlp_block_decode,
+    prefill_linear,
     prefill_mlp,
     quantize_rows,
     reduce_residual_bf16,

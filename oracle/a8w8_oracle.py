@@ -28,7 +28,8 @@ round to nearest-even); ``fl32(.)`` is one FP32 operation.
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against brute force,
 closed forms, invariants or error bounds.  The end-to-end compositions
-(``mlp_block_decode``, ``layer_linears_decode``, ``prefill_mlp``) are pinned only
+(``mlp_block_decode``, ``layer_linears_decode``, ``prefill_mlp``,
+``layer_linears_prefill``) are pinned only
 through their stage pins plus an error bound against exact (unquantized) FP64 math:
 the pages print no worked example of a whole block, so as compositions they are
 "parity unpinned" beyond those stage pins.
@@ -356,3 +357,44 @@ def prefill_mlp(x_bits, gamma_bits, eps, w_g, s_g, w_u, s_u, w_d, s_d, res_bits)
     d = _bf16_matmul_f64_to_f32(h, wd)
     out = rne_bf16(d + bf16_to_f32(res_bits))
     return out, dict(xn=xn, a=a, g=g, u=u, h=h, d=d, out=out)
+
+
+def prefill_linear(a_bits, w, s, residual_bits=None):
+    """One W8A16 linear: ``y = rne_bf16(fl32(sum_k f(a) * f(W')) [+ f(res)])``.
+
+    ``W' = dequant_weight_bf16(w, s)``; the dot products are accumulated in FP64 and
+    rounded once to FP32, the residual (when given) is one FP32 add, and the result is
+    narrowed with RNE ([PR810] What changed > Gate/Up INT8 path: prefill keeps the shared
+    INT8 weights by dequantizing each tile to BF16; the Gemini review: narrowing with
+    ``mode="rint"``).
+    """
+    y = _bf16_matmul_f64_to_f32(a_bits, dequant_weight_bf16(w, s))
+    if residual_bits is not None:
+        y = y + bf16_to_f32(residual_bits)
+    return rne_bf16(y)
+
+
+def layer_linears_prefill(x_bits, gamma_in_bits, gamma_post_bits, eps, w_qkv, s_qkv, w_o,
+                          s_o, w_g, s_g, w_u, s_u, w_d, s_d, n_q_heads: int, head_dim: int):
+    """All linears of one prefill layer, W8A16, attention replaced by identity.
+
+    The decode layer's readings (``layer_linears_decode``) with the prefill linear in place
+    of the A8W8 one: ``a = rne_bf16(RMSNorm(x, gamma_in))``;
+    ``qkv = prefill_linear(a, W_qkv)``; ``attn = qkv[:, :n_q_heads*head_dim]`` (the Q
+    slice, already BF16, so it is the next operand as it stands);
+    ``h1 = prefill_linear(attn, W_o, residual=x)``; then ``prefill_mlp`` with
+    ``x = res = h1``.  The pages name prefill on the shared INT8 weights ([PR810] What
+    changed > Gate/Up INT8 path) and a prefill hidden-state path in the serving PR; the
+    layer composition is this build's reading.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    xn_in = rmsnorm(x_bits, gamma_in_bits, eps)
+    a = rne_bf16(xn_in)
+    qkv = prefill_linear(a, w_qkv, s_qkv)
+    attn = qkv[:, : n_q_heads * head_dim]
+    h1 = prefill_linear(attn, w_o, s_o, residual_bits=x_bits)
+    out, mlp = prefill_mlp(h1, gamma_post_bits, eps, w_g, s_g, w_u, s_u, w_d, s_d, h1)
+    st = dict(xn_in=xn_in, a=a, qkv=qkv, h1=h1)
+    st.update({"mlp_" + k: v for k, v in mlp.items()})
+    st["out"] = out
+    return out, st

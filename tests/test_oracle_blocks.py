@@ -9,8 +9,11 @@ checked against a closed form and a per-element quantization error bound.
 import numpy as np
 import pytest
 
+from fractions import Fraction
+
 from oracle import (bf16_to_f32, dequant_weight_bf16, int_gemm, layer_linears_decode,
-                    linear_decode, mlp_block_decode, prefill_mlp, quantize_rows, rne_bf16)
+                    layer_linears_prefill, linear_decode, mlp_block_decode, prefill_linear,
+                    prefill_mlp, quantize_rows, rne_bf16)
 from w8a8_quantized_decode_amd import synth
 
 C0 = synth.CONFIGS[0]
@@ -143,3 +146,76 @@ def test_prefill_weight_tiles_and_output():
     # FP64 accumulation rounded once: g equals the exactly rounded BF16 dot products
     gg = _f(st["a"]) @ _f(wq).T
     assert np.array_equal(st["g"], gg.astype(np.float32))
+
+
+def test_prefill_linear_brute_force():
+    """Exact rational dot products of the BF16 operands, rounded once to FP32, then RNE
+    to BF16 (with and without the residual add)."""
+    rng = np.random.default_rng(11)
+    M, N, K = 3, 4, 7
+    a = rne_bf16(rng.normal(size=(M, K)).astype(np.float32))
+    w = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    sw = rng.uniform(1e-3, 1e-2, size=N).astype(np.float32)
+    res = rne_bf16(rng.normal(size=(M, N)).astype(np.float32))
+    wq = dequant_weight_bf16(w, sw)
+    got = prefill_linear(a, w, sw)
+    got_r = prefill_linear(a, w, sw, residual_bits=res)
+    af, wf, rf = bf16_to_f32(a), bf16_to_f32(wq), bf16_to_f32(res)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(af[m, k])) * Fraction(float(wf[n, k])) for k in range(K))
+            y = np.float32(float(exact))  # the exact sum fits FP64: one rounding to FP32
+            assert got[m, n] == rne_bf16(np.array([y], np.float32))[0]
+            yr = np.float32(y + np.float32(rf[m, n]))
+            assert got_r[m, n] == rne_bf16(np.array([yr], np.float32))[0]
+
+
+def test_layer_prefill_identity_weights():
+    """Identity QKV (first H rows) and O weights: W' = 1 exactly (127 * fl32(1/127) rounds
+    to 1), so the Q slice is the normalized operand itself and h1 = rne(a + x).  Pins the
+    slice (Q first), the residual (the layer input) and the MLP input (h1)."""
+    cfg = C0
+    H, hd = 256, 128
+    nq, nkv = 2, 1
+    n_qkv = (nq + 2 * nkv) * hd
+    rng = np.random.default_rng(5)
+    d = synth.mlp_inputs(cfg, M=3)
+    x = d["x"]
+    g_in = rne_bf16(rng.uniform(0.5, 1.5, size=H).astype(np.float32))
+    w_qkv = np.zeros((n_qkv, H), np.int8)
+    w_qkv[:H] = 127 * np.eye(H, dtype=np.int8)
+    w_qkv[H:] = rng.integers(-127, 128, size=(n_qkv - H, H)).astype(np.int8)
+    s_qkv = np.full(n_qkv, np.float32(1.0) / np.float32(127.0), np.float32)
+    w_o = (127 * np.eye(H)).astype(np.int8)
+    s_o = np.full(H, np.float32(1.0) / np.float32(127.0), np.float32)
+    assert np.all(bf16_to_f32(dequant_weight_bf16(w_o, s_o)) == np.eye(H, dtype=np.float32))
+    out, st = layer_linears_prefill(x, g_in, d["gamma_post"], cfg.eps, w_qkv, s_qkv, w_o, s_o,
+                                    d["w_gate"], d["s_gate"], d["w_up"], d["s_up"],
+                                    d["w_down"], d["s_down"], nq, hd)
+    assert np.array_equal(st["qkv"][:, :H], st["a"])
+    assert np.array_equal(st["h1"], rne_bf16(bf16_to_f32(st["a"]) + bf16_to_f32(x)))
+    mlp_out, _ = prefill_mlp(st["h1"], d["gamma_post"], cfg.eps, d["w_gate"], d["s_gate"],
+                             d["w_up"], d["s_up"], d["w_down"], d["s_down"], st["h1"])
+    assert np.array_equal(out, mlp_out)
+
+
+def test_layer_prefill_against_exact_math():
+    cfg = C0
+    d = synth.layer_inputs(cfg, M=4)
+    out, st = layer_linears_prefill(d["x"], d["gamma_in"], d["gamma_post"], cfg.eps,
+                                    d["w_qkv"], d["s_qkv"], d["w_o"], d["s_o"], d["w_gate"],
+                                    d["s_gate"], d["w_up"], d["s_up"], d["w_down"],
+                                    d["s_down"], cfg.n_q_heads, cfg.head_dim)
+    x = _f(d["x"])
+    xn = _rms_f64(x, _f(d["gamma_in"]), cfg.eps)
+    qkv = xn @ (d["w_qkv"].astype(np.float64) * d["s_qkv"][:, None]).T
+    r = np.linalg.norm(_f(st["qkv"]) - qkv) / np.linalg.norm(qkv)
+    assert r < 0.01, r          # BF16 operands, weights and output: a few 2**-8 roundings
+    attn = qkv[:, : cfg.n_q_heads * cfg.head_dim]
+    h1 = attn @ (d["w_o"].astype(np.float64) * d["s_o"][:, None]).T + x
+    r = np.linalg.norm(_f(st["h1"]) - h1) / np.linalg.norm(h1)
+    assert r < 0.01, r
+    dd = dict(d, x=st["h1"])
+    down_exact, _ = _mlp_exact(dd, cfg.eps)
+    r = np.linalg.norm(_f(out) - _f(st["h1"]) - down_exact) / np.linalg.norm(down_exact)
+    assert r < 0.02, r
