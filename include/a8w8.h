@@ -266,6 +266,32 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
                                void* workspace, size_t ws_bytes,
                                const a8w8_layer_taps* taps, void* stream);
 
+/*
+ * All linears of one prefill layer, W8A16 on the shared INT8 weights (pypto-lib PR #810,
+ * What changed > Gate/Up INT8 path: prefill dequantizes each weight tile to BF16; the
+ * layer composition is the decode layer's with that linear).  Same shapes as
+ * a8w8_layer_linears; attention replaced by identity.
+ * Steps: a = rne_bf16(RMSNorm(x, gamma_in)) -> qkv = rne_bf16(a W'_qkv^T) -> the Q slice
+ * qkv[:, :H] -> h1 = rne_bf16(attn W'_o^T + x) -> the prefill MLP block (a8w8_mlp_block in
+ * A8W8_MODE_PREFILL_W8A16) with input h1 and residual h1.  W' = rne_bf16(w * scale) per
+ * tile; products accumulate in FP32 on BF16 matrix cores.
+ *   qkv_out_bf16 [M, n_qkv] receives qkv, h1_out_bf16 [M, H] receives h1 (each may be
+ *   NULL: kept in the workspace); out_bf16 [M, H] (may alias x_bf16); workspace from
+ *   a8w8_workspace_bytes(A8W8_OP_LAYER_LINEARS, M, H, I, n_qkv, 2,
+ *   A8W8_MODE_PREFILL_W8A16).
+ * Needs H % 256 == 0, I % 256 == 0, n_qkv % 128 == 0, M * max(H, I, n_qkv) < 2^31.
+ * Errors as a8w8_layer_linears (shape errors before any launch).  Kernels: row norm,
+ * QKV GEMM, Q-slice copy to the operand layout, O GEMM, then the prefill MLP's kernels.
+ */
+a8w8_status a8w8_layer_linears_prefill(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                                       const uint16_t* gamma_post_bf16, float eps,
+                                       a8w8_qweight qkv, a8w8_qweight o, a8w8_qweight gate,
+                                       a8w8_qweight up, a8w8_qweight down, int64_t M,
+                                       int64_t H, int64_t I, int n_q_heads, int n_kv_heads,
+                                       int head_dim, uint16_t* qkv_out_bf16,
+                                       uint16_t* h1_out_bf16, uint16_t* out_bf16,
+                                       void* workspace, size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* a8w8_status_string(a8w8_status status);
 

@@ -37,6 +37,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"a8w8_quantize_rows", "a8w8_linear", "a8w8_mlp_block", "a8w8_layer_linears",
+            "a8w8_layer_linears_prefill",
             "a8w8_workspace_bytes", "a8w8_status_string", "a8w8_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -133,3 +134,22 @@ def test_layer_validation(L):
     assert call(nq=3) == 2                   # n_q * head_dim != H
     assert call(hd=0) == 2
     assert call(wsb=ws - 1) == 4
+
+
+def test_layer_prefill_validation(L):
+    """Shape, workspace and alignment errors are returned before any launch."""
+    f = L.a8w8_layer_linears_prefill
+    ws = B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 1, 256, 768, 512, 2, B.MODE_PREFILL_W8A16)
+    assert ws > B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, 1, 256, 768, 0, 2, B.MODE_PREFILL_W8A16)
+    assert B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 1, 256, 768, 512 + 16, 2,
+                                  B.MODE_PREFILL_W8A16) == 0   # n_qkv % 128
+
+    def call(M=1, H=256, nq=2, nkv=1, hd=128, wsb=ws, x=FAKE, wsp=FAKE):
+        return f(x, FAKE, FAKE, 1e-6, QW, QW, QW, QW, QW, M, H, 768, nq, nkv, hd, None, None,
+                 FAKE, wsp, wsb, None)
+    assert call(M=0) == 0
+    assert call(nq=3) == 2                   # n_q * head_dim != H
+    assert call(wsb=ws - 1) == 4
+    assert call(x=None) == 1
+    assert call(x=MIS) == 3
+    assert call(wsp=FAKE + 16) == 3

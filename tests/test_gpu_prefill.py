@@ -148,3 +148,87 @@ def test_prefill_qwen3_14b_m256():
     check(d, got, want, t, st)
     same = float(np.mean(got == want))
     print(f"[note] prefill M=256: {same:.4f} of BF16 outputs bit-identical to the oracle")
+
+
+# ------------------------------------------------------------------ the prefill layer
+TOY_LAYER = synth.Config(0, "toy layer", 1, 256, 768, "layer", n_q_heads=2, n_kv_heads=1,
+                         head_dim=128)
+
+
+def run_layer_prefill(cfg, M, layout=B.LAYOUT_TILED):
+    d = synth.layer_inputs(cfg, layer=3, M=M)
+    H, I, n_qkv = cfg.H, cfg.I, cfg.n_qkv
+    out = empty((M, H), np.uint16)
+    qkv_out = empty((M, n_qkv), np.uint16)
+    h1_out = empty((M, H), np.uint16)
+    nbytes = B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, M, H, I, n_qkv, 2, B.MODE_PREFILL_W8A16)
+    assert nbytes > 0
+    ws = zeros((nbytes,), np.uint8)
+    B.a8w8_layer_linears_prefill(dev(d["x"]), dev(d["gamma_in"]), dev(d["gamma_post"]), cfg.eps,
+                                 qw(d["w_qkv"], d["s_qkv"], layout), qw(d["w_o"], d["s_o"], layout),
+                                 qw(d["w_gate"], d["s_gate"], layout),
+                                 qw(d["w_up"], d["s_up"], layout),
+                                 qw(d["w_down"], d["s_down"], layout), out, ws, cfg.n_q_heads,
+                                 cfg.n_kv_heads, cfg.head_dim, qkv_out=qkv_out, h1_out=h1_out)
+    return cfg, d, host(qkv_out, np.uint16), host(h1_out, np.uint16), host(out, np.uint16)
+
+
+def _linear_boundary_check(got, want, a_bits, w_bits, res_bits=None):
+    """got = rne_bf16 of an FP32-accumulated GEMM of exact BF16 operands; want = the oracle's
+    once-rounded FP64 sum on the same operands.  The FP32 sums differ by at most
+    K * 2**-24 * sum |a||W'| (plus one rounding each, and the residual add); the BF16 values
+    are identical unless a rounding boundary lies in that interval, and never further apart
+    than that interval plus one BF16 ulp."""
+    a, w = _f64(a_bits), _f64(w_bits)
+    y = (a @ w.T).astype(np.float32).astype(np.float64)
+    if res_bits is not None:
+        y = y + _f64(res_bits)
+    delta = a.shape[1] * U * (np.abs(a) @ np.abs(w).T) + 4 * U * np.abs(y) + 1e-30
+    flip = boundary_within(y, delta)
+    np.testing.assert_array_equal(got[~flip], want[~flip])
+    assert np.all(np.abs(_f64(got) - _f64(want)) <= delta + np.maximum(bf16_ulp(got), bf16_ulp(want)))
+    return float(np.mean(got == want))
+
+
+def check_layer_prefill(cfg, d, qkv, h1, got):
+    """Stage-wise: each stage of the oracle runs on the GPU's own input to that stage, so
+    an FP32 rounding difference upstream is not amplified downstream; the oracle's values
+    never depend on the GPU's arithmetic, only on its (checked) intermediate rows."""
+    H = cfg.H
+    xn = O.rmsnorm(d["x"], d["gamma_in"], cfg.eps)
+    a = O.rne_bf16(xn)
+    wq = O.dequant_weight_bf16(d["w_qkv"], d["s_qkv"])
+    f_qkv = _linear_boundary_check(qkv, O.prefill_linear(a, d["w_qkv"], d["s_qkv"]), a, wq)
+    attn = qkv[:, :H]
+    wo = O.dequant_weight_bf16(d["w_o"], d["s_o"])
+    f_h1 = _linear_boundary_check(h1, O.prefill_linear(attn, d["w_o"], d["s_o"], d["x"]),
+                                  attn, wo, d["x"])
+    want, _ = O.prefill_mlp(h1, d["gamma_post"], cfg.eps, d["w_gate"], d["s_gate"], d["w_up"],
+                            d["s_up"], d["w_down"], d["s_down"], h1)
+    # The MLP block on the GPU's own h1: the stated tolerance on the output's scale, as
+    # for the prefill MLP block (whose stages are checked one by one above).
+    err = np.abs(_f64(got) - _f64(want))
+    wv = np.abs(_f64(want))
+    scale = max(1.0, float(np.sqrt(np.mean(wv * wv))))
+    ok = np.where(wv < scale, err <= 1e-2 * scale, err <= 1e-2 * wv)
+    rel = np.linalg.norm(_f64(got) - _f64(want)) / np.linalg.norm(_f64(want))
+    print(f"[note] prefill layer: qkv {f_qkv:.6f} and h1 {f_h1:.6f} identical, "
+          f"{np.mean(got == want):.4f} of outputs identical, normwise rel {rel:.2e}")
+    assert np.all(ok), f"{np.count_nonzero(~ok)} outputs beyond the scaled tolerance"
+    assert rel <= 1e-2
+
+
+@pytest.mark.parametrize("M", [1, 64, 200])
+def test_layer_prefill_toy(M):
+    announce(f"layer prefill toy M={M}")
+    check_layer_prefill(*run_layer_prefill(TOY_LAYER, M))
+
+
+def test_layer_prefill_toy_rowmajor():
+    announce("layer prefill toy M=65 row-major")
+    check_layer_prefill(*run_layer_prefill(TOY_LAYER, 65, B.LAYOUT_ROWMAJOR))
+
+
+def test_layer_prefill_qwen3_14b_m256():
+    announce("layer prefill qwen3-14b M=256")
+    check_layer_prefill(*run_layer_prefill(synth.CONFIGS[2], 256))

@@ -92,6 +92,12 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, _vp, _vp, _vp, ctypes.c_size_t,
                                          ctypes.POINTER(LayerTaps), _vp]
+        L.a8w8_layer_linears_prefill.restype = ctypes.c_int
+        L.a8w8_layer_linears_prefill.argtypes = [_vp, _vp, _vp, ctypes.c_float, QWeight,
+                                                 QWeight, QWeight, QWeight, QWeight, _c_i64,
+                                                 _c_i64, _c_i64, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, _vp, _vp, _vp, _vp,
+                                                 ctypes.c_size_t, _vp]
         _LIB = L
     return _LIB
 
@@ -215,6 +221,19 @@ def a8w8_layer_linears(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out
                                   _ptr(workspace), workspace.numel(),
                                   ctypes.byref(t) if t is not None else None, _stream(stream))
     _check(st, "a8w8_layer_linears")
+
+
+def a8w8_layer_linears_prefill(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out,
+                               workspace, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                               qkv_out=None, h1_out=None, stream=None) -> None:
+    M, H = x.shape
+    I = gate[1].shape[0]
+    st = lib().a8w8_layer_linears_prefill(_ptr(x), _ptr(gamma_in), _ptr(gamma_post), float(eps),
+                                          _qw(qkv), _qw(o), _qw(gate), _qw(up), _qw(down), M, H,
+                                          I, int(n_q_heads), int(n_kv_heads), int(head_dim),
+                                          _ptr(qkv_out), _ptr(h1_out), _ptr(out), _ptr(workspace),
+                                          workspace.numel(), _stream(stream))
+    _check(st, "a8w8_layer_linears_prefill")
 
 
 def a8w8_version() -> int:

@@ -214,18 +214,31 @@ struct PrefillBuffers {
   uint16_t* a;       // BF16 activations rne_bf16(RMSNorm(x)), prefill operand layout
   uint16_t* h;       // BF16 silu(g) * u, prefill operand layout
   float* slots;      // partial sums of split tiles
+  uint16_t* qkv;     // layer: [M, n_qkv] BF16 QKV projection
+  uint16_t* h1;      // layer: [M, H] BF16 attention-block output
 };
 
-PrefillBuffers carve_prefill(Carver& c, int64_t M, int64_t H, int64_t I) {
+// n_qkv > 0: the layer (QKV and O GEMMs before the MLP, their outputs kept here).
+PrefillBuffers carve_prefill(Carver& c, int64_t M, int64_t H, int64_t I, int64_t n_qkv = 0) {
   const PrefillPlan gu = plan_prefill(EPI_PF_SILU, M, I, H);
   const PrefillPlan dn = plan_prefill(EPI_PF_RES, M, H, I);
-  const int64_t grid = gu.grid > dn.grid ? gu.grid : dn.grid;
+  int64_t grid = gu.grid > dn.grid ? gu.grid : dn.grid;
+  if (n_qkv > 0) {
+    const PrefillPlan q = plan_prefill(EPI_PF_RES, M, n_qkv, H);
+    const PrefillPlan o = plan_prefill(EPI_PF_RES, M, H, H);
+    if (q.grid > grid) grid = q.grid;
+    if (o.grid > grid) grid = o.grid;
+  }
   const int64_t Mp = (M + 31) / 32 * 32;  // the operand layout pads rows to 32
   PrefillBuffers b{};
   take_epoch(c);
   b.a = c.take<uint16_t>(size_t(Mp) * H);
   b.h = c.take<uint16_t>(size_t(Mp) * I);
   b.slots = c.take<float>(size_t(2 * grid) * prefill_slot_floats());
+  if (n_qkv > 0) {
+    b.qkv = c.take<uint16_t>(size_t(M) * n_qkv);
+    b.h1 = c.take<uint16_t>(size_t(M) * H);
+  }
   return b;
 }
 
@@ -472,9 +485,16 @@ size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_q
                             int split_k, int mode) {
   if (check_mlp_shapes(M, H, I, split_k) != A8W8_OK) return 0;
   if (mode == A8W8_MODE_PREFILL_W8A16) {
-    if (op != A8W8_OP_MLP_BLOCK || !prefill_shapes_ok(M, H, I)) return 0;
+    if (!prefill_shapes_ok(M, H, I)) return 0;
     Carver c(nullptr);
-    carve_prefill(c, M, H, I);
+    if (op == A8W8_OP_MLP_BLOCK) {
+      carve_prefill(c, M, H, I);
+    } else if (op == A8W8_OP_LAYER_LINEARS) {
+      if (n_qkv <= 0 || n_qkv % prefill_tile_channels(EPI_PF_RES)) return 0;
+      carve_prefill(c, M, H, I, n_qkv);
+    } else {
+      return 0;
+    }
     return c.size() > 0 ? c.size() : kAlign;
   }
   if (mode != A8W8_MODE_DECODE_A8W8) return 0;
@@ -625,6 +645,98 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
 
   return run_mlp_decode(b.h1, gamma_post_bf16, eps, gate, up, down, b.h1, out_bf16, M, H, I,
                         split_k, pl, b, 2, mt, tm, st);
+}
+
+a8w8_status a8w8_layer_linears_prefill(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                                       const uint16_t* gamma_post_bf16, float eps,
+                                       a8w8_qweight qkv, a8w8_qweight o, a8w8_qweight gate,
+                                       a8w8_qweight up, a8w8_qweight down, int64_t M,
+                                       int64_t H, int64_t I, int n_q_heads, int n_kv_heads,
+                                       int head_dim, uint16_t* qkv_out_bf16,
+                                       uint16_t* h1_out_bf16, uint16_t* out_bf16,
+                                       void* workspace, size_t ws_bytes, void* stream) {
+  if (a8w8_status s = check_mlp_shapes(M, H, I, 2)) return s;
+  if (n_q_heads <= 0 || n_kv_heads < 0 || head_dim <= 0) return A8W8_ERR_SHAPE;
+  if (int64_t(n_q_heads) * head_dim != H) return A8W8_ERR_SHAPE;
+  const int64_t n_qkv = (int64_t(n_q_heads) + 2 * int64_t(n_kv_heads)) * head_dim;
+  if (!prefill_shapes_ok(M, H, I) || n_qkv % prefill_tile_channels(EPI_PF_RES) ||
+      M * n_qkv >= (int64_t(1) << 31))
+    return A8W8_ERR_SHAPE;
+  if (M == 0) return A8W8_OK;
+  if (!x_bf16 || !gamma_in_bf16 || !gamma_post_bf16 || !out_bf16) return A8W8_ERR_NULL;
+  for (const a8w8_qweight* w : {&qkv, &o, &gate, &up, &down})
+    if (a8w8_status s = check_qweight(*w)) return s;
+  if (!aligned16(x_bf16) || !aligned16(gamma_in_bf16) || !aligned16(gamma_post_bf16) ||
+      !aligned16(out_bf16) || (qkv_out_bf16 && !aligned16(qkv_out_bf16)) ||
+      (h1_out_bf16 && !aligned16(h1_out_bf16)))
+    return A8W8_ERR_ALIGN;
+  const size_t need = a8w8_workspace_bytes(A8W8_OP_LAYER_LINEARS, M, H, I, n_qkv, 2,
+                                           A8W8_MODE_PREFILL_W8A16);
+  if (!workspace || ws_bytes < need) return A8W8_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return A8W8_ERR_ALIGN;
+  Carver c(workspace);
+  const PrefillBuffers pb = carve_prefill(c, M, H, I, n_qkv);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Timer tm(nullptr, st);
+  uint16_t* qkv_buf = qkv_out_bf16 ? qkv_out_bf16 : pb.qkv;
+  uint16_t* h1_buf = h1_out_bf16 ? h1_out_bf16 : pb.h1;
+
+  // a = rne_bf16(RMSNorm(x, gamma_in)) in the prefill operand layout.
+  QuantRowsArgs q{};
+  q.x = x_bf16;
+  q.ldx = H;
+  q.gamma = gamma_in_bf16;
+  q.eps = eps;
+  q.M = M;
+  q.K = H;
+  q.a_bf16 = pb.a;
+  q.a_bf16_tiled = 1;
+  q.write_codes = 0;
+  A8W8_HIP(launch_quant_rows(q, st));
+  // qkv = rne_bf16(a W'_qkv^T), row-major [M, n_qkv].
+  PrefillGemmArgs g{};
+  g.epi = EPI_PF_RES;
+  g.layout = layout_of(qkv);
+  g.M = M;
+  g.N = n_qkv;
+  g.K = H;
+  g.act = pb.a;
+  g.w0 = qkv.w;
+  g.sw0 = qkv.scale;
+  g.out = qkv_buf;
+  g.ldo = n_qkv;
+  g.res = nullptr;
+  g.slots = pb.slots;
+  A8W8_HIP(launch_prefill_gemm(g, st));
+  // The Q slice (identity attention) into the operand layout: a BF16 copy.
+  QuantRowsArgs qa{};
+  qa.x = qkv_buf;
+  qa.ldx = n_qkv;
+  qa.M = M;
+  qa.K = H;
+  qa.a_bf16 = pb.a;
+  qa.a_bf16_tiled = 1;
+  qa.write_codes = 0;
+  A8W8_HIP(launch_quant_rows(qa, st));
+  // h1 = rne_bf16(attn W'_o^T + x).
+  PrefillGemmArgs og{};
+  og.epi = EPI_PF_RES;
+  og.layout = layout_of(o);
+  og.M = M;
+  og.N = H;
+  og.K = H;
+  og.act = pb.a;
+  og.w0 = o.w;
+  og.sw0 = o.scale;
+  og.out = h1_buf;
+  og.ldo = H;
+  og.res = x_bf16;
+  og.ldr = H;
+  og.slots = pb.slots;
+  A8W8_HIP(launch_prefill_gemm(og, st));
+  // The MLP block on h1, with h1 as its residual.
+  return run_mlp_prefill(h1_buf, gamma_post_bf16, eps, gate, up, down, h1_buf, out_bf16, M, H,
+                         I, pb, nullptr, tm, st);
 }
 
 }  // extern "C"

@@ -39,7 +39,8 @@
 //     bases computed once per quad plus constant lane offsets.
 //   * EPI_PF_SILU: h = rne_bf16(silu(g) * u) in the prefill operand layout for the Down
 //     GEMM (+ FP32 taps of g and u, a row-major tap of h).
-//     EPI_PF_RES: out = rne_bf16(d + res) row-major (+ FP32 tap of d).
+//     EPI_PF_RES: out = rne_bf16(d + res) row-major (+ FP32 tap of d); without a residual
+//                 (res == nullptr) out = rne_bf16(d).
 #include <type_traits>
 
 #include "device_common.h"
@@ -93,12 +94,19 @@ __device__ __forceinline__ void epilogue_group(const PrefillGemmArgs& p, int64_t
     if (p.tap_h) *reinterpret_cast<u32x2*>(p.tap_h + m * p.N + n0) = o;
   } else {
     if (p.tap_d) *reinterpret_cast<f32x4*>(p.tap_d + m * p.N + n0) = g;
-    const u32x2 rr = *reinterpret_cast<const u32x2*>(p.res + m * p.ldr + n0);
+    // Without a residual the accumulator is narrowed as it is (no add of +0, which
+    // would turn a -0 result into +0).
+    f32x4 y = g;
+    if (p.res) {
+      const u32x2 rr = *reinterpret_cast<const u32x2*>(p.res + m * p.ldr + n0);
+      y[0] = g[0] + bf16_lo(rr[0]);
+      y[1] = g[1] + bf16_hi(rr[0]);
+      y[2] = g[2] + bf16_lo(rr[1]);
+      y[3] = g[3] + bf16_hi(rr[1]);
+    }
     u32x2 o;
-    o[0] = uint32_t(f32_to_bf16_rne(g[0] + bf16_lo(rr[0]))) |
-           (uint32_t(f32_to_bf16_rne(g[1] + bf16_hi(rr[0]))) << 16);
-    o[1] = uint32_t(f32_to_bf16_rne(g[2] + bf16_lo(rr[1]))) |
-           (uint32_t(f32_to_bf16_rne(g[3] + bf16_hi(rr[1]))) << 16);
+    o[0] = uint32_t(f32_to_bf16_rne(y[0])) | (uint32_t(f32_to_bf16_rne(y[1])) << 16);
+    o[1] = uint32_t(f32_to_bf16_rne(y[2])) | (uint32_t(f32_to_bf16_rne(y[3])) << 16);
     *reinterpret_cast<u32x2*>(p.out + m * p.ldo + n0) = o;
   }
 }

@@ -221,7 +221,7 @@ struct PrefillGemmArgs {
   const float* sw1;
   uint16_t* out;            // EPI_PF_SILU: h, prefill operand layout (N columns);
   int64_t ldo;              // EPI_PF_RES: [M, ldo] BF16 block output
-  const uint16_t* res;      // EPI_PF_RES: [M, ldr] BF16 residual (may alias out)
+  const uint16_t* res;      // EPI_PF_RES: [M, ldr] BF16 residual (may alias out) or nullptr
   int64_t ldr;
   uint16_t* tap_h;          // EPI_PF_SILU tap: [M, N] row-major h or nullptr
   float* tap_g;             // EPI_PF_SILU taps: [M, N] FP32 accumulators or nullptr
