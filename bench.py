@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--config", type=int, default=2,
                    help="2: layer M=1; 3: 40-layer M=16 stack; 4: W8A16 prefill MLP M=256")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--layer", action="store_true",
+                   help="with --config 4: the whole prefill layer (QKV, O and the MLP block)")
     p.add_argument("--graph", type=int, default=1,
                    help="also time the steps replayed from one captured HIP graph (0: skip)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -243,6 +245,60 @@ def bench_prefill(args, cfg, torch, B) -> None:
     print(json.dumps(out_line))
 
 
+def bench_prefill_layer(args, torch, B) -> None:
+    """The W8A16 prefill layer at M = 256 (QKV, O, then the MLP block): TFLOP/s of its
+    five GEMMs; the roofline is the whole call against the BF16 matrix-core peak."""
+    from w8a8_quantized_decode_amd import synth
+    cfg = synth.CONFIGS[2]
+    M, H, I, n_qkv = synth.CONFIGS[4].M, cfg.H, cfg.I, cfg.n_qkv
+    d = synth.layer_inputs(cfg, layer=0, M=M)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    def upw(w, s):
+        rm = up(w)
+        tiled = torch.empty_like(rm)
+        B.a8w8_pack_weight(rm, tiled)
+        return (tiled, up(s), B.LAYOUT_TILED)
+
+    w = {k: upw(d["w_" + k], d["s_" + k]) for k in ("qkv", "o", "gate", "up", "down")}
+    x, gin, gpost = up(d["x"]), up(d["gamma_in"]), up(d["gamma_post"])
+    out = torch.empty_like(x)
+    ws = torch.zeros(B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, M, H, I, n_qkv, 2,
+                                            B.MODE_PREFILL_W8A16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        B.a8w8_layer_linears_prefill(x, gin, gpost, cfg.eps, w["qkv"], w["o"], w["gate"], w["up"],
+                                     w["down"], out, ws, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    flops = 2.0 * M * (n_qkv * H + H * H + 3 * H * I)
+    tf = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "W8A16 prefill layer TFLOP/s (QKV, O, Gate/Up, Down GEMMs), BF16 matrix cores",
+        "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded PCG64, Qwen3-14B shapes, random INT8 weights)",
+        "config": {"workload": "Qwen3-14B W8A16 prefill layer linears, M=256", "M": M,
+                   "hidden": H, "intermediate": I, "n_qkv": n_qkv},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole call (norm, QKV, slice copy, O, MLP kernels)",
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None}))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -258,6 +314,9 @@ def main():
     from w8a8_quantized_decode_amd import synth
 
     cfg = synth.CONFIGS[args.config]
+    if cfg.kind == "prefill" and args.layer:
+        bench_prefill_layer(args, torch, B)
+        return
     if cfg.kind == "prefill":
         bench_prefill(args, cfg, torch, B)
         return
