@@ -17,10 +17,12 @@ from .a8w8_oracle import (  # noqa: F401
     mlp_block_decode,
     prefill_linear,
     prefill_mlp,
+    qk_norm_rope_kv,
     quantize_rows,
     reduce_residual_bf16,
     rmsnorm,
     rne_bf16,
+    rope_rotate_half,
     silu_mul,
     split_k_ranges,
 )

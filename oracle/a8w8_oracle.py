@@ -398,3 +398,66 @@ def layer_linears_prefill(x_bits, gamma_in_bits, gamma_post_bits, eps, w_qkv, s_
     st.update({"mlp_" + k: v for k, v in mlp.items()})
     st["out"] = out
     return out, st
+
+
+# ------------------------------------------------------------- QK-norm, RoPE, KV write
+
+def rope_rotate_half(x, cos, sin) -> np.ndarray:
+    """Rotary position embedding, rotate-half form, on FP32 vectors ``x [..., d]`` with
+    ``cos, sin [..., d/2]`` (broadcast): for ``i < d/2``,
+    ``o[i] = fl32(fl32(x[i]*c[i]) - fl32(x[i+d/2]*s[i]))`` and
+    ``o[i+d/2] = fl32(fl32(x[i+d/2]*c[i]) + fl32(x[i]*s[i]))``.
+
+    The pages name RoPE on Q and K before the BF16 KV-cache write ([ISSUE52] Current
+    behavior: the fused QK-norm path and its Q RoPE; [PR810] walkthrough, BF16 cache and
+    interface contracts: RoPE writes use BF16 KV caches) but not its form; rotate-half is
+    the Qwen3 family's, and the angle tables are inputs (both sides read the same values).
+    """
+    x = np.asarray(x, dtype=F32)
+    h = x.shape[-1] // 2
+    c = np.asarray(cos, dtype=F32)
+    s_ = np.asarray(sin, dtype=F32)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s_, x2 * c + x1 * s_], axis=-1).astype(F32)
+
+
+def qk_norm_rope_kv(qkv_bits, n_q_heads: int, n_kv_heads: int, head_dim: int, q_gamma_bits,
+                    k_gamma_bits, eps, cos_table, sin_table, positions, block_table,
+                    k_cache_bits, v_cache_bits):
+    """QK-norm, RoPE and the BF16 KV-cache write that follow the QKV projection.
+
+    ``qkv [M, (n_q + 2 n_kv) * d]`` holds the Q heads, then the K heads, then the V heads.
+    Per row ``m`` at position ``p = positions[m]``:
+    * each Q head ``q = rne_bf16(rope(RMSNorm_d(q, q_gamma), cos[p], sin[p]))`` (the
+      attention input);
+    * each K head likewise with ``k_gamma``, written to the cache slot of position ``p``;
+    * each V head copied to the same slot of the V cache.
+    RMSNorm over one head is ``rmsnorm`` above on a row of ``d`` values.  The cache is
+    paged: ``cache[b, o, h, :]`` with ``b = block_table[m, p // block_size]``,
+    ``o = p % block_size`` ([PR48] runner: paged KV cache with a block table and bounds
+    validated before dispatch).  Readings: QK-norm gains shared by the heads of each kind
+    (one ``[d]`` vector each) and the paged layout ``[blocks, block_size, n_kv, d]``.
+    Returns the Q output and new copies of the two caches.
+    """
+    qkv = np.asarray(qkv_bits, dtype=np.uint16)
+    M = qkv.shape[0]
+    d = head_dim
+    kc = np.array(k_cache_bits, dtype=np.uint16, copy=True)
+    vc = np.array(v_cache_bits, dtype=np.uint16, copy=True)
+    bs = kc.shape[1]
+    q_out = np.empty((M, n_q_heads * d), dtype=np.uint16)
+    for m in range(M):
+        p = int(positions[m])
+        c, s_ = cos_table[p], sin_table[p]
+        for h in range(n_q_heads):
+            v = qkv[m : m + 1, h * d : (h + 1) * d]
+            q_out[m, h * d : (h + 1) * d] = rne_bf16(rope_rotate_half(rmsnorm(v, q_gamma_bits, eps), c, s_))[0]
+        b = int(block_table[m, p // bs])
+        o = p % bs
+        for h in range(n_kv_heads):
+            k0 = (n_q_heads + h) * d
+            v0 = (n_q_heads + n_kv_heads + h) * d
+            kv = qkv[m : m + 1, k0 : k0 + d]
+            kc[b, o, h] = rne_bf16(rope_rotate_half(rmsnorm(kv, k_gamma_bits, eps), c, s_))[0]
+            vc[b, o, h] = qkv[m, v0 : v0 + d]
+    return q_out, kc, vc

@@ -118,3 +118,12 @@ def layer_inputs(cfg: Config, layer: int = 0, M: int | None = None, with_x: bool
     d["w_o"] = int8_weights(seed_for(c, layer, "w_o"), (H, cfg.n_q_heads * cfg.head_dim))
     d["s_o"] = channel_scales(seed_for(c, layer, "s_o"), H)
     return d
+
+
+def rope_tables(max_pos: int, head_dim: int, base: float = 1_000_000.0):
+    """Rotary-embedding angle tables, an input of the QK-norm + RoPE step: for position p and
+    pair i < head_dim / 2, the angle p * base**(-2i / head_dim) (Qwen3's base 1e6), as FP32
+    cos and sin tables [max_pos, head_dim / 2] computed in FP64 and rounded once."""
+    inv = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
