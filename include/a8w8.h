@@ -292,6 +292,36 @@ a8w8_status a8w8_layer_linears_prefill(const uint16_t* x_bf16, const uint16_t* g
                                        uint16_t* h1_out_bf16, uint16_t* out_bf16,
                                        void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * QK-norm, rotate-half RoPE and the paged BF16 KV-cache write after the QKV projection
+ * (pypto-serving issue #52, Current behavior: the fused QK-norm path and its Q RoPE;
+ * pypto-lib PR #810 walkthrough, BF16 cache and interface contracts: RoPE writes into
+ * BF16 KV caches; pypto-serving PR #48: paged KV cache with a block table).
+ *   qkv_bf16 [M, (n_q + 2 n_kv) * d]: Q heads, then K heads, then V heads (the QKV
+ *   projection's output); q_gamma, k_gamma [d] BF16 (shared by the heads of each kind);
+ *   cos_table, sin_table [max_pos, d/2] FP32 (4-byte aligned; the caller's angles);
+ *   positions [M] int32; block_table [M, blocks_per_seq] int32;
+ *   k_cache, v_cache [num_blocks, block_size, n_kv, d] BF16; q_out [M, n_q * d] BF16.
+ * Per row m at position p: each Q head -> rne_bf16(rope(RMSNorm_d(q, q_gamma))) into
+ * q_out; each K head likewise with k_gamma, and each V head as it is, into the cache slot
+ * (block_table[m, p / block_size], p % block_size).  RMSNorm over a head as in
+ * a8w8_quantize_rows; rope: o[i] = x[i] c - x[i+d/2] s, o[i+d/2] = x[i+d/2] c + x[i] s
+ * with c, s = cos/sin_table[p, i], each product and sum one FP32 operation.
+ * Shapes: d even and <= 512, n_q > 0, n_kv >= 0 (k_gamma, block_table and the caches may
+ * be NULL when n_kv == 0), M <= 65535.  A row whose position is outside [0, max_pos) or
+ * whose block index or block number is out of range is skipped (its outputs are not
+ * written).  One kernel.
+ */
+a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_heads,
+                                 int n_kv_heads, int head_dim, const uint16_t* q_gamma_bf16,
+                                 const uint16_t* k_gamma_bf16, float eps,
+                                 const float* cos_table, const float* sin_table,
+                                 int64_t max_pos, const int32_t* positions,
+                                 const int32_t* block_table, int64_t blocks_per_seq,
+                                 uint16_t* k_cache_bf16, uint16_t* v_cache_bf16,
+                                 int64_t num_blocks, int64_t block_size, uint16_t* q_out_bf16,
+                                 void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* a8w8_status_string(a8w8_status status);
 

@@ -37,7 +37,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"a8w8_quantize_rows", "a8w8_linear", "a8w8_mlp_block", "a8w8_layer_linears",
-            "a8w8_layer_linears_prefill",
+            "a8w8_layer_linears_prefill", "a8w8_qk_norm_rope_kv",
             "a8w8_workspace_bytes", "a8w8_status_string", "a8w8_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -153,3 +153,21 @@ def test_layer_prefill_validation(L):
     assert call(x=None) == 1
     assert call(x=MIS) == 3
     assert call(wsp=FAKE + 16) == 3
+
+
+def test_qk_rope_validation(L):
+    """Shape, null and alignment errors are returned before any launch."""
+    f = L.a8w8_qk_norm_rope_kv
+
+    def call(M=1, nq=40, nkv=8, d=128, qkv=FAKE, cos=FAKE, bt=FAKE, kc=FAKE, maxp=64, nb=4):
+        return f(qkv, M, nq, nkv, d, FAKE, FAKE, 1e-6, cos, FAKE, maxp, FAKE, bt, 2, kc, FAKE,
+                 nb, 16, FAKE, None)
+    assert call(M=0) == 0
+    assert call(d=127) == 2                  # odd head_dim
+    assert call(d=1024) == 2                 # above 512
+    assert call(nq=0) == 2
+    assert call(maxp=0) == 2
+    assert call(nb=0) == 2
+    assert call(qkv=None) == 1
+    assert call(kc=None) == 1
+    assert call(cos=FAKE + 2) == 3

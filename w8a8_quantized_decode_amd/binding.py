@@ -98,6 +98,10 @@ def lib() -> ctypes.CDLL:
                                                  _c_i64, _c_i64, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, _vp, _vp, _vp, _vp,
                                                  ctypes.c_size_t, _vp]
+        L.a8w8_qk_norm_rope_kv.restype = ctypes.c_int
+        L.a8w8_qk_norm_rope_kv.argtypes = [_vp, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           _vp, _vp, ctypes.c_float, _vp, _vp, _c_i64, _vp, _vp,
+                                           _c_i64, _vp, _vp, _c_i64, _c_i64, _vp, _vp]
         _LIB = L
     return _LIB
 
@@ -234,6 +238,19 @@ def a8w8_layer_linears_prefill(x, gamma_in, gamma_post, eps, qkv, o, gate, up, d
                                           _ptr(qkv_out), _ptr(h1_out), _ptr(out), _ptr(workspace),
                                           workspace.numel(), _stream(stream))
     _check(st, "a8w8_layer_linears_prefill")
+
+
+def a8w8_qk_norm_rope_kv(qkv, n_q_heads: int, n_kv_heads: int, head_dim: int, q_gamma, k_gamma,
+                         eps, cos_table, sin_table, positions, block_table, k_cache, v_cache,
+                         q_out, stream=None) -> None:
+    M = qkv.shape[0]
+    st = lib().a8w8_qk_norm_rope_kv(_ptr(qkv), M, int(n_q_heads), int(n_kv_heads), int(head_dim),
+                                    _ptr(q_gamma), _ptr(k_gamma), float(eps), _ptr(cos_table),
+                                    _ptr(sin_table), cos_table.shape[0], _ptr(positions),
+                                    _ptr(block_table), block_table.shape[1], _ptr(k_cache),
+                                    _ptr(v_cache), k_cache.shape[0], k_cache.shape[1],
+                                    _ptr(q_out), _stream(stream))
+    _check(st, "a8w8_qk_norm_rope_kv")
 
 
 def a8w8_version() -> int:

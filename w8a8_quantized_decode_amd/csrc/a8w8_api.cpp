@@ -739,4 +739,55 @@ a8w8_status a8w8_layer_linears_prefill(const uint16_t* x_bf16, const uint16_t* g
                          I, pb, nullptr, tm, st);
 }
 
+a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_heads,
+                                 int n_kv_heads, int head_dim, const uint16_t* q_gamma_bf16,
+                                 const uint16_t* k_gamma_bf16, float eps,
+                                 const float* cos_table, const float* sin_table,
+                                 int64_t max_pos, const int32_t* positions,
+                                 const int32_t* block_table, int64_t blocks_per_seq,
+                                 uint16_t* k_cache_bf16, uint16_t* v_cache_bf16,
+                                 int64_t num_blocks, int64_t block_size, uint16_t* q_out_bf16,
+                                 void* stream) {
+  if (M < 0 || M > 65535 || n_q_heads <= 0 || n_kv_heads < 0 || head_dim <= 0 ||
+      head_dim % 2 || head_dim > 512 || max_pos <= 0 || max_pos > (int64_t(1) << 31) - 1)
+    return A8W8_ERR_SHAPE;
+  if (n_q_heads + 2 * int64_t(n_kv_heads) > 65535) return A8W8_ERR_SHAPE;
+  if (n_kv_heads > 0 && (blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0 ||
+                         num_blocks > (int64_t(1) << 31) - 1))
+    return A8W8_ERR_SHAPE;
+  if (M == 0) return A8W8_OK;
+  if (!qkv_bf16 || !q_gamma_bf16 || !cos_table || !sin_table || !positions || !q_out_bf16)
+    return A8W8_ERR_NULL;
+  if (n_kv_heads > 0 && (!k_gamma_bf16 || !block_table || !k_cache_bf16 || !v_cache_bf16))
+    return A8W8_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(cos_table) | reinterpret_cast<uintptr_t>(sin_table) |
+       reinterpret_cast<uintptr_t>(positions) |
+       reinterpret_cast<uintptr_t>(block_table)) & 3u)
+    return A8W8_ERR_ALIGN;
+  QkRopeArgs a{};
+  a.qkv = qkv_bf16;
+  a.M = M;
+  a.n_q = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.head_dim = head_dim;
+  a.ld_qkv = (int64_t(n_q_heads) + 2 * int64_t(n_kv_heads)) * head_dim;
+  a.q_gamma = q_gamma_bf16;
+  a.k_gamma = k_gamma_bf16;
+  a.eps = eps;
+  a.cos_table = cos_table;
+  a.sin_table = sin_table;
+  a.max_pos = max_pos;
+  a.positions = positions;
+  a.block_table = block_table;
+  a.blocks_per_seq = blocks_per_seq;
+  a.k_cache = k_cache_bf16;
+  a.v_cache = v_cache_bf16;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.q_out = q_out_bf16;
+  a.ld_q = int64_t(n_q_heads) * head_dim;
+  A8W8_HIP(launch_qk_rope(a, static_cast<hipStream_t>(stream)));
+  return A8W8_OK;
+}
+
 }  // extern "C"

@@ -38,6 +38,9 @@ __device__ __forceinline__ int64_t prefill_operand_index(int64_t m, int64_t k, i
 
 // Low / high BF16 of a packed pair.
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
+  return __uint_as_float(uint32_t(v) << 16);
+}
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 // Symmetric INT8 code of one value: clamp(rint(v / s), -127, 127), s > 0.

@@ -28,6 +28,28 @@ struct QuantRowsArgs {
 };
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- QK-norm + RoPE + KV
+struct QkRopeArgs {
+  const uint16_t* qkv;      // [M, ld_qkv] BF16: Q heads, then K heads, then V heads
+  int64_t M, ld_qkv;
+  int n_q, n_kv, head_dim;
+  const uint16_t* q_gamma;  // [head_dim] BF16 QK-norm gains
+  const uint16_t* k_gamma;
+  float eps;
+  const float* cos_table;   // [max_pos, head_dim / 2]
+  const float* sin_table;
+  int64_t max_pos;
+  const int32_t* positions;    // [M]
+  const int32_t* block_table;  // [M, blocks_per_seq]
+  int64_t blocks_per_seq;
+  uint16_t* k_cache;        // [num_blocks, block_size, n_kv, head_dim] BF16
+  uint16_t* v_cache;
+  int64_t num_blocks, block_size;
+  uint16_t* q_out;          // [M, ld_q] BF16
+  int64_t ld_q;
+};
+hipError_t launch_qk_rope(const QkRopeArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- weight layouts
 // LAYOUT_ROWMAJOR: w[n * K + k].
 // LAYOUT_TILED: 16-row tiles, one 1 KB block per 64-byte k step, each block in the
