@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--config", type=int, default=2,
                    help="2: layer M=1; 3: 40-layer M=16 stack; 4: W8A16 prefill MLP M=256")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--qk-rope", action="store_true",
+                   help="time the QK-norm + RoPE + KV-cache write step (Qwen3-14B heads, M=1 and 16)")
     p.add_argument("--layer", action="store_true",
                    help="with --config 4: the whole prefill layer (QKV, O and the MLP block)")
     p.add_argument("--graph", type=int, default=1,
@@ -299,6 +301,66 @@ def bench_prefill_layer(args, torch, B) -> None:
         "cpu_baseline": None}))
 
 
+def bench_qk_rope(args, torch, B) -> None:
+    """QK-norm + RoPE + paged BF16 KV-cache write after QKV, Qwen3-14B heads (40 Q and 8 KV
+    heads of 128) at the decode batches 1 and 16: microseconds per call from HIP events
+    over calls replayed from a captured graph, and the bytes the step must move per call (qkv read, q out,
+    K and V written, the gains, the two table rows) over that time against HBM peak."""
+    from w8a8_quantized_decode_amd import synth
+    nq, nkv, d, bs, bps = 40, 8, 128, 16, 64
+    cos, sin = synth.rope_tables(bs * bps, d)
+    rows = []
+    for M in (1, 16):
+        rng = np.random.default_rng(M)
+        qkv = torch.from_numpy(rng.integers(0, 1 << 15, size=(M, (nq + 2 * nkv) * d),
+                                            dtype=np.int16)).to("cuda")
+        g = torch.full((d,), 0x3F80, dtype=torch.int16, device="cuda")   # BF16 1.0
+        pos = torch.from_numpy(rng.integers(0, bs * bps, size=M).astype(np.int32)).to("cuda")
+        bt = torch.from_numpy(np.arange(M * bps, dtype=np.int32).reshape(M, bps)).to("cuda")
+        kc = torch.zeros((M * bps, bs, nkv, d), dtype=torch.int16, device="cuda")
+        vc = torch.zeros_like(kc)
+        q = torch.empty((M, nq * d), dtype=torch.int16, device="cuda")
+        ct, st = torch.from_numpy(cos).to("cuda"), torch.from_numpy(sin).to("cuda")
+
+        def call():
+            B.a8w8_qk_norm_rope_kv(qkv, nq, nkv, d, g, g, 1e-6, ct, st, pos, bt, kc, vc, q)
+        for _ in range(args.warmup):
+            call()
+        # Replayed from a captured graph of 20 calls, so host launch cost does not pace it.
+        gr = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for _ in range(20):
+                call()
+        gr.replay()
+        reps = max(1, args.steps // 20)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / (reps * 20) * 1e3
+        nbytes = M * ((nq + 2 * nkv) * d * 2 + nq * d * 2 + 2 * nkv * d * 2 + 4 + 4 + d * 4) + 2 * d * 2
+        rows.append({"M": M, "us_per_call": round(us, 2), "bytes_per_call": nbytes,
+                     "gb_s": round(nbytes / (us * 1e-6) / 1e9, 2)})
+    r16 = rows[-1]
+    print(json.dumps({
+        "metric": "QK-norm + RoPE + paged BF16 KV-cache write, microseconds per call",
+        "value": r16["us_per_call"], "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r16["us_per_call"] / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (Qwen3-14B head counts, random BF16 rows)",
+        "config": {"workload": "QK-norm + RoPE + KV write, 40 Q / 8 KV heads of 128, M=16",
+                   "per_batch": rows},
+        "roofline": {"bound": "hbm", "achieved": r16["gb_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r16["gb_s"] / HBM_PEAK_GBS, 6), "traffic": None,
+                     "kernel": "qk_rope_kernel (latency-bound: a few KB per call)",
+                     "algorithmic_bytes_per_launch": r16["bytes_per_call"]},
+        "cpu_baseline": None}))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -313,6 +375,9 @@ def main():
     from w8a8_quantized_decode_amd import binding as B
     from w8a8_quantized_decode_amd import synth
 
+    if args.qk_rope:
+        bench_qk_rope(args, torch, B)
+        return
     cfg = synth.CONFIGS[args.config]
     if cfg.kind == "prefill" and args.layer:
         bench_prefill_layer(args, torch, B)
