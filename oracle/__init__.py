@@ -6,6 +6,7 @@ may import this package.  The product path never routes through it.
 
 from .a8w8_oracle import (  # noqa: F401
     bf16_to_f32,
+    decode_attention,
     dequant,
     dequant_weight_bf16,
     down_split,

@@ -461,3 +461,42 @@ def qk_norm_rope_kv(qkv_bits, n_q_heads: int, n_kv_heads: int, head_dim: int, q_
             kc[b, o, h] = rne_bf16(rope_rotate_half(rmsnorm(kv, k_gamma_bits, eps), c, s_))[0]
             vc[b, o, h] = qkv[m, v0 : v0 + d]
     return q_out, kc, vc
+
+
+# ------------------------------------------------------------------ decode attention
+
+def decode_attention(q_bits, n_q_heads: int, n_kv_heads: int, head_dim: int, k_cache_bits,
+                     v_cache_bits, block_table, context_lens, scale):
+    """Decode attention over the paged BF16 KV cache, defined exactly (FP64), then RNE.
+
+    Row ``m`` attends to its positions ``0 .. L-1`` (``L = context_lens[m]``), read from
+    the cache slots ``(block_table[m, j // block_size], j % block_size)``.  Q head ``h``
+    uses KV head ``h // (n_q / n_kv)`` (grouped-query attention; consecutive Q heads share
+    a KV head).  ``o = sum_j softmax_j(scale * q . k_j) v_j`` over exact real numbers
+    (FP64 here), and the output is ``rne_bf16(o)``.  The pages place attention over a BF16
+    KV cache between QKV and O ([PR810] walkthrough: attention loads use BF16 KV caches;
+    [PR48] runner: paged KV cache with a block table) but give none of its arithmetic;
+    this is the plain definition, and a GPU computing it in FP32 is held to the stated
+    BF16 output tolerance.
+    """
+    q = bf16_to_f32(np.asarray(q_bits, dtype=np.uint16)).astype(np.float64)
+    kc = bf16_to_f32(np.asarray(k_cache_bits, dtype=np.uint16)).astype(np.float64)
+    vc = bf16_to_f32(np.asarray(v_cache_bits, dtype=np.uint16)).astype(np.float64)
+    M = q.shape[0]
+    d = head_dim
+    bs = kc.shape[1]
+    group = n_q_heads // n_kv_heads
+    out = np.empty((M, n_q_heads * d), dtype=np.uint16)
+    for m in range(M):
+        L = int(context_lens[m])
+        j = np.arange(L)
+        blocks = np.asarray(block_table[m], dtype=np.int64)[j // bs]
+        for h in range(n_q_heads):
+            g = h // group
+            k = kc[blocks, j % bs, g]                     # [L, d]
+            v = vc[blocks, j % bs, g]
+            s_ = float(scale) * (k @ q[m, h * d : (h + 1) * d])
+            w = np.exp(s_ - s_.max())
+            o = (w / w.sum()) @ v
+            out[m, h * d : (h + 1) * d] = rne_bf16(o.astype(np.float32))
+    return out
