@@ -38,6 +38,7 @@ def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"a8w8_quantize_rows", "a8w8_linear", "a8w8_mlp_block", "a8w8_layer_linears",
             "a8w8_layer_linears_prefill", "a8w8_qk_norm_rope_kv",
+            "a8w8_decode_attention",
             "a8w8_workspace_bytes", "a8w8_status_string", "a8w8_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -171,3 +172,19 @@ def test_qk_rope_validation(L):
     assert call(qkv=None) == 1
     assert call(kc=None) == 1
     assert call(cos=FAKE + 2) == 3
+
+
+def test_attention_validation(L):
+    """Shape, null and alignment errors are returned before any launch."""
+    f = L.a8w8_decode_attention
+
+    def call(M=1, nq=40, nkv=8, d=128, kc=FAKE, bt=FAKE):
+        return f(FAKE, M, nq, nkv, d, kc, FAKE, 16, 16, bt, 4, FAKE, 0.088, FAKE, None)
+    assert call(M=0) == 0
+    assert call(nq=41) == 2                  # n_q % n_kv
+    assert call(nq=72) == 2                  # group of 9 > 8
+    assert call(d=96) == 2                   # d % 64
+    assert call(d=512) == 2
+    assert call(kc=None) == 1
+    assert call(kc=MIS) == 3
+    assert call(bt=FAKE + 2) == 3

@@ -790,4 +790,42 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
   return A8W8_OK;
 }
 
+a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_heads,
+                                  int n_kv_heads, int head_dim, const uint16_t* k_cache_bf16,
+                                  const uint16_t* v_cache_bf16, int64_t num_blocks,
+                                  int64_t block_size, const int32_t* block_table,
+                                  int64_t blocks_per_seq, const int32_t* context_lens,
+                                  float scale, uint16_t* out_bf16, void* stream) {
+  if (M < 0 || M > 65535 || n_kv_heads <= 0 || n_kv_heads > 65535 || n_q_heads <= 0 ||
+      n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > 8 || head_dim <= 0 ||
+      head_dim % 64 || head_dim > 256 || num_blocks <= 0 || block_size <= 0 ||
+      blocks_per_seq <= 0 || num_blocks > (int64_t(1) << 31) - 1)
+    return A8W8_ERR_SHAPE;
+  if (M == 0) return A8W8_OK;
+  if (!q_bf16 || !k_cache_bf16 || !v_cache_bf16 || !block_table || !context_lens || !out_bf16)
+    return A8W8_ERR_NULL;
+  if (!aligned16(k_cache_bf16) || !aligned16(v_cache_bf16) ||
+      ((reinterpret_cast<uintptr_t>(block_table) | reinterpret_cast<uintptr_t>(context_lens)) & 3u))
+    return A8W8_ERR_ALIGN;
+  AttnArgs a{};
+  a.q = q_bf16;
+  a.M = M;
+  a.ld_q = int64_t(n_q_heads) * head_dim;
+  a.n_q = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.group = n_q_heads / n_kv_heads;
+  a.head_dim = head_dim;
+  a.k_cache = k_cache_bf16;
+  a.v_cache = v_cache_bf16;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.block_table = block_table;
+  a.blocks_per_seq = blocks_per_seq;
+  a.context_lens = context_lens;
+  a.scale = scale;
+  a.out = out_bf16;
+  A8W8_HIP(launch_decode_attention(a, static_cast<hipStream_t>(stream)));
+  return A8W8_OK;
+}
+
 }  // extern "C"

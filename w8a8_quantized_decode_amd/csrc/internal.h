@@ -50,6 +50,22 @@ struct QkRopeArgs {
 };
 hipError_t launch_qk_rope(const QkRopeArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- decode attention
+struct AttnArgs {
+  const uint16_t* q;        // [M, ld_q] BF16, n_q heads of head_dim
+  int64_t M, ld_q;
+  int n_q, n_kv, group, head_dim;
+  const uint16_t* k_cache;  // [num_blocks, block_size, n_kv, head_dim] BF16
+  const uint16_t* v_cache;
+  int64_t num_blocks, block_size;
+  const int32_t* block_table;   // [M, blocks_per_seq]
+  int64_t blocks_per_seq;
+  const int32_t* context_lens;  // [M]
+  float scale;
+  uint16_t* out;            // [M, ld_q] BF16
+};
+hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- weight layouts
 // LAYOUT_ROWMAJOR: w[n * K + k].
 // LAYOUT_TILED: 16-row tiles, one 1 KB block per 64-byte k step, each block in the
