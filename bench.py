@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--qk-rope", action="store_true",
                    help="time the QK-norm + RoPE + KV-cache write step (Qwen3-14B heads, M=1 and 16)")
+    p.add_argument("--attention", action="store_true",
+                   help="time decode attention over the paged cache (Qwen3-14B heads, M=1 and 16)")
+    p.add_argument("--context", type=int, default=1024, help="context length for --attention")
     p.add_argument("--layer", action="store_true",
                    help="with --config 4: the whole prefill layer (QKV, O and the MLP block)")
     p.add_argument("--graph", type=int, default=1,
@@ -361,6 +364,65 @@ def bench_qk_rope(args, torch, B) -> None:
         "cpu_baseline": None}))
 
 
+def bench_attention(args, torch, B) -> None:
+    """Decode attention over the paged BF16 KV cache, Qwen3-14B heads (40 Q, 8 KV of 128),
+    every row at the same context length, at the decode batches 1 and 16: microseconds per
+    call (graph-replayed) and the cache bytes the step must read (K and V of every
+    position of every row) over that time against HBM peak."""
+    import math
+    nq, nkv, d, bs = 40, 8, 128, 16
+    L = args.context
+    bps = (L + bs - 1) // bs
+    rows = []
+    for M in (1, 16):
+        rng = np.random.default_rng(M)
+        nblocks = M * bps
+        q = torch.from_numpy(rng.integers(0x3C00, 0x3F80, size=(M, nq * d), dtype=np.int16)).to("cuda")
+        kc = torch.from_numpy(rng.integers(0x3C00, 0x3F80, size=(nblocks, bs, nkv, d),
+                                           dtype=np.int16)).to("cuda")
+        vc = torch.from_numpy(rng.integers(0x3C00, 0x3F80, size=(nblocks, bs, nkv, d),
+                                           dtype=np.int16)).to("cuda")
+        bt = torch.from_numpy(rng.permutation(nblocks).astype(np.int32).reshape(M, bps)).to("cuda")
+        lens = torch.full((M,), L, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(q)
+
+        def call():
+            B.a8w8_decode_attention(q, nq, nkv, d, kc, vc, bt, lens, 1.0 / math.sqrt(d), out)
+        for _ in range(3):
+            call()
+        gr = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for _ in range(10):
+                call()
+        gr.replay()
+        reps = max(1, args.steps // 10)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / (reps * 10) * 1e3
+        nbytes = M * (L * nkv * d * 2 * 2 + 2 * nq * d * 2)
+        rows.append({"M": M, "context": L, "us_per_call": round(us, 2), "bytes_per_call": nbytes,
+                     "gb_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    r16 = rows[-1]
+    print(json.dumps({
+        "metric": "decode attention over the paged BF16 KV cache, microseconds per call",
+        "value": r16["us_per_call"], "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": 3, "ms_per_step": round(r16["us_per_call"] / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (Qwen3-14B head counts, random BF16 cache)",
+        "config": {"workload": f"decode attention, 40 Q / 8 KV heads of 128, context {L}, M=16",
+                   "per_batch": rows},
+        "roofline": {"bound": "hbm", "achieved": r16["gb_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r16["gb_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_attention_kernel", "algorithmic_bytes_per_launch": r16["bytes_per_call"]},
+        "cpu_baseline": None}))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -377,6 +439,9 @@ def main():
 
     if args.qk_rope:
         bench_qk_rope(args, torch, B)
+        return
+    if args.attention:
+        bench_attention(args, torch, B)
         return
     cfg = synth.CONFIGS[args.config]
     if cfg.kind == "prefill" and args.layer:

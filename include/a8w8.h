@@ -333,7 +333,7 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
  * (block_table[m, j / block_size], j % block_size); Q head h uses KV head
  * h / (n_q / n_kv).  out = rne_bf16(sum_j softmax_j(scale * q . k_j) v_j), computed in
  * FP32 (online softmax over chunks of 64 positions).  Shapes: n_q % n_kv == 0,
- * n_q / n_kv <= 8, d % 64 == 0 and d <= 256, M <= 65535.  A row with L outside
+ * n_q / n_kv <= 8, d % 64 == 0 and d <= 128, M <= 65535.  A row with L outside
  * [1, blocks_per_seq * block_size] is skipped (its output is not written); a position
  * whose block number is out of range is left out of the softmax.  One kernel, one
  * workgroup per (row, KV head).

@@ -184,7 +184,7 @@ def test_attention_validation(L):
     assert call(nq=41) == 2                  # n_q % n_kv
     assert call(nq=72) == 2                  # group of 9 > 8
     assert call(d=96) == 2                   # d % 64
-    assert call(d=512) == 2
+    assert call(d=256) == 2                  # above 128
     assert call(kc=None) == 1
     assert call(kc=MIS) == 3
     assert call(bt=FAKE + 2) == 3

@@ -798,7 +798,7 @@ a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_hea
                                   float scale, uint16_t* out_bf16, void* stream) {
   if (M < 0 || M > 65535 || n_kv_heads <= 0 || n_kv_heads > 65535 || n_q_heads <= 0 ||
       n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > 8 || head_dim <= 0 ||
-      head_dim % 64 || head_dim > 256 || num_blocks <= 0 || block_size <= 0 ||
+      head_dim % 64 || head_dim > 128 || num_blocks <= 0 || block_size <= 0 ||
       blocks_per_seq <= 0 || num_blocks > (int64_t(1) << 31) - 1)
     return A8W8_ERR_SHAPE;
   if (M == 0) return A8W8_OK;

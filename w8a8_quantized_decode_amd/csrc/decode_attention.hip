@@ -2,7 +2,7 @@
 // walkthrough: attention loads use BF16 KV caches; pypto-serving PR #48: paged KV cache
 // with a block table).
 //
-// One workgroup of four waves per (row, KV head) serves the group's Q heads (grouped-
+// One workgroup of 16 waves per (row, KV head) serves the group's Q heads (grouped-
 // query attention: Q head h reads KV head h / (n_q / n_kv)).  The query rows sit in LDS
 // (every lane reads them as broadcasts).  The waves take chunks of 64 positions in turn:
 //   * scores: lane l takes position j = chunk + l, reads its whole key row and forms the
@@ -11,7 +11,7 @@
 //     wave's running maximum and normalizer, rescaling its output accumulators;
 //   * values: lane l owns head dimensions l, l + 64, ...; the chunk's weights go through
 //     LDS and each value row is read once, coalesced.
-// At the end the four waves' states are combined through LDS and the output is narrowed
+// At the end the waves' states are combined through LDS and the output is narrowed
 // to BF16 with RNE.  FP32 throughout; the oracle is the exact definition.
 #include "device_common.h"
 #include "internal.h"
@@ -19,9 +19,9 @@
 namespace a8w8 {
 namespace {
 
-constexpr int kAttWaves = 4;
+constexpr int kAttWaves = 16;      // a chunk of 64 positions per wave at a time
 constexpr int kAttMaxGroup = 8;    // Q heads per KV head
-constexpr int kAttMaxDim = 256;    // head_dim
+constexpr int kAttMaxDim = 128;    // head_dim
 constexpr int kAttDimPerLane = kAttMaxDim / kWave;
 
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -38,6 +38,7 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 __global__ __launch_bounds__(kAttWaves * kWave) void decode_attention_kernel(AttnArgs p) {
   __shared__ float qs[kAttMaxGroup][kAttMaxDim];
   __shared__ float pw[kAttWaves][kAttMaxGroup][kWave];
+  __shared__ int64_t pslot[kAttWaves][kWave];  // cache slot of each chunk position (-1: none)
   __shared__ float st_m[kAttWaves][kAttMaxGroup], st_l[kAttWaves][kAttMaxGroup];
   __shared__ float st_o[kAttWaves][kAttMaxGroup][kAttMaxDim];
 
@@ -75,24 +76,32 @@ __global__ __launch_bounds__(kAttWaves * kWave) void decode_attention_kernel(Att
       live = blk >= 0 && blk < p.num_blocks;
       slot = (int64_t(blk) * p.block_size + j % p.block_size) * row_stride + int64_t(kvh) * d;
     }
+    pslot[wave][lane] = live ? slot : -1;
     float s[kAttMaxGroup];
 #pragma unroll
     for (int h = 0; h < kAttMaxGroup; ++h) s[h] = 0.0f;
-    if (live) {
-      const uint16_t* kr = p.k_cache + slot;
-      for (int i = 0; i < d; i += 8) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(kr + i);
-        float kf[8];
+    {
+      // The key row in groups of 64 elements: eight 16-byte loads issued together, then
+      // used (a lane without a position reads row 0 and its scores are discarded).
+      const uint16_t* kr = p.k_cache + (live ? slot : 0);
+      for (int i0 = 0; i0 < d; i0 += 64) {
+        u32x4 kv[8];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          kf[2 * c] = bf16_lo(kv[c]);
-          kf[2 * c + 1] = bf16_hi(kv[c]);
+        for (int u = 0; u < 8; ++u) kv[u] = *reinterpret_cast<const u32x4*>(kr + i0 + 8 * u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float kf[8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            kf[2 * c] = bf16_lo(kv[u][c]);
+            kf[2 * c + 1] = bf16_hi(kv[u][c]);
+          }
+#pragma unroll
+          for (int h = 0; h < kAttMaxGroup; ++h)
+            if (h < G)
+#pragma unroll
+              for (int c = 0; c < 8; ++c) s[h] = fmaf(qs[h][i0 + 8 * u + c], kf[c], s[h]);
         }
-#pragma unroll
-        for (int h = 0; h < kAttMaxGroup; ++h)
-          if (h < G)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) s[h] = fmaf(qs[h][i + c], kf[c], s[h]);
       }
     }
     // Online softmax per head.
@@ -118,30 +127,37 @@ __global__ __launch_bounds__(kAttWaves * kWave) void decode_attention_kernel(Att
 #pragma unroll
       for (int c = 0; c < kAttDimPerLane; ++c) acc[h][c] *= scale_old[h];
     }
+    // Eight positions per step: their slots come from LDS, all their value loads are
+    // issued before any is used (a position without a slot reads row 0 of the cache and
+    // has weight 0).
     const int32_t nj = (L - base) < kWave ? (L - base) : kWave;
-    for (int32_t jj = 0; jj < nj; ++jj) {
-      const int32_t jp = base + jj;
-      const int32_t blk = bt[jp / p.block_size];
-      if (blk < 0 || blk >= p.num_blocks) continue;
-      const uint16_t* vr = p.v_cache + (int64_t(blk) * p.block_size + jp % p.block_size) * row_stride +
-                           int64_t(kvh) * d;
-      float vf[kAttDimPerLane];
+    for (int32_t jj = 0; jj < nj; jj += 8) {
+      float vf[8][kAttDimPerLane];
 #pragma unroll
-      for (int c = 0; c < kAttDimPerLane; ++c) {
-        const int i = lane + c * kWave;
-        vf[c] = i < d ? bf16_bits_to_f32(vr[i]) : 0.0f;
+      for (int u = 0; u < 8; ++u) {
+        const int64_t sl = (jj + u < nj) ? pslot[wave][jj + u] : -1;
+        const uint16_t* vr = p.v_cache + (sl >= 0 ? sl : 0);
+#pragma unroll
+        for (int c = 0; c < kAttDimPerLane; ++c) {
+          const int i = lane + c * kWave;
+          vf[u][c] = i < d ? bf16_bits_to_f32(vr[i]) : 0.0f;
+        }
       }
 #pragma unroll
-      for (int h = 0; h < kAttMaxGroup; ++h) {
-        if (h >= G) break;
-        const float w = pw[wave][h][jj];
+      for (int u = 0; u < 8; ++u) {
+        if (jj + u >= nj) break;
 #pragma unroll
-        for (int c = 0; c < kAttDimPerLane; ++c) acc[h][c] = fmaf(w, vf[c], acc[h][c]);
+        for (int h = 0; h < kAttMaxGroup; ++h) {
+          if (h >= G) break;
+          const float w = pw[wave][h][jj + u];
+#pragma unroll
+          for (int c = 0; c < kAttDimPerLane; ++c) acc[h][c] = fmaf(w, vf[u][c], acc[h][c]);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
-  // Combine the four waves.
+  // Combine the waves.
   for (int h = 0; h < G; ++h) {
     if (lane == 0) {
       st_m[wave][h] = run_m[h];
