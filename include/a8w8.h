@@ -326,24 +326,32 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
  * Decode attention over the paged BF16 KV cache, between QKV (after
  * a8w8_qk_norm_rope_kv) and O (pypto-lib PR #810 walkthrough: attention loads use BF16
  * KV caches; pypto-serving PR #48: paged KV cache with a block table).
- *   q_bf16 [M, n_q * d]; k_cache, v_cache [num_blocks, block_size, n_kv, d] BF16 (16-byte
- *   aligned); block_table [M, blocks_per_seq] int32; context_lens [M] int32;
- *   out_bf16 [M, n_q * d].
+ *   q_bf16 [M, n_q * d] and out_bf16 [M, n_q * d] (16-byte aligned);
+ *   k_cache, v_cache [num_blocks, block_size, n_kv, d] BF16 (16-byte aligned);
+ *   block_table [M, blocks_per_seq] int32; context_lens [M] int32.
  * Row m attends to its positions 0 .. L-1 (L = context_lens[m]) at the cache slots
  * (block_table[m, j / block_size], j % block_size); Q head h uses KV head
  * h / (n_q / n_kv).  out = rne_bf16(sum_j softmax_j(scale * q . k_j) v_j), computed in
- * FP32 (online softmax over chunks of 64 positions).  Shapes: n_q % n_kv == 0,
- * n_q / n_kv <= 8, d % 64 == 0 and d <= 128, M <= 65535.  A row with L outside
+ * FP32 with an online softmax.  Shapes: n_q % n_kv == 0, n_q / n_kv <= 8, d in {64, 128},
+ * M <= 65535, blocks_per_seq * block_size <= 2^30.  A row with L outside
  * [1, blocks_per_seq * block_size] is skipped (its output is not written); a position
- * whose block number is out of range is left out of the softmax.  One kernel, one
- * workgroup per (row, KV head).
+ * whose block number is out of range is left out of the softmax.
+ * workspace: NULL, or ws_bytes >= a8w8_decode_attention_workspace_bytes(M, n_q, n_kv,
+ * d, blocks_per_seq * block_size), 256-byte aligned scratch (contents on entry do not
+ * matter).  With a workspace the context of each row is cut into splits that separate
+ * workgroups take (one kernel for the splits, one that merges them; the merge runs
+ * only when there is more than one split); with NULL one workgroup per (row, KV head)
+ * walks the whole context (one kernel; slow for long contexts at small M).
  */
+size_t a8w8_decode_attention_workspace_bytes(int64_t M, int n_q_heads, int n_kv_heads,
+                                             int head_dim, int64_t max_context);
 a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_heads,
                                   int n_kv_heads, int head_dim, const uint16_t* k_cache_bf16,
                                   const uint16_t* v_cache_bf16, int64_t num_blocks,
                                   int64_t block_size, const int32_t* block_table,
                                   int64_t blocks_per_seq, const int32_t* context_lens,
-                                  float scale, uint16_t* out_bf16, void* stream);
+                                  float scale, uint16_t* out_bf16, void* workspace,
+                                  size_t ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* a8w8_status_string(a8w8_status status);

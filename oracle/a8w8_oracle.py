@@ -477,7 +477,9 @@ def decode_attention(q_bits, n_q_heads: int, n_kv_heads: int, head_dim: int, k_c
     KV cache between QKV and O ([PR810] walkthrough: attention loads use BF16 KV caches;
     [PR48] runner: paged KV cache with a block table) but give none of its arithmetic;
     this is the plain definition, and a GPU computing it in FP32 is held to the stated
-    BF16 output tolerance.
+    BF16 output tolerance.  A position whose block number lies outside ``[0, num_blocks)``
+    is left out of the softmax (the library's stated behaviour for a hole in the block
+    table); a row with no position left gets zeros.
     """
     q = bf16_to_f32(np.asarray(q_bits, dtype=np.uint16)).astype(np.float64)
     kc = bf16_to_f32(np.asarray(k_cache_bits, dtype=np.uint16)).astype(np.float64)
@@ -491,7 +493,12 @@ def decode_attention(q_bits, n_q_heads: int, n_kv_heads: int, head_dim: int, k_c
         L = int(context_lens[m])
         j = np.arange(L)
         blocks = np.asarray(block_table[m], dtype=np.int64)[j // bs]
+        keep = (blocks >= 0) & (blocks < kc.shape[0])
+        j, blocks = j[keep], blocks[keep]
         for h in range(n_q_heads):
+            if j.size == 0:
+                out[m, h * d : (h + 1) * d] = 0
+                continue
             g = h // group
             k = kc[blocks, j % bs, g]                     # [L, d]
             v = vc[blocks, j % bs, g]

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"a8w8_quantize_rows", "a8w8_linear", "a8w8_mlp_block", "a8w8_layer_linears",
             "a8w8_layer_linears_prefill", "a8w8_qk_norm_rope_kv",
-            "a8w8_decode_attention",
+            "a8w8_decode_attention", "a8w8_decode_attention_workspace_bytes",
             "a8w8_workspace_bytes", "a8w8_status_string", "a8w8_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -175,16 +175,34 @@ def test_qk_rope_validation(L):
 
 
 def test_attention_validation(L):
-    """Shape, null and alignment errors are returned before any launch."""
+    """Shape, null, alignment and workspace errors are returned before any launch."""
     f = L.a8w8_decode_attention
 
-    def call(M=1, nq=40, nkv=8, d=128, kc=FAKE, bt=FAKE):
-        return f(FAKE, M, nq, nkv, d, kc, FAKE, 16, 16, bt, 4, FAKE, 0.088, FAKE, None)
+    def call(M=1, nq=40, nkv=8, d=128, q=FAKE, kc=FAKE, bt=FAKE, bps=4, ws=None, wsb=0):
+        return f(q, M, nq, nkv, d, kc, FAKE, 16, 16, bt, bps, FAKE, 0.088, FAKE, ws, wsb, None)
     assert call(M=0) == 0
     assert call(nq=41) == 2                  # n_q % n_kv
     assert call(nq=72) == 2                  # group of 9 > 8
     assert call(d=96) == 2                   # d % 64
     assert call(d=256) == 2                  # above 128
+    assert call(bps=(1 << 26) + 1) == 2      # blocks_per_seq * block_size > 2^30
     assert call(kc=None) == 1
     assert call(kc=MIS) == 3
+    assert call(q=FAKE + 8) == 3
     assert call(bt=FAKE + 2) == 3
+    # context 1024 at M=1 is cut into splits: the workspace must fit them and be aligned
+    need = B.a8w8_decode_attention_workspace_bytes(1, 40, 8, 128, 64 * 16)
+    assert need == 1 * 40 * 16 * (128 + 2) * 4
+    assert call(bps=64, ws=FAKE, wsb=need - 1) == 4
+    assert call(bps=64, ws=FAKE + 16, wsb=need) == 3
+
+
+def test_attention_workspace_bytes(L):
+    ws = B.a8w8_decode_attention_workspace_bytes
+    assert ws(1, 40, 8, 128, 64) == 0            # one split: no workspace
+    assert ws(1, 40, 8, 128, 4096) == 40 * 64 * 130 * 4
+    # many rows: splits grow in whole chunks so the grid stays near 4096 waves
+    assert ws(16, 40, 8, 128, 4096) == 16 * 40 * 32 * 130 * 4
+    assert ws(1, 41, 8, 128, 4096) == 0          # invalid shapes
+    assert ws(1, 40, 8, 96, 4096) == 0
+    assert ws(1, 40, 8, 128, 0) == 0

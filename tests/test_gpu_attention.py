@@ -2,10 +2,13 @@
 
 The oracle is the exact definition (FP64); the kernel computes in FP32 with an online
 softmax, so outputs are held to the stated BF16 tolerance: relative 1e-2, absolute 1e-2
-where |y| < 1.  Cases: the Qwen3-14B head counts (40 Q, 8 KV heads of 128) at the decode
-batches 1 and 16 with context lengths that cross chunk and block boundaries, a toy shape
-with a different group and head size, and a row with an out-of-range length, which must
-leave its output untouched.
+where |y| < 1.  Each case runs twice: with a workspace (the context cut into splits that
+separate workgroups take, then merged) and without one (one workgroup walks the whole
+context).  Cases: the Qwen3-14B head counts (40 Q, 8 KV heads of 128) at the decode
+batches 1 and 16 with context lengths that cross chunk and block boundaries, a context
+of 4096 at batch 1 (64 splits), a toy shape with a different group and head size, a row
+with an out-of-range length, which must leave its output untouched, and block tables with
+holes (block numbers out of range), whose positions are left out.
 """
 
 import math
@@ -19,8 +22,11 @@ from gpu_helpers import announce, dev, host, torch
 
 pytestmark = pytest.mark.gpu
 
+MODES = ["split", "whole"]
 
-def _run(lens, nq, nkv, d, bs, bps, seed):
+
+def _run(lens, nq, nkv, d, bs, bps, seed, mode, holes=0):
+    from w8a8_quantized_decode_amd import binding as B
     rng = np.random.default_rng(seed)
     M = len(lens)
     nblocks = M * bps + 3
@@ -28,12 +34,21 @@ def _run(lens, nq, nkv, d, bs, bps, seed):
     kc = O.rne_bf16(rng.normal(size=(nblocks, bs, nkv, d)).astype(np.float32))
     vc = O.rne_bf16(rng.normal(size=(nblocks, bs, nkv, d)).astype(np.float32))
     bt = rng.permutation(nblocks)[: M * bps].reshape(M, bps).astype(np.int32)
+    for i in range(holes):                      # out-of-range block numbers, both signs
+        bt[i % M, rng.integers(0, bps)] = -1 - i if i % 2 == 0 else nblocks + i
     lens = np.asarray(lens, np.int32)
     scale = 1.0 / math.sqrt(d)
     good = (lens >= 1) & (lens <= bs * bps)
     out = torch().full((M, nq * d), 0x7FC0, dtype=torch().int16, device="cuda")  # BF16 NaN
-    from w8a8_quantized_decode_amd import binding as B
-    B.a8w8_decode_attention(dev(q), nq, nkv, d, dev(kc), dev(vc), dev(bt), dev(lens), scale, out)
+    ws = None
+    if mode == "split":
+        nbytes = B.a8w8_decode_attention_workspace_bytes(M, nq, nkv, d, bs * bps)
+        if nbytes:
+            ws = torch().full((nbytes,), 0x7F, dtype=torch().uint8, device="cuda")
+    print(f"[case] M={M} nq={nq} nkv={nkv} d={d} bs={bs} bps={bps} mode={mode} "
+          f"workspace={0 if ws is None else ws.numel()}", flush=True)
+    B.a8w8_decode_attention(dev(q), nq, nkv, d, dev(kc), dev(vc), dev(bt), dev(lens), scale, out,
+                            workspace=ws)
     torch().cuda.synchronize()
     got = host(out, np.uint16)
     assert np.all(got[~good] == 0x7FC0)
@@ -46,19 +61,33 @@ def _run(lens, nq, nkv, d, bs, bps, seed):
     assert np.all(ok), f"{np.count_nonzero(~ok)} outputs beyond tolerance"
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("M", [1, 16])
-def test_attention_qwen3_14b(M):
-    announce(f"decode attention qwen3-14b M={M}")
+def test_attention_qwen3_14b(M, mode):
+    announce(f"decode attention qwen3-14b M={M} {mode}")
     lens = np.random.default_rng(100 + M).integers(1, 1024, size=M)
     lens[0] = 1 if M > 1 else 777
-    _run(lens, 40, 8, 128, bs=16, bps=64, seed=M)
+    _run(lens, 40, 8, 128, bs=16, bps=64, seed=M, mode=mode)
 
 
-def test_attention_toy_group4_d64():
-    announce("decode attention toy group 4 d=64")
-    _run([1, 63, 64, 65, 129, 200], 8, 2, 64, bs=8, bps=32, seed=3)
+def test_attention_qwen3_14b_context_4096():
+    announce("decode attention qwen3-14b M=1 context 4096 split")
+    _run([4096], 40, 8, 128, bs=16, bps=256, seed=7, mode="split")
 
 
-def test_attention_skips_out_of_range_rows():
-    announce("decode attention out-of-range lengths")
-    _run([5, 0, 70, 4096], 4, 1, 128, bs=16, bps=8, seed=4)
+@pytest.mark.parametrize("mode", MODES)
+def test_attention_toy_group4_d64(mode):
+    announce(f"decode attention toy group 4 d=64 {mode}")
+    _run([1, 63, 64, 65, 129, 200], 8, 2, 64, bs=8, bps=32, seed=3, mode=mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_attention_skips_out_of_range_rows(mode):
+    announce(f"decode attention out-of-range lengths {mode}")
+    _run([5, 0, 70, 4096], 4, 1, 128, bs=16, bps=8, seed=4, mode=mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_attention_block_table_holes(mode):
+    announce(f"decode attention block-table holes {mode}")
+    _run([300, 129, 64, 17], 16, 2, 128, bs=16, bps=20, seed=9, mode=mode, holes=6)

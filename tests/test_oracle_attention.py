@@ -71,3 +71,18 @@ def test_brute_force_small():
                 o_i = sum(wj * float(vf[b, o, g, i]) for wj, (b, o) in zip(w, slots)) / tot
                 want = rne_bf16(np.array([o_i], np.float32))[0]
                 assert out[m, h * d + i] == want, (m, h, i)
+
+
+def test_block_table_holes_are_left_out():
+    """A block number outside [0, num_blocks) drops its positions: a table with a hole in
+    the middle gives what the table without that block gives over the shorter context,
+    and a row with nothing left gives zeros."""
+    rng = np.random.default_rng(5)
+    nq, nkv, d, bs = 4, 2, 16, 4
+    kc, vc = _cache(rng, 4, bs, nkv, d)
+    q = rne_bf16(rng.normal(size=(2, nq * d)).astype(np.float32))
+    holed = np.array([[2, -1, 0], [7, 4, -3]], np.int32)
+    out = decode_attention(q, nq, nkv, d, kc, vc, holed, [10, 9], 0.25)
+    compact = decode_attention(q[:1], nq, nkv, d, kc, vc, np.array([[2, 0]], np.int32), [6], 0.25)
+    assert np.array_equal(out[0], compact[0])
+    assert np.all(out[1] == 0)

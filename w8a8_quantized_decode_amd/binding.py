@@ -105,7 +105,10 @@ def lib() -> ctypes.CDLL:
         L.a8w8_decode_attention.restype = ctypes.c_int
         L.a8w8_decode_attention.argtypes = [_vp, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp,
-                                            ctypes.c_float, _vp, _vp]
+                                            ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
+        L.a8w8_decode_attention_workspace_bytes.restype = ctypes.c_size_t
+        L.a8w8_decode_attention_workspace_bytes.argtypes = [_c_i64, ctypes.c_int, ctypes.c_int,
+                                                            ctypes.c_int, _c_i64]
         _LIB = L
     return _LIB
 
@@ -257,13 +260,26 @@ def a8w8_qk_norm_rope_kv(qkv, n_q_heads: int, n_kv_heads: int, head_dim: int, q_
     _check(st, "a8w8_qk_norm_rope_kv")
 
 
+def a8w8_decode_attention_workspace_bytes(M: int, n_q_heads: int, n_kv_heads: int,
+                                          head_dim: int, max_context: int) -> int:
+    return int(lib().a8w8_decode_attention_workspace_bytes(int(M), int(n_q_heads),
+                                                           int(n_kv_heads), int(head_dim),
+                                                           int(max_context)))
+
+
 def a8w8_decode_attention(q, n_q_heads: int, n_kv_heads: int, head_dim: int, k_cache, v_cache,
-                          block_table, context_lens, scale: float, out, stream=None) -> None:
+                          block_table, context_lens, scale: float, out, workspace=None,
+                          stream=None) -> None:
+    """workspace: None or a uint8 device tensor of at least
+    a8w8_decode_attention_workspace_bytes(...) bytes."""
     M = q.shape[0]
     st = lib().a8w8_decode_attention(_ptr(q), M, int(n_q_heads), int(n_kv_heads), int(head_dim),
                                      _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
                                      k_cache.shape[1], _ptr(block_table), block_table.shape[1],
-                                     _ptr(context_lens), float(scale), _ptr(out), _stream(stream))
+                                     _ptr(context_lens), float(scale), _ptr(out),
+                                     _ptr(workspace) if workspace is not None else None,
+                                     workspace.numel() if workspace is not None else 0,
+                                     _stream(stream))
     _check(st, "a8w8_decode_attention")
 
 

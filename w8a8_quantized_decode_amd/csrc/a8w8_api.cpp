@@ -790,23 +790,56 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
   return A8W8_OK;
 }
 
+// Positions per split: one wave per 64 positions while that keeps the grid under
+// kAttnTargetWaves waves, otherwise whole multiples of 64 so that it does.
+constexpr int64_t kAttnTargetWaves = 4096;
+static int64_t attn_split_len(int64_t M, int n_kv, int64_t max_ctx) {
+  const int64_t chunks = (max_ctx + 63) / 64;
+  int64_t per = (M * n_kv * chunks + kAttnTargetWaves - 1) / kAttnTargetWaves;
+  if (per < 1) per = 1;
+  if (per > chunks) per = chunks;
+  return per * 64;
+}
+
+static bool attn_shapes_ok(int64_t M, int n_q, int n_kv, int d, int64_t max_ctx) {
+  return M >= 0 && M <= 65535 && n_kv > 0 && n_kv <= 65535 && n_q > 0 && n_q % n_kv == 0 &&
+         n_q / n_kv <= 8 && (d == 64 || d == 128) && max_ctx > 0 &&
+         max_ctx <= (int64_t(1) << 30);
+}
+
+size_t a8w8_decode_attention_workspace_bytes(int64_t M, int n_q_heads, int n_kv_heads,
+                                             int head_dim, int64_t max_context) {
+  if (!attn_shapes_ok(M, n_q_heads, n_kv_heads, head_dim, max_context)) return 0;
+  const int64_t split = attn_split_len(M, n_kv_heads, max_context);
+  const int64_t S = (max_context + split - 1) / split;
+  if (S <= 1) return 0;
+  int64_t n = 0;
+  if (__builtin_mul_overflow(M * n_q_heads, S, &n) ||
+      __builtin_mul_overflow(n, int64_t(head_dim + 2) * int64_t(sizeof(float)), &n))
+    return 0;
+  return static_cast<size_t>(n);
+}
+
 a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_heads,
                                   int n_kv_heads, int head_dim, const uint16_t* k_cache_bf16,
                                   const uint16_t* v_cache_bf16, int64_t num_blocks,
                                   int64_t block_size, const int32_t* block_table,
                                   int64_t blocks_per_seq, const int32_t* context_lens,
-                                  float scale, uint16_t* out_bf16, void* stream) {
-  if (M < 0 || M > 65535 || n_kv_heads <= 0 || n_kv_heads > 65535 || n_q_heads <= 0 ||
-      n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > 8 || head_dim <= 0 ||
-      head_dim % 64 || head_dim > 128 || num_blocks <= 0 || block_size <= 0 ||
-      blocks_per_seq <= 0 || num_blocks > (int64_t(1) << 31) - 1)
+                                  float scale, uint16_t* out_bf16, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  if (num_blocks <= 0 || block_size <= 0 || blocks_per_seq <= 0 ||
+      num_blocks > (int64_t(1) << 31) - 1 || block_size > (int64_t(1) << 31) - 1 ||
+      blocks_per_seq > (int64_t(1) << 30) / block_size ||
+      !attn_shapes_ok(M, n_q_heads, n_kv_heads, head_dim, blocks_per_seq * block_size))
     return A8W8_ERR_SHAPE;
   if (M == 0) return A8W8_OK;
   if (!q_bf16 || !k_cache_bf16 || !v_cache_bf16 || !block_table || !context_lens || !out_bf16)
     return A8W8_ERR_NULL;
-  if (!aligned16(k_cache_bf16) || !aligned16(v_cache_bf16) ||
+  if (!aligned16(q_bf16) || !aligned16(out_bf16) || !aligned16(k_cache_bf16) ||
+      !aligned16(v_cache_bf16) ||
       ((reinterpret_cast<uintptr_t>(block_table) | reinterpret_cast<uintptr_t>(context_lens)) & 3u))
     return A8W8_ERR_ALIGN;
+  const int64_t max_ctx = blocks_per_seq * block_size;
   AttnArgs a{};
   a.q = q_bf16;
   a.M = M;
@@ -824,6 +857,21 @@ a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_hea
   a.context_lens = context_lens;
   a.scale = scale;
   a.out = out_bf16;
+  if (workspace == nullptr) {
+    a.split_len = (max_ctx + 63) / 64 * 64;  // one split: no workspace needed
+  } else {
+    a.split_len = attn_split_len(M, n_kv_heads, max_ctx);
+  }
+  a.n_split = (max_ctx + a.split_len - 1) / a.split_len;
+  if (a.n_split > 1) {
+    const size_t need =
+        a8w8_decode_attention_workspace_bytes(M, n_q_heads, n_kv_heads, head_dim, max_ctx);
+    if (need == 0) return A8W8_ERR_SHAPE;  // partials beyond the addressable range
+    if (ws_bytes < need) return A8W8_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return A8W8_ERR_ALIGN;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + M * n_q_heads * a.n_split * head_dim;
+  }
   A8W8_HIP(launch_decode_attention(a, static_cast<hipStream_t>(stream)));
   return A8W8_OK;
 }

@@ -2,199 +2,314 @@
 // walkthrough: attention loads use BF16 KV caches; pypto-serving PR #48: paged KV cache
 // with a block table).
 //
-// One workgroup of 16 waves per (row, KV head) serves the group's Q heads (grouped-
-// query attention: Q head h reads KV head h / (n_q / n_kv)).  The query rows sit in LDS
-// (every lane reads them as broadcasts).  The waves take chunks of 64 positions in turn:
-//   * scores: lane l takes position j = chunk + l, reads its whole key row and forms the
-//     scaled dot product with every Q head of the group (FP32);
-//   * online softmax: per head, the chunk's maximum and sum across the wave update the
-//     wave's running maximum and normalizer, rescaling its output accumulators;
-//   * values: lane l owns head dimensions l, l + 64, ...; the chunk's weights go through
-//     LDS and each value row is read once, coalesced.
-// At the end the waves' states are combined through LDS and the output is narrowed
-// to BF16 with RNE.  FP32 throughout; the oracle is the exact definition.
+// The context of each (row, KV head) is cut into splits of split_len positions; one
+// wave per (split, KV head, row) serves the group's Q heads (grouped-query attention:
+// Q head h reads KV head h / (n_q / n_kv)) and walks its split in chunks of 64
+// positions:
+//   * scores: a key row of D BF16 values is read by D/8 lanes, 16 bytes each, so one
+//     load instruction covers 64/(D/8) rows.  Each lane keeps the matching 8 query
+//     values of every head in registers, forms 8-term partial dot products, and the
+//     row's lanes add them with DPP row permutations (no LDS traffic);
+//   * online softmax: per head, the chunk's maximum and sum over the wave update the
+//     running maximum and normalizer and rescale the output accumulators;
+//   * values: value rows are read like key rows; each lane accumulates its 8 output
+//     dimensions over the rows it reads, with the weights taken from a 64-entry LDS
+//     table, and the row groups are summed once at the end of the split.
+// With one split the wave writes rne_bf16(o / l) directly; otherwise it writes the
+// split's FP32 (max, normalizer, unnormalized output) and a second kernel merges the
+// splits of each (row, Q head).  FP32 throughout; the oracle is the exact definition.
 #include "device_common.h"
 #include "internal.h"
 
 namespace a8w8 {
 namespace {
 
-constexpr int kAttWaves = 16;      // a chunk of 64 positions per wave at a time
-constexpr int kAttMaxGroup = 8;    // Q heads per KV head
-constexpr int kAttMaxDim = 128;    // head_dim
-constexpr int kAttDimPerLane = kAttMaxDim / kWave;
+// DPP control words (row = 16 lanes): quad_perm(1,0,3,2), quad_perm(2,3,0,1), row
+// half-mirror (lane i of each 8 reads lane 7-i), row mirror (lane i reads lane 15-i).
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141,
+              kDppMirror = 0x140;
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
 
-__global__ __launch_bounds__(kAttWaves * kWave) void decode_attention_kernel(AttnArgs p) {
-  __shared__ float qs[kAttMaxGroup][kAttMaxDim];
-  __shared__ float pw[kAttWaves][kAttMaxGroup][kWave];
-  __shared__ int64_t pslot[kAttWaves][kWave];  // cache slot of each chunk position (-1: none)
-  __shared__ float st_m[kAttWaves][kAttMaxGroup], st_l[kAttWaves][kAttMaxGroup];
-  __shared__ float st_o[kAttWaves][kAttMaxGroup][kAttMaxDim];
+// Sum over each aligned group of kLanes (8 or 16) lanes; every lane of the group ends
+// with the same value (each step adds two equal-order partial sums).
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (kLanes == 16) v += dpp_f32<kDppMirror>(v);
+  return v;
+}
 
-  const int64_t m = blockIdx.x;
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  return fmaxf(v, __shfl_xor(v, 32, kWave));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  v += __shfl_xor(v, 16, kWave);
+  return v + __shfl_xor(v, 32, kWave);
+}
+
+__device__ __forceinline__ void unpack8(const u32x4& w, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(w[i]);
+    v[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs p) {
+  constexpr int LPR = D / 8;        // lanes per cache row
+  constexpr int RG = kWave / LPR;   // rows per load instruction
+  constexpr int T = LPR;            // load instructions per chunk (T * RG == 64)
+  __shared__ int64_t pslot[kWave];  // cache offset of each chunk position (-1: none)
+  __shared__ float pw[G][RG][LPR];  // softmax weight of chunk position RG * t + g at [g][t]
+
+  const int64_t m = blockIdx.z;
   const int kvh = static_cast<int>(blockIdx.y);
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int d = p.head_dim, G = p.group;
+  const int lane = threadIdx.x;
+  const int r = lane % LPR, g = lane / LPR;
   const int32_t L = p.context_lens[m];
   if (L <= 0 || int64_t(L) > p.blocks_per_seq * p.block_size) return;
+  const int64_t begin = int64_t(blockIdx.x) * p.split_len;
+  if (begin >= L) return;
+  const int32_t end = static_cast<int32_t>(begin + p.split_len < L ? begin + p.split_len : L);
 
-  for (int e = tid; e < G * d; e += kAttWaves * kWave) {
-    const int h = e / d, i = e % d;
-    qs[h][i] = bf16_bits_to_f32(p.q[m * p.ld_q + int64_t(kvh * G + h) * d + i]);
-  }
-  __syncthreads();
-
-  float run_m[kAttMaxGroup], run_l[kAttMaxGroup], acc[kAttMaxGroup][kAttDimPerLane];
+  float qf[G][8];
 #pragma unroll
-  for (int h = 0; h < kAttMaxGroup; ++h) {
+  for (int h = 0; h < G; ++h)
+    unpack8(*reinterpret_cast<const u32x4*>(p.q + m * p.ld_q + int64_t(kvh * G + h) * D + r * 8),
+            qf[h]);
+  float run_m[G], run_l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
     run_m[h] = -INFINITY;
     run_l[h] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kAttDimPerLane; ++c) acc[h][c] = 0.0f;
+    for (int c = 0; c < 8; ++c) acc[h][c] = 0.0f;
   }
   const int32_t* bt = p.block_table + m * p.blocks_per_seq;
-  const int64_t row_stride = int64_t(p.n_kv) * d;  // one (block, offset) slot
-  for (int32_t base = wave * kWave; base < L; base += kAttWaves * kWave) {
-    // Scores: lane l takes position base + l.
-    const int32_t j = base + lane;
-    bool live = j < L;
-    int64_t slot = 0;
-    if (live) {
-      const int32_t blk = bt[j / p.block_size];
-      live = blk >= 0 && blk < p.num_blocks;
-      slot = (int64_t(blk) * p.block_size + j % p.block_size) * row_stride + int64_t(kvh) * d;
-    }
-    pslot[wave][lane] = live ? slot : -1;
-    float s[kAttMaxGroup];
-#pragma unroll
-    for (int h = 0; h < kAttMaxGroup; ++h) s[h] = 0.0f;
+  const int64_t row_stride = int64_t(p.n_kv) * D;
+
+  for (int32_t base = static_cast<int32_t>(begin); base < end; base += kWave) {
     {
-      // The key row in groups of 64 elements: eight 16-byte loads issued together, then
-      // used (a lane without a position reads row 0 and its scores are discarded).
-      const uint16_t* kr = p.k_cache + (live ? slot : 0);
-      for (int i0 = 0; i0 < d; i0 += 64) {
-        u32x4 kv[8];
+      const int32_t j = base + lane;
+      int64_t slot = -1;
+      if (j < end) {
+        const int32_t blk = bt[j / p.block_size];
+        if (blk >= 0 && blk < p.num_blocks)
+          slot = (int64_t(blk) * p.block_size + j % p.block_size) * row_stride +
+                 int64_t(kvh) * D;
+      }
+      pslot[lane] = slot;
+    }
+    __syncthreads();
+
+    // Scores.  Load instruction t reads chunk position RG * t + g; after the row sums
+    // lane (g, r) keeps the scores of position RG * r + g.  All T key loads are in
+    // flight together, and the value loads are issued as soon as the keys are used, so
+    // their latency overlaps the softmax.
+    float sel[G];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kv[u] = *reinterpret_cast<const u32x4*>(kr + i0 + 8 * u);
+    for (int h = 0; h < G; ++h) sel[h] = 0.0f;
+    bool has[T];
+    u32x4 kv[T];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float kf[8];
+    for (int t = 0; t < T; ++t) {
+      const int64_t sl = pslot[RG * t + g];
+      has[t] = sl >= 0;
+      kv[t] = *reinterpret_cast<const u32x4*>(p.k_cache + (has[t] ? sl : 0) + r * 8);
+    }
+    u32x4 vv[T];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            kf[2 * c] = bf16_lo(kv[u][c]);
-            kf[2 * c + 1] = bf16_hi(kv[u][c]);
-          }
+    for (int t = 0; t < T; ++t) {
+      float kf[8];
+      unpack8(kv[t], kf);
+      // the value row of the same position reuses this lane's address
+      const int64_t sl = pslot[RG * t + g];
+      vv[t] = *reinterpret_cast<const u32x4*>(p.v_cache + (has[t] ? sl : 0) + r * 8);
 #pragma unroll
-          for (int h = 0; h < kAttMaxGroup; ++h)
-            if (h < G)
+      for (int h = 0; h < G; ++h) {
+        float s = 0.0f;
 #pragma unroll
-              for (int c = 0; c < 8; ++c) s[h] = fmaf(qs[h][i0 + 8 * u + c], kf[c], s[h]);
-        }
+        for (int c = 0; c < 8; ++c) s = fmaf(qf[h][c], kf[c], s);
+        s = group_sum<LPR>(s);
+        sel[h] = (r == t) ? s : sel[h];
       }
     }
+    const bool live = pslot[RG * r + g] >= 0;
+
     // Online softmax per head.
-    float scale_old[kAttMaxGroup];
 #pragma unroll
-    for (int h = 0; h < kAttMaxGroup; ++h) {
-      if (h >= G) break;
-      const float sh = live ? s[h] * p.scale : -INFINITY;
-      const float cmax = wave_max_f32(sh);
-      const float nm = fmaxf(run_m[h], cmax);
+    for (int h = 0; h < G; ++h) {
+      const float sh = live ? sel[h] * p.scale : -INFINITY;
+      const float nm = fmaxf(run_m[h], wave_max(sh));
       const float w = live ? __expf(sh - nm) : 0.0f;
-      pw[wave][h][lane] = w;
-      scale_old[h] = (run_m[h] == -INFINITY) ? 0.0f : __expf(run_m[h] - nm);
-      run_l[h] = run_l[h] * scale_old[h] + wave_sum_f32(w);
+      pw[h][g][r] = w;
+      const float f = (run_m[h] == -INFINITY) ? 0.0f : __expf(run_m[h] - nm);
+      run_l[h] = run_l[h] * f + wave_sum(w);
       run_m[h] = nm;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] *= f;
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's weights are in LDS
-    __builtin_amdgcn_wave_barrier();
-    // Values: lane owns dims lane, lane + 64, ...
+    __syncthreads();
+
+    // Values: a position without a slot contributes nothing (its row is not used,
+    // whatever row 0 of the cache holds).
 #pragma unroll
-    for (int h = 0; h < kAttMaxGroup; ++h) {
-      if (h >= G) break;
+    for (int t = 0; t < T; ++t) {
+      if (!has[t]) continue;
+      float vf[8];
+      unpack8(vv[t], vf);
 #pragma unroll
-      for (int c = 0; c < kAttDimPerLane; ++c) acc[h][c] *= scale_old[h];
-    }
-    // Eight positions per step: their slots come from LDS, all their value loads are
-    // issued before any is used (a position without a slot reads row 0 of the cache and
-    // has weight 0).
-    const int32_t nj = (L - base) < kWave ? (L - base) : kWave;
-    for (int32_t jj = 0; jj < nj; jj += 8) {
-      float vf[8][kAttDimPerLane];
+      for (int h = 0; h < G; ++h) {
+        const float w = pw[h][g][t];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t sl = (jj + u < nj) ? pslot[wave][jj + u] : -1;
-        const uint16_t* vr = p.v_cache + (sl >= 0 ? sl : 0);
-#pragma unroll
-        for (int c = 0; c < kAttDimPerLane; ++c) {
-          const int i = lane + c * kWave;
-          vf[u][c] = i < d ? bf16_bits_to_f32(vr[i]) : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (jj + u >= nj) break;
-#pragma unroll
-        for (int h = 0; h < kAttMaxGroup; ++h) {
-          if (h >= G) break;
-          const float w = pw[wave][h][jj + u];
-#pragma unroll
-          for (int c = 0; c < kAttDimPerLane; ++c) acc[h][c] = fmaf(w, vf[u][c], acc[h][c]);
-        }
+        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(w, vf[c], acc[h][c]);
       }
     }
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
   }
-  // Combine the waves.
+
+  // Sum the row groups (lanes with the same r hold the same output dimensions).
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] += __shfl_xor(acc[h][c], o, kWave);
+
+  if (p.n_split == 1) {
+    if (g != 0) return;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = run_l[h] > 0.0f ? acc[h][2 * i] / run_l[h] : 0.0f;
+        const float b = run_l[h] > 0.0f ? acc[h][2 * i + 1] / run_l[h] : 0.0f;
+        o[i] = uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
+      }
+      *reinterpret_cast<u32x4*>(p.out + m * p.ld_q + int64_t(kvh * G + h) * D + r * 8) = o;
+    }
+    return;
+  }
+#pragma unroll
   for (int h = 0; h < G; ++h) {
+    const int64_t idx = (m * p.n_q + kvh * G + h) * p.n_split + blockIdx.x;
+    if (g == 0) {
+      float* o = p.ws_o + idx * D + r * 8;
+      *reinterpret_cast<f32x4*>(o) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+    }
     if (lane == 0) {
-      st_m[wave][h] = run_m[h];
-      st_l[wave][h] = run_l[h];
-    }
-#pragma unroll
-    for (int c = 0; c < kAttDimPerLane; ++c) {
-      const int i = lane + c * kWave;
-      if (i < d) st_o[wave][h][i] = acc[h][c];
+      p.ws_ml[2 * idx] = run_m[h];
+      p.ws_ml[2 * idx + 1] = run_l[h];
     }
   }
-  __syncthreads();
-  for (int e = tid; e < G * d; e += kAttWaves * kWave) {
-    const int h = e / d, i = e % d;
-    float mx = -INFINITY;
+}
+
+// Merge the splits of one (row, Q head): o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+// Lane s of each group of 64 splits forms that split's factor and the factors go through
+// LDS; each lane sums its output dimensions over the splits with 32 splits' loads in
+// flight, the first 32 requested before the maxima are known.
+template <int D>
+__global__ __launch_bounds__(kWave) void attn_combine_kernel(AttnArgs p) {
+  constexpr int DPL = D / kWave;  // output dimensions per lane
+  constexpr int kB = 32;          // splits per batch of loads
+  __shared__ float fs[kWave];
+  const int64_t m = blockIdx.y;
+  const int hq = static_cast<int>(blockIdx.x);
+  const int lane = threadIdx.x;
+  const int32_t L = p.context_lens[m];
+  if (L <= 0 || int64_t(L) > p.blocks_per_seq * p.block_size) return;
+  const int64_t ns = (int64_t(L) + p.split_len - 1) / p.split_len;
+  const int64_t idx0 = (m * p.n_q + hq) * p.n_split;
+  const float* ml = p.ws_ml + 2 * idx0;
+  const float* po = p.ws_o + idx0 * D + lane;
+  float v[kB][DPL];
 #pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) mx = fmaxf(mx, st_m[w][h]);
-    float o = 0.0f, l = 0.0f;
+  for (int u = 0; u < kB; ++u)
 #pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) {
-      if (st_m[w][h] == -INFINITY) continue;
-      const float f = __expf(st_m[w][h] - mx);
-      o = fmaf(st_o[w][h][i], f, o);
-      l = fmaf(st_l[w][h], f, l);
+    for (int c = 0; c < DPL; ++c) v[u][c] = (u < ns) ? po[int64_t(u) * D + c * kWave] : 0.0f;
+  float mx = -INFINITY;
+  for (int64_t s = lane; s < ns; s += kWave) mx = fmaxf(mx, ml[2 * s]);
+  mx = wave_max(mx);
+  float l = 0.0f, o[DPL];
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) o[c] = 0.0f;
+  for (int64_t s0 = 0; s0 < ns; s0 += kWave) {
+    float f = 0.0f;
+    if (s0 + lane < ns) {
+      const float ms = ml[2 * (s0 + lane)];
+      if (ms != -INFINITY) {
+        f = __expf(ms - mx);
+        l = fmaf(ml[2 * (s0 + lane) + 1], f, l);
+      }
     }
-    p.out[m * p.ld_q + int64_t(kvh * G + h) * d + i] = f32_to_bf16_rne(l > 0.0f ? o / l : 0.0f);
+    fs[lane] = f;
+    __syncthreads();
+    const int nb = static_cast<int>(ns - s0 < kWave ? ns - s0 : kWave);
+    for (int u0 = 0; u0 < nb; u0 += kB) {
+      if (s0 + u0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+#pragma unroll
+          for (int c = 0; c < DPL; ++c)
+            v[u][c] = (u0 + u < nb) ? po[(s0 + u0 + u) * D + c * kWave] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+#pragma unroll
+        for (int c = 0; c < DPL; ++c) o[c] = fmaf(fs[(u0 + u) & (kWave - 1)], v[u][c], o[c]);
+    }
+    __syncthreads();
   }
+  l = wave_sum(l);
+#pragma unroll
+  for (int c = 0; c < DPL; ++c)
+    p.out[m * p.ld_q + int64_t(hq) * D + lane + c * kWave] =
+        f32_to_bf16_rne(l > 0.0f ? o[c] / l : 0.0f);
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.n_split), static_cast<unsigned>(a.n_kv),
+                  static_cast<unsigned>(a.M));
+  switch (a.group) {
+#define A8W8_ATTN_CASE(GG) \
+  case GG: hipLaunchKernelGGL((attn_split_kernel<D, GG>), grid, dim3(kWave), 0, stream, a); break;
+    A8W8_ATTN_CASE(1) A8W8_ATTN_CASE(2) A8W8_ATTN_CASE(3) A8W8_ATTN_CASE(4)
+    A8W8_ATTN_CASE(5) A8W8_ATTN_CASE(6) A8W8_ATTN_CASE(7) A8W8_ATTN_CASE(8)
+#undef A8W8_ATTN_CASE
+    default: return hipErrorInvalidValue;
+  }
+  if (a.n_split > 1)
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(static_cast<unsigned>(a.n_q),
+                                                      static_cast<unsigned>(a.M)),
+                       dim3(kWave), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_attention(const AttnArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_attention_kernel, dim3(static_cast<unsigned>(a.M),
-                                                   static_cast<unsigned>(a.n_kv)),
-                     dim3(kAttWaves * kWave), 0, stream, a);
-  return hipGetLastError();
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace a8w8
