@@ -183,6 +183,26 @@ def cpu_baseline(cfg, seconds: float):
             "us_per_layer": round(t_total / done * 1e6, 1)}
 
 
+def oracle_per_call(run, seconds: float, sample: str):
+    """The oracle as it stands, called on the host until about `seconds` have passed (at
+    least once) on the benchmarked workload's own inputs: microseconds per call."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        cores = os.cpu_count() or 1
+    n, t = 0, 0.0
+    while n == 0 or t < seconds:
+        t0 = time.perf_counter()
+        with np.errstate(all="ignore"):  # random bit patterns include BF16 NaN and Inf
+            run()
+        t += time.perf_counter() - t0
+        n += 1
+    return {"value": round(t / n * 1e6, 1), "unit": "us per call", "cores": int(cores),
+            "kind": "oracle", "sample": f"{n} oracle calls on {sample} (inputs prepared "
+                                        f"beforehand), {t:.1f} s"}
+
+
 def bench_prefill(args, cfg, torch, B) -> None:
     """Secondary line: the W8A16 prefill MLP block (RMSNorm, Gate/Up, SiLU, Down + residual)
     at M = 256; value in TFLOP/s of the three GEMMs, roofline of the Gate/Up GEMM (with
@@ -247,6 +267,12 @@ def bench_prefill(args, cfg, torch, B) -> None:
                      "kernel_us": round(k_ms * 1e3, 2), "algorithmic_flops_per_launch": gu_flops},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        out_line["cpu_baseline"] = oracle_per_call(
+            lambda: O.prefill_mlp(d["x"], d["gamma_post"], cfg.eps, d["w_gate"], d["s_gate"],
+                                  d["w_up"], d["s_up"], d["w_down"], d["s_down"], d["res"]),
+            args.cpu_seconds, f"the same M={M} prefill MLP block")
     print(json.dumps(out_line))
 
 
@@ -289,6 +315,16 @@ def bench_prefill_layer(args, torch, B) -> None:
     ms = (time.perf_counter() - t0) / args.steps * 1e3
     flops = 2.0 * M * (n_qkv * H + H * H + 3 * H * I)
     tf = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        cpu = oracle_per_call(
+            lambda: O.layer_linears_prefill(d["x"], d["gamma_in"], d["gamma_post"], cfg.eps,
+                                            d["w_qkv"], d["s_qkv"], d["w_o"], d["s_o"],
+                                            d["w_gate"], d["s_gate"], d["w_up"], d["s_up"],
+                                            d["w_down"], d["s_down"], cfg.n_q_heads,
+                                            cfg.head_dim),
+            args.cpu_seconds, f"the same M={M} prefill layer")
     print(json.dumps({
         "metric": "W8A16 prefill layer TFLOP/s (QKV, O, Gate/Up, Down GEMMs), BF16 matrix cores",
         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -301,7 +337,7 @@ def bench_prefill_layer(args, torch, B) -> None:
                      "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "whole call (norm, QKV, slice copy, O, MLP kernels)",
                      "algorithmic_flops_per_launch": flops},
-        "cpu_baseline": None}))
+        "cpu_baseline": cpu}))
 
 
 def bench_qk_rope(args, torch, B) -> None:
@@ -313,10 +349,11 @@ def bench_qk_rope(args, torch, B) -> None:
     nq, nkv, d, bs, bps = 40, 8, 128, 16, 64
     cos, sin = synth.rope_tables(bs * bps, d)
     rows = []
+    cpu = None
     for M in (1, 16):
         rng = np.random.default_rng(M)
-        qkv = torch.from_numpy(rng.integers(0, 1 << 15, size=(M, (nq + 2 * nkv) * d),
-                                            dtype=np.int16)).to("cuda")
+        qkv_h = rng.integers(0, 1 << 15, size=(M, (nq + 2 * nkv) * d), dtype=np.int16)
+        qkv = torch.from_numpy(qkv_h).to("cuda")
         g = torch.full((d,), 0x3F80, dtype=torch.int16, device="cuda")   # BF16 1.0
         pos = torch.from_numpy(rng.integers(0, bs * bps, size=M).astype(np.int32)).to("cuda")
         bt = torch.from_numpy(np.arange(M * bps, dtype=np.int32).reshape(M, bps)).to("cuda")
@@ -346,6 +383,15 @@ def bench_qk_rope(args, torch, B) -> None:
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / (reps * 20) * 1e3
         nbytes = M * ((nq + 2 * nkv) * d * 2 + nq * d * 2 + 2 * nkv * d * 2 + 4 + 4 + d * 4) + 2 * d * 2
+        if M == 16 and not args.no_cpu_baseline:
+            import oracle as O
+            g_h = np.full(d, 0x3F80, np.uint16)
+            pos_h, bt_h = pos.cpu().numpy(), bt.cpu().numpy()
+            kc_h = np.zeros((M * bps, bs, nkv, d), np.uint16)
+            cpu = oracle_per_call(
+                lambda: O.qk_norm_rope_kv(qkv_h.view(np.uint16), nq, nkv, d, g_h, g_h, 1e-6,
+                                          cos, sin, pos_h, bt_h, kc_h, kc_h.copy()),
+                min(args.cpu_seconds, 5.0), "the same M=16 inputs")
         rows.append({"M": M, "us_per_call": round(us, 2), "bytes_per_call": nbytes,
                      "gb_s": round(nbytes / (us * 1e-6) / 1e9, 2)})
     r16 = rows[-1]
@@ -361,7 +407,7 @@ def bench_qk_rope(args, torch, B) -> None:
                      "frac": round(r16["gb_s"] / HBM_PEAK_GBS, 6), "traffic": None,
                      "kernel": "qk_rope_kernel (latency-bound: a few KB per call)",
                      "algorithmic_bytes_per_launch": r16["bytes_per_call"]},
-        "cpu_baseline": None}))
+        "cpu_baseline": cpu}))
 
 
 def bench_attention(args, torch, B) -> None:
@@ -374,15 +420,16 @@ def bench_attention(args, torch, B) -> None:
     L = args.context
     bps = (L + bs - 1) // bs
     rows = []
+    cpu = None
     for M in (1, 16):
         rng = np.random.default_rng(M)
         nblocks = M * bps
-        q = torch.from_numpy(rng.integers(0x3C00, 0x3F80, size=(M, nq * d), dtype=np.int16)).to("cuda")
-        kc = torch.from_numpy(rng.integers(0x3C00, 0x3F80, size=(nblocks, bs, nkv, d),
-                                           dtype=np.int16)).to("cuda")
-        vc = torch.from_numpy(rng.integers(0x3C00, 0x3F80, size=(nblocks, bs, nkv, d),
-                                           dtype=np.int16)).to("cuda")
-        bt = torch.from_numpy(rng.permutation(nblocks).astype(np.int32).reshape(M, bps)).to("cuda")
+        q_h = rng.integers(0x3C00, 0x3F80, size=(M, nq * d), dtype=np.int16)
+        kc_h = rng.integers(0x3C00, 0x3F80, size=(nblocks, bs, nkv, d), dtype=np.int16)
+        vc_h = rng.integers(0x3C00, 0x3F80, size=(nblocks, bs, nkv, d), dtype=np.int16)
+        bt_h = rng.permutation(nblocks).astype(np.int32).reshape(M, bps)
+        q, kc, vc = (torch.from_numpy(a).to("cuda") for a in (q_h, kc_h, vc_h))
+        bt = torch.from_numpy(bt_h).to("cuda")
         lens = torch.full((M,), L, dtype=torch.int32, device="cuda")
         out = torch.empty_like(q)
         nws = B.a8w8_decode_attention_workspace_bytes(M, nq, nkv, d, bps * bs)
@@ -409,6 +456,13 @@ def bench_attention(args, torch, B) -> None:
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / (reps * 10) * 1e3
         nbytes = M * (L * nkv * d * 2 * 2 + 2 * nq * d * 2)
+        if M == 16 and not args.no_cpu_baseline:
+            import oracle as O
+            cpu = oracle_per_call(
+                lambda: O.decode_attention(q_h.view(np.uint16), nq, nkv, d, kc_h.view(np.uint16),
+                                           vc_h.view(np.uint16), bt_h, np.full(M, L, np.int32),
+                                           1.0 / math.sqrt(d)),
+                min(args.cpu_seconds, 10.0), f"the same M=16 inputs at context {L}")
         rows.append({"M": M, "context": L, "workspace_bytes": nws,
                      "us_per_call": round(us, 2), "bytes_per_call": nbytes,
                      "gb_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
@@ -425,7 +479,7 @@ def bench_attention(args, torch, B) -> None:
                      "frac": round(r16["gb_s"] / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "attn_split_kernel + attn_combine_kernel (one call)",
                      "algorithmic_bytes_per_launch": r16["bytes_per_call"]},
-        "cpu_baseline": None}))
+        "cpu_baseline": cpu}))
 
 
 def main():

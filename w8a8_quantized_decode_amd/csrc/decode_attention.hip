@@ -81,17 +81,25 @@ __global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs p) {
   const int kvh = static_cast<int>(blockIdx.y);
   const int lane = threadIdx.x;
   const int r = lane % LPR, g = lane / LPR;
+  // The context length, the query and the block number of this lane's first position
+  // are requested together (the table entry exists whenever the position is below
+  // blocks_per_seq * block_size, which the host keeps below 2^30).
+  const int32_t bs = static_cast<int32_t>(p.block_size);
+  const int32_t max_ctx = static_cast<int32_t>(p.blocks_per_seq * p.block_size);
+  const int32_t* bt = p.block_table + m * p.blocks_per_seq;
+  const int32_t begin = static_cast<int32_t>(int64_t(blockIdx.x) * p.split_len);
   const int32_t L = p.context_lens[m];
-  if (L <= 0 || int64_t(L) > p.blocks_per_seq * p.block_size) return;
-  const int64_t begin = int64_t(blockIdx.x) * p.split_len;
-  if (begin >= L) return;
+  int32_t blk_next = (begin + lane < max_ctx) ? bt[(begin + lane) / bs] : -1;
+  u32x4 qraw[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qraw[h] = *reinterpret_cast<const u32x4*>(p.q + m * p.ld_q + int64_t(kvh * G + h) * D + r * 8);
+  if (L <= 0 || L > max_ctx || begin >= L) return;
   const int32_t end = static_cast<int32_t>(begin + p.split_len < L ? begin + p.split_len : L);
 
   float qf[G][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-    unpack8(*reinterpret_cast<const u32x4*>(p.q + m * p.ld_q + int64_t(kvh * G + h) * D + r * 8),
-            qf[h]);
+  for (int h = 0; h < G; ++h) unpack8(qraw[h], qf[h]);
   float run_m[G], run_l[G], acc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -100,20 +108,19 @@ __global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.0f;
   }
-  const int32_t* bt = p.block_table + m * p.blocks_per_seq;
   const int64_t row_stride = int64_t(p.n_kv) * D;
 
-  for (int32_t base = static_cast<int32_t>(begin); base < end; base += kWave) {
+  for (int32_t base = begin; base < end; base += kWave) {
     {
       const int32_t j = base + lane;
+      const int32_t blk = blk_next;
       int64_t slot = -1;
-      if (j < end) {
-        const int32_t blk = bt[j / p.block_size];
-        if (blk >= 0 && blk < p.num_blocks)
-          slot = (int64_t(blk) * p.block_size + j % p.block_size) * row_stride +
-                 int64_t(kvh) * D;
-      }
+      if (j < end && blk >= 0 && blk < p.num_blocks)
+        slot = (int64_t(blk) * bs + j % bs) * row_stride + int64_t(kvh) * D;
       pslot[lane] = slot;
+      // the next chunk's block number is requested before this chunk's rows
+      const int32_t jn = j + kWave;
+      blk_next = (base + kWave < end && jn < end) ? bt[jn / bs] : -1;
     }
     __syncthreads();
 
