@@ -7,6 +7,7 @@ may import this package.  The product path never routes through it.
 from .a8w8_oracle import (  # noqa: F401
     bf16_to_f32,
     decode_attention,
+    decode_layer,
     dequant,
     dequant_weight_bf16,
     down_split,
@@ -16,6 +17,7 @@ from .a8w8_oracle import (  # noqa: F401
     layer_linears_prefill,
     linear_decode,
     mlp_block_decode,
+    o_projection,
     prefill_linear,
     prefill_mlp,
     qk_norm_rope_kv,

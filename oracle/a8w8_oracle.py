@@ -507,3 +507,38 @@ def decode_attention(q_bits, n_q_heads: int, n_kv_heads: int, head_dim: int, k_c
             o = (w / w.sum()) @ v
             out[m, h * d : (h + 1) * d] = rne_bf16(o.astype(np.float32))
     return out
+
+
+# ------------------------------------------------------------ decode layer, real attention
+
+def o_projection(attn_bits, x_bits, w_o, s_o) -> np.ndarray:
+    """O on the attention output with the layer input as residual, as in
+    ``layer_linears_decode``: the attention rows are quantized once per row, multiplied
+    in INT32 and dequantized, and ``h1 = rne_bf16(fl32(y_o + f(x)))``."""
+    q_a, s_a = quantize_rows(bf16_to_f32(np.asarray(attn_bits, dtype=np.uint16)))
+    acc_o = int_gemm(q_a, w_o)
+    return rne_bf16(dequant(acc_o, s_a, s_o) + bf16_to_f32(np.asarray(x_bits, dtype=np.uint16)))
+
+
+def decode_layer(x_bits, gamma_in_bits, gamma_post_bits, eps, w_qkv, s_qkv, w_o, s_o, w_g,
+                 s_g, w_u, s_u, w_d, s_d, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                 split_k, q_gamma_bits, k_gamma_bits, qk_eps, cos_table, sin_table,
+                 positions, context_lens, block_table, k_cache_bits, v_cache_bits, scale):
+    """One decode layer with real attention, in the layer order the pages give ([PR810]
+    walkthrough: QKV, QK-norm/RoPE, the BF16 KV cache and attention, O, the post-attention
+    norm and the MLP): QKV as in ``layer_linears_decode``; ``qk_norm_rope_kv`` writes the
+    new token's K and V to the cache and rotates Q; ``decode_attention`` over the updated
+    cache; ``o_projection`` (+ x) gives h1; ``mlp_block_decode`` on h1.  Returns the
+    output and the stages (qkv, q_rot, the two caches, attn, h1)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    q_in, s_in = quantize_rows(rmsnorm(x_bits, gamma_in_bits, eps))
+    qkv = rne_bf16(dequant(int_gemm(q_in, w_qkv), s_in, s_qkv))
+    q_rot, kc, vc = qk_norm_rope_kv(qkv, n_q_heads, n_kv_heads, head_dim, q_gamma_bits,
+                                    k_gamma_bits, qk_eps, cos_table, sin_table, positions,
+                                    block_table, k_cache_bits, v_cache_bits)
+    attn = decode_attention(q_rot, n_q_heads, n_kv_heads, head_dim, kc, vc, block_table,
+                            context_lens, scale)
+    h1 = o_projection(attn, x_bits, w_o, s_o)
+    out, _ = mlp_block_decode(h1, gamma_post_bits, eps, w_g, s_g, w_u, s_u, w_d, s_d, h1,
+                              split_k)
+    return out, dict(qkv=qkv, q_rot=q_rot, k_cache=kc, v_cache=vc, attn=attn, h1=h1)

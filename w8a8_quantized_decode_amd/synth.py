@@ -24,6 +24,7 @@ TENSOR_IDS = {
     "w_gate": 3, "s_gate": 4, "w_up": 5, "s_up": 6, "w_down": 7, "s_down": 8,
     "res": 9, "gamma_in": 10,
     "w_qkv": 11, "s_qkv": 12, "w_o": 13, "s_o": 14,
+    "q_gamma": 15, "k_gamma": 16, "k_cache": 17, "v_cache": 18, "block_table": 19,
 }
 
 
@@ -127,3 +128,30 @@ def rope_tables(max_pos: int, head_dim: int, base: float = 1_000_000.0):
     inv = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
     ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def attention_inputs(cfg: Config, contexts, block_size: int = 16, layer: int = 0):
+    """Seeded inputs of the attention step of one decode layer: row m holds its new token
+    at position contexts[m] - 1 and attends to contexts[m] positions.  QK-norm gains in
+    [0.5, 1.5); K and V caches of standard-normal BF16 values (the earlier positions'
+    entries; the step writes the new token's); a block table of disjoint random blocks per
+    row with room for the longest context; Qwen3 RoPE tables; scale 1/sqrt(head_dim)."""
+    c, d = cfg.index, cfg.head_dim
+    contexts = np.asarray(contexts, dtype=np.int32)
+    M = contexts.size
+    bps = int(-(-int(contexts.max()) // block_size))
+    nblocks = M * bps + 2
+    cos, sin = rope_tables(bps * block_size, d)
+    perm = _rng(seed_for(c, layer, "block_table")).permutation(nblocks)[: M * bps]
+    return {
+        "q_gamma": uniform_bf16(seed_for(c, layer, "q_gamma"), (d,), 0.5, 1.5),
+        "k_gamma": uniform_bf16(seed_for(c, layer, "k_gamma"), (d,), 0.5, 1.5),
+        "cos": cos, "sin": sin,
+        "positions": contexts - 1, "context_lens": contexts,
+        "block_table": perm.reshape(M, bps).astype(np.int32),
+        "k_cache": normal_bf16(seed_for(c, layer, "k_cache"),
+                               (nblocks, block_size, cfg.n_kv_heads, d)),
+        "v_cache": normal_bf16(seed_for(c, layer, "v_cache"),
+                               (nblocks, block_size, cfg.n_kv_heads, d)),
+        "scale": float(1.0 / np.sqrt(d)),
+    }
