@@ -353,6 +353,60 @@ a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_hea
                                   float scale, uint16_t* out_bf16, void* workspace,
                                   size_t ws_bytes, void* stream);
 
+/*
+ * Inputs and buffers of the attention step inside a8w8_decode_layer: the arguments of
+ * a8w8_qk_norm_rope_kv and a8w8_decode_attention that the layer does not already hold.
+ *   q_gamma_bf16, k_gamma_bf16 [d]; qk_eps; cos_table, sin_table [max_pos, d/2] FP32;
+ *   positions [M] (the new token's position), context_lens [M] (positions attended,
+ *   normally positions + 1); block_table [M, blocks_per_seq]; k_cache, v_cache
+ *   [num_blocks, block_size, n_kv, d] BF16 (the step writes the new token's K and V);
+ *   scale; q_rot_bf16 [M, n_q * d] and attn_bf16 [M, n_q * d] caller buffers that
+ *   receive the rotated Q and the attention output (O's input); attn_workspace /
+ *   attn_ws_bytes as the workspace of a8w8_decode_attention (may be NULL).
+ */
+typedef struct a8w8_attention_step {
+  const uint16_t* q_gamma_bf16;
+  const uint16_t* k_gamma_bf16;
+  float qk_eps;
+  const float* cos_table;
+  const float* sin_table;
+  int64_t max_pos;
+  const int32_t* positions;
+  const int32_t* context_lens;
+  const int32_t* block_table;
+  int64_t blocks_per_seq;
+  uint16_t* k_cache_bf16;
+  uint16_t* v_cache_bf16;
+  int64_t num_blocks;
+  int64_t block_size;
+  float scale;
+  uint16_t* q_rot_bf16;
+  uint16_t* attn_bf16;
+  void* attn_workspace;
+  size_t attn_ws_bytes;
+} a8w8_attention_step;
+
+/*
+ * One decode layer with real attention: QKV (as in a8w8_layer_linears), QK-norm + RoPE +
+ * KV-cache write (a8w8_qk_norm_rope_kv), decode attention over the paged cache
+ * (a8w8_decode_attention), then O on the attention output with the layer input as
+ * residual -> h1, then the MLP block (PR #810 walkthrough: the layer's order QKV ->
+ * QK-norm/RoPE -> BF16 KV cache and attention -> O -> post-attention norm -> MLP).
+ * Arguments as in a8w8_layer_linears (workspace sized by a8w8_workspace_bytes with
+ * A8W8_OP_LAYER_LINEARS) and a8w8_attention_step; attn must not be NULL and its shapes
+ * follow the two steps' rules (d in {64, 128}, n_q / n_kv <= 8).  qkv_out_bf16 [M, n_qkv]
+ * and h1_out_bf16 [M, H] are optional outputs (NULL: kept in the workspace).  Every
+ * argument is checked before anything is enqueued.
+ */
+a8w8_status a8w8_decode_layer(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                              const uint16_t* gamma_post_bf16, float eps, a8w8_qweight qkv,
+                              a8w8_qweight o, a8w8_qweight gate, a8w8_qweight up,
+                              a8w8_qweight down, int64_t M, int64_t H, int64_t I,
+                              int n_q_heads, int n_kv_heads, int head_dim, int split_k,
+                              const a8w8_attention_step* attn, uint16_t* qkv_out_bf16,
+                              uint16_t* h1_out_bf16, uint16_t* out_bf16, void* workspace,
+                              size_t ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* a8w8_status_string(a8w8_status status);
 

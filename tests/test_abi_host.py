@@ -39,6 +39,7 @@ def test_every_declared_symbol_is_exported(L):
     assert {"a8w8_quantize_rows", "a8w8_linear", "a8w8_mlp_block", "a8w8_layer_linears",
             "a8w8_layer_linears_prefill", "a8w8_qk_norm_rope_kv",
             "a8w8_decode_attention", "a8w8_decode_attention_workspace_bytes",
+            "a8w8_decode_layer",
             "a8w8_workspace_bytes", "a8w8_status_string", "a8w8_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -206,3 +207,26 @@ def test_attention_workspace_bytes(L):
     assert ws(1, 41, 8, 128, 4096) == 0          # invalid shapes
     assert ws(1, 40, 8, 96, 4096) == 0
     assert ws(1, 40, 8, 128, 0) == 0
+
+
+def test_decode_layer_validation(L):
+    """The attention step's arguments are checked with the layer's, before any launch: a
+    missing step, a bad block size (QK step) and a context range the attention step
+    rejects all return their status with nothing enqueued."""
+    need = B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 1, 256, 768, 512, 2)
+
+    def call(step=True, bs=16, bps=4, rot=FAKE):
+        a = B.AttentionStep()
+        for f in ("q_gamma", "k_gamma", "cos_table", "sin_table", "positions", "context_lens",
+                  "block_table", "k_cache", "v_cache", "attn"):
+            setattr(a, f, FAKE)
+        a.q_rot = rot
+        a.qk_eps, a.max_pos, a.blocks_per_seq, a.num_blocks = 1e-6, 64, bps, 8
+        a.block_size, a.scale = bs, 0.088
+        return L.a8w8_decode_layer(FAKE, FAKE, FAKE, 1e-6, QW, QW, QW, QW, QW, 1, 256, 768, 2, 1,
+                                   128, 2, ctypes.byref(a) if step else None, None, None, FAKE,
+                                   FAKE, need, None)
+    assert call(step=False) == 1
+    assert call(bs=0) == 2
+    assert call(rot=None) == 1
+    assert call(bps=(1 << 26) + 1) == 2      # context range above 2^30: attention's check

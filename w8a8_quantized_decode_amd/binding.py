@@ -51,6 +51,16 @@ class MlpTaps(ctypes.Structure):
                [("ev_kernel", ctypes.c_int)]
 
 
+class AttentionStep(ctypes.Structure):
+    _fields_ = [("q_gamma", _vp), ("k_gamma", _vp), ("qk_eps", ctypes.c_float),
+                ("cos_table", _vp), ("sin_table", _vp), ("max_pos", ctypes.c_int64),
+                ("positions", _vp), ("context_lens", _vp), ("block_table", _vp),
+                ("blocks_per_seq", ctypes.c_int64), ("k_cache", _vp), ("v_cache", _vp),
+                ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int64),
+                ("scale", ctypes.c_float), ("q_rot", _vp), ("attn", _vp),
+                ("attn_workspace", _vp), ("attn_ws_bytes", ctypes.c_size_t)]
+
+
 class LayerTaps(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("xn_in", "q_in", "s_in", "acc_qkv", "qkv", "q_attn",
                                    "s_attn", "acc_o", "h1")] + [("mlp", MlpTaps)]
@@ -106,6 +116,12 @@ def lib() -> ctypes.CDLL:
         L.a8w8_decode_attention.argtypes = [_vp, _c_i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _vp,
                                             ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
+        L.a8w8_decode_layer.restype = ctypes.c_int
+        L.a8w8_decode_layer.argtypes = [_vp, _vp, _vp, ctypes.c_float, QWeight, QWeight, QWeight,
+                                        QWeight, QWeight, _c_i64, _c_i64, _c_i64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(AttentionStep), _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
         L.a8w8_decode_attention_workspace_bytes.restype = ctypes.c_size_t
         L.a8w8_decode_attention_workspace_bytes.argtypes = [_c_i64, ctypes.c_int, ctypes.c_int,
                                                             ctypes.c_int, _c_i64]
@@ -232,6 +248,34 @@ def a8w8_layer_linears(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out
                                   _ptr(workspace), workspace.numel(),
                                   ctypes.byref(t) if t is not None else None, _stream(stream))
     _check(st, "a8w8_layer_linears")
+
+
+def a8w8_decode_layer(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out, workspace,
+                      n_q_heads: int, n_kv_heads: int, head_dim: int, *, q_gamma, k_gamma,
+                      qk_eps: float, cos_table, sin_table, positions, context_lens, block_table,
+                      k_cache, v_cache, scale: float, q_rot, attn, attn_workspace=None,
+                      split_k: int = 2, qkv_out=None, h1_out=None, stream=None) -> None:
+    """One decode layer with real attention; the attention-step tensors follow
+    a8w8_qk_norm_rope_kv and a8w8_decode_attention (q_rot and attn receive the rotated
+    Q and the attention output)."""
+    M, H = x.shape
+    I = gate[1].shape[0]
+    a = AttentionStep()
+    a.q_gamma, a.k_gamma, a.qk_eps = _ptr(q_gamma), _ptr(k_gamma), float(qk_eps)
+    a.cos_table, a.sin_table, a.max_pos = _ptr(cos_table), _ptr(sin_table), cos_table.shape[0]
+    a.positions, a.context_lens = _ptr(positions), _ptr(context_lens)
+    a.block_table, a.blocks_per_seq = _ptr(block_table), block_table.shape[1]
+    a.k_cache, a.v_cache = _ptr(k_cache), _ptr(v_cache)
+    a.num_blocks, a.block_size = k_cache.shape[0], k_cache.shape[1]
+    a.scale, a.q_rot, a.attn = float(scale), _ptr(q_rot), _ptr(attn)
+    a.attn_workspace = _ptr(attn_workspace) if attn_workspace is not None else None
+    a.attn_ws_bytes = attn_workspace.numel() if attn_workspace is not None else 0
+    st = lib().a8w8_decode_layer(_ptr(x), _ptr(gamma_in), _ptr(gamma_post), float(eps), _qw(qkv),
+                                 _qw(o), _qw(gate), _qw(up), _qw(down), M, H, I, int(n_q_heads),
+                                 int(n_kv_heads), int(head_dim), int(split_k), ctypes.byref(a),
+                                 _ptr(qkv_out), _ptr(h1_out), _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    _check(st, "a8w8_decode_layer")
 
 
 def a8w8_layer_linears_prefill(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out,

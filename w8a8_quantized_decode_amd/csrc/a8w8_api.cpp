@@ -547,14 +547,24 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
                         I, split_k, pl, b, 0, taps, tm, st);
 }
 
-a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
-                               const uint16_t* gamma_post_bf16, float eps,
-                               a8w8_qweight qkv, a8w8_qweight o, a8w8_qweight gate,
-                               a8w8_qweight up, a8w8_qweight down, int64_t M, int64_t H,
-                               int64_t I, int n_q_heads, int n_kv_heads, int head_dim,
-                               int split_k, uint16_t* qkv_out_bf16, uint16_t* out_bf16,
-                               void* workspace, size_t ws_bytes,
-                               const a8w8_layer_taps* taps, void* stream) {
+static a8w8_status make_qk_args(const uint16_t*, int64_t, int, int, int, const uint16_t*,
+                                const uint16_t*, float, const float*, const float*, int64_t,
+                                const int32_t*, const int32_t*, int64_t, uint16_t*, uint16_t*,
+                                int64_t, int64_t, uint16_t*, QkRopeArgs&);
+static a8w8_status make_attn_args(const uint16_t*, int64_t, int, int, int, const uint16_t*,
+                                  const uint16_t*, int64_t, int64_t, const int32_t*, int64_t,
+                                  const int32_t*, float, uint16_t*, void*, size_t, AttnArgs&);
+
+// The decode layer: QKV, then either the identity attention on the Q slice (att ==
+// nullptr) or QK-norm + RoPE + KV write and decode attention, then O (+ x) and the MLP.
+static a8w8_status layer_decode(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                                const uint16_t* gamma_post_bf16, float eps, a8w8_qweight qkv,
+                                a8w8_qweight o, a8w8_qweight gate, a8w8_qweight up,
+                                a8w8_qweight down, int64_t M, int64_t H, int64_t I,
+                                int n_q_heads, int n_kv_heads, int head_dim, int split_k,
+                                const a8w8_attention_step* att, uint16_t* qkv_out_bf16,
+                                uint16_t* h1_out_bf16, uint16_t* out_bf16, void* workspace,
+                                size_t ws_bytes, const a8w8_layer_taps* taps, void* stream) {
   if (a8w8_status s = check_mlp_shapes(M, H, I, split_k)) return s;
   if (n_q_heads <= 0 || n_kv_heads < 0 || head_dim <= 0) return A8W8_ERR_SHAPE;
   if (int64_t(n_q_heads) * head_dim != H) return A8W8_ERR_SHAPE;
@@ -565,7 +575,8 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   for (const a8w8_qweight* w : {&qkv, &o, &gate, &up, &down})
     if (a8w8_status s = check_qweight(*w)) return s;
   if (!aligned16(x_bf16) || !aligned16(gamma_in_bf16) || !aligned16(gamma_post_bf16) ||
-      !aligned16(out_bf16) || (qkv_out_bf16 && !aligned16(qkv_out_bf16)))
+      !aligned16(out_bf16) || (qkv_out_bf16 && !aligned16(qkv_out_bf16)) ||
+      (h1_out_bf16 && !aligned16(h1_out_bf16)))
     return A8W8_ERR_ALIGN;
   const size_t need = a8w8_workspace_bytes(A8W8_OP_LAYER_LINEARS, M, H, I, n_qkv, split_k,
                                            A8W8_MODE_DECODE_A8W8);
@@ -578,6 +589,29 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   const a8w8_mlp_taps* mt = taps ? &taps->mlp : nullptr;
   const Timer tm(mt, st);
   uint16_t* qkv_buf = qkv_out_bf16 ? qkv_out_bf16 : b.qkv;
+  uint16_t* h1 = h1_out_bf16 ? h1_out_bf16 : b.h1;
+  // Attention arguments are checked before anything is enqueued.
+  QkRopeArgs qa{};
+  AttnArgs aa{};
+  if (att) {
+    if (!att->q_rot_bf16 || !att->attn_bf16) return A8W8_ERR_NULL;
+    if (a8w8_status e = make_qk_args(qkv_buf, M, n_q_heads, n_kv_heads, head_dim,
+                                     att->q_gamma_bf16, att->k_gamma_bf16, att->qk_eps,
+                                     att->cos_table, att->sin_table, att->max_pos,
+                                     att->positions, att->block_table, att->blocks_per_seq,
+                                     att->k_cache_bf16, att->v_cache_bf16, att->num_blocks,
+                                     att->block_size, att->q_rot_bf16, qa))
+      return e;
+    if (a8w8_status e = make_attn_args(att->q_rot_bf16, M, n_q_heads, n_kv_heads, head_dim,
+                                       att->k_cache_bf16, att->v_cache_bf16, att->num_blocks,
+                                       att->block_size, att->block_table, att->blocks_per_seq,
+                                       att->context_lens, att->scale, att->attn_bf16,
+                                       att->attn_workspace, att->attn_ws_bytes, aa))
+      return e;
+  }
+  // O's input rows: the attention output, or the Q slice of QKV (identity attention).
+  const uint16_t* o_in = att ? att->attn_bf16 : qkv_buf;
+  const int64_t o_ld = att ? H : n_qkv;
 
 
   // QKV projection (input RMSNorm + quantization fused or separate) -> BF16.
@@ -612,23 +646,27 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
     A8W8_HIP(hipMemcpyAsync(taps->qkv, qkv_buf, size_t(M) * n_qkv * sizeof(uint16_t),
                             hipMemcpyDeviceToDevice, st));
 
-  // Identity attention: the Q slice qkv[:, :H] is quantized and fed to O; O adds the
-  // layer input as residual -> h1.
+  if (att) {
+    A8W8_HIP(launch_qk_rope(qa, st));
+    A8W8_HIP(launch_decode_attention(aa, st));
+  }
+
+  // O's input rows are quantized and fed to O; O adds the layer input as residual -> h1.
   StreamKArgs og = gemm_args(EPI_BF16_RES, pl.o, M, H, H, o, b, 1);
-  og.out = b.h1;
+  og.out = h1;
   og.ldo = H;
   og.res = x_bf16;
   og.ldr = H;
   og.tap_acc0 = taps ? taps->acc_o : nullptr;
   if (pl.fused) {
     og.prologue = PRO_QUANT_BF16;
-    og.x = qkv_buf;
-    og.ldx = n_qkv;
+    og.x = o_in;
+    og.ldx = o_ld;
     og.tap_q = taps ? taps->q_attn : nullptr;
     og.tap_s = taps ? taps->s_attn : nullptr;
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_ATTN));
-    A8W8_HIP(quant_kernel(qkv_buf, n_qkv, 0, nullptr, 0.0f, M, H, b.q_a, b.s_a, nullptr,
+    A8W8_HIP(quant_kernel(o_in, o_ld, 0, nullptr, 0.0f, M, H, b.q_a, b.s_a, nullptr,
                           taps ? taps->q_attn : nullptr, taps ? taps->s_attn : nullptr, st));
     A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_ATTN));
     og.prologue = PRO_CODES;
@@ -640,11 +678,38 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   A8W8_HIP(launch_streamk(og, pl.o, st));
   A8W8_HIP(tm.after(A8W8_KERNEL_O));
   if (taps && taps->h1)
-    A8W8_HIP(hipMemcpyAsync(taps->h1, b.h1, size_t(M) * H * sizeof(uint16_t),
+    A8W8_HIP(hipMemcpyAsync(taps->h1, h1, size_t(M) * H * sizeof(uint16_t),
                             hipMemcpyDeviceToDevice, st));
 
-  return run_mlp_decode(b.h1, gamma_post_bf16, eps, gate, up, down, b.h1, out_bf16, M, H, I,
+  return run_mlp_decode(h1, gamma_post_bf16, eps, gate, up, down, h1, out_bf16, M, H, I,
                         split_k, pl, b, 2, mt, tm, st);
+}
+
+a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                               const uint16_t* gamma_post_bf16, float eps,
+                               a8w8_qweight qkv, a8w8_qweight o, a8w8_qweight gate,
+                               a8w8_qweight up, a8w8_qweight down, int64_t M, int64_t H,
+                               int64_t I, int n_q_heads, int n_kv_heads, int head_dim,
+                               int split_k, uint16_t* qkv_out_bf16, uint16_t* out_bf16,
+                               void* workspace, size_t ws_bytes,
+                               const a8w8_layer_taps* taps, void* stream) {
+  return layer_decode(x_bf16, gamma_in_bf16, gamma_post_bf16, eps, qkv, o, gate, up, down, M,
+                      H, I, n_q_heads, n_kv_heads, head_dim, split_k, nullptr, qkv_out_bf16,
+                      nullptr, out_bf16, workspace, ws_bytes, taps, stream);
+}
+
+a8w8_status a8w8_decode_layer(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                              const uint16_t* gamma_post_bf16, float eps, a8w8_qweight qkv,
+                              a8w8_qweight o, a8w8_qweight gate, a8w8_qweight up,
+                              a8w8_qweight down, int64_t M, int64_t H, int64_t I,
+                              int n_q_heads, int n_kv_heads, int head_dim, int split_k,
+                              const a8w8_attention_step* attn, uint16_t* qkv_out_bf16,
+                              uint16_t* h1_out_bf16, uint16_t* out_bf16, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  if (!attn) return A8W8_ERR_NULL;
+  return layer_decode(x_bf16, gamma_in_bf16, gamma_post_bf16, eps, qkv, o, gate, up, down, M,
+                      H, I, n_q_heads, n_kv_heads, head_dim, split_k, attn, qkv_out_bf16,
+                      h1_out_bf16, out_bf16, workspace, ws_bytes, nullptr, stream);
 }
 
 a8w8_status a8w8_layer_linears_prefill(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
@@ -739,15 +804,17 @@ a8w8_status a8w8_layer_linears_prefill(const uint16_t* x_bf16, const uint16_t* g
                          I, pb, nullptr, tm, st);
 }
 
-a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_heads,
-                                 int n_kv_heads, int head_dim, const uint16_t* q_gamma_bf16,
-                                 const uint16_t* k_gamma_bf16, float eps,
-                                 const float* cos_table, const float* sin_table,
-                                 int64_t max_pos, const int32_t* positions,
-                                 const int32_t* block_table, int64_t blocks_per_seq,
-                                 uint16_t* k_cache_bf16, uint16_t* v_cache_bf16,
-                                 int64_t num_blocks, int64_t block_size, uint16_t* q_out_bf16,
-                                 void* stream) {
+// Validates the QK-norm + RoPE + KV step and fills its kernel arguments (a.M == 0 on
+// return: nothing to launch).
+static a8w8_status make_qk_args(const uint16_t* qkv_bf16, int64_t M, int n_q_heads,
+                                int n_kv_heads, int head_dim, const uint16_t* q_gamma_bf16,
+                                const uint16_t* k_gamma_bf16, float eps,
+                                const float* cos_table, const float* sin_table,
+                                int64_t max_pos, const int32_t* positions,
+                                const int32_t* block_table, int64_t blocks_per_seq,
+                                uint16_t* k_cache_bf16, uint16_t* v_cache_bf16,
+                                int64_t num_blocks, int64_t block_size, uint16_t* q_out_bf16,
+                                QkRopeArgs& a) {
   if (M < 0 || M > 65535 || n_q_heads <= 0 || n_kv_heads < 0 || head_dim <= 0 ||
       head_dim % 2 || head_dim > 512 || max_pos <= 0 || max_pos > (int64_t(1) << 31) - 1)
     return A8W8_ERR_SHAPE;
@@ -755,7 +822,10 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
   if (n_kv_heads > 0 && (blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0 ||
                          num_blocks > (int64_t(1) << 31) - 1))
     return A8W8_ERR_SHAPE;
-  if (M == 0) return A8W8_OK;
+  if (M == 0) {
+    a = QkRopeArgs{};
+    return A8W8_OK;
+  }
   if (!qkv_bf16 || !q_gamma_bf16 || !cos_table || !sin_table || !positions || !q_out_bf16)
     return A8W8_ERR_NULL;
   if (n_kv_heads > 0 && (!k_gamma_bf16 || !block_table || !k_cache_bf16 || !v_cache_bf16))
@@ -764,7 +834,7 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
        reinterpret_cast<uintptr_t>(positions) |
        reinterpret_cast<uintptr_t>(block_table)) & 3u)
     return A8W8_ERR_ALIGN;
-  QkRopeArgs a{};
+  a = QkRopeArgs{};
   a.qkv = qkv_bf16;
   a.M = M;
   a.n_q = n_q_heads;
@@ -786,6 +856,25 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
   a.block_size = block_size;
   a.q_out = q_out_bf16;
   a.ld_q = int64_t(n_q_heads) * head_dim;
+  return A8W8_OK;
+}
+
+a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_heads,
+                                 int n_kv_heads, int head_dim, const uint16_t* q_gamma_bf16,
+                                 const uint16_t* k_gamma_bf16, float eps,
+                                 const float* cos_table, const float* sin_table,
+                                 int64_t max_pos, const int32_t* positions,
+                                 const int32_t* block_table, int64_t blocks_per_seq,
+                                 uint16_t* k_cache_bf16, uint16_t* v_cache_bf16,
+                                 int64_t num_blocks, int64_t block_size, uint16_t* q_out_bf16,
+                                 void* stream) {
+  QkRopeArgs a;
+  if (a8w8_status e = make_qk_args(qkv_bf16, M, n_q_heads, n_kv_heads, head_dim, q_gamma_bf16,
+                                   k_gamma_bf16, eps, cos_table, sin_table, max_pos, positions,
+                                   block_table, blocks_per_seq, k_cache_bf16, v_cache_bf16,
+                                   num_blocks, block_size, q_out_bf16, a))
+    return e;
+  if (a.M == 0) return A8W8_OK;
   A8W8_HIP(launch_qk_rope(a, static_cast<hipStream_t>(stream)));
   return A8W8_OK;
 }
@@ -820,19 +909,24 @@ size_t a8w8_decode_attention_workspace_bytes(int64_t M, int n_q_heads, int n_kv_
   return static_cast<size_t>(n);
 }
 
-a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_heads,
+// Validates decode attention and fills its kernel arguments (a.M == 0 on return:
+// nothing to launch).
+static a8w8_status make_attn_args(const uint16_t* q_bf16, int64_t M, int n_q_heads,
                                   int n_kv_heads, int head_dim, const uint16_t* k_cache_bf16,
                                   const uint16_t* v_cache_bf16, int64_t num_blocks,
                                   int64_t block_size, const int32_t* block_table,
                                   int64_t blocks_per_seq, const int32_t* context_lens,
                                   float scale, uint16_t* out_bf16, void* workspace,
-                                  size_t ws_bytes, void* stream) {
+                                  size_t ws_bytes, AttnArgs& a) {
   if (num_blocks <= 0 || block_size <= 0 || blocks_per_seq <= 0 ||
       num_blocks > (int64_t(1) << 31) - 1 || block_size > (int64_t(1) << 31) - 1 ||
       blocks_per_seq > (int64_t(1) << 30) / block_size ||
       !attn_shapes_ok(M, n_q_heads, n_kv_heads, head_dim, blocks_per_seq * block_size))
     return A8W8_ERR_SHAPE;
-  if (M == 0) return A8W8_OK;
+  if (M == 0) {
+    a = AttnArgs{};
+    return A8W8_OK;
+  }
   if (!q_bf16 || !k_cache_bf16 || !v_cache_bf16 || !block_table || !context_lens || !out_bf16)
     return A8W8_ERR_NULL;
   if (!aligned16(q_bf16) || !aligned16(out_bf16) || !aligned16(k_cache_bf16) ||
@@ -840,7 +934,7 @@ a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_hea
       ((reinterpret_cast<uintptr_t>(block_table) | reinterpret_cast<uintptr_t>(context_lens)) & 3u))
     return A8W8_ERR_ALIGN;
   const int64_t max_ctx = blocks_per_seq * block_size;
-  AttnArgs a{};
+  a = AttnArgs{};
   a.q = q_bf16;
   a.M = M;
   a.ld_q = int64_t(n_q_heads) * head_dim;
@@ -872,6 +966,23 @@ a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_hea
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = a.ws_o + M * n_q_heads * a.n_split * head_dim;
   }
+  return A8W8_OK;
+}
+
+a8w8_status a8w8_decode_attention(const uint16_t* q_bf16, int64_t M, int n_q_heads,
+                                  int n_kv_heads, int head_dim, const uint16_t* k_cache_bf16,
+                                  const uint16_t* v_cache_bf16, int64_t num_blocks,
+                                  int64_t block_size, const int32_t* block_table,
+                                  int64_t blocks_per_seq, const int32_t* context_lens,
+                                  float scale, uint16_t* out_bf16, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  AttnArgs a;
+  if (a8w8_status e = make_attn_args(q_bf16, M, n_q_heads, n_kv_heads, head_dim, k_cache_bf16,
+                                     v_cache_bf16, num_blocks, block_size, block_table,
+                                     blocks_per_seq, context_lens, scale, out_bf16, workspace,
+                                     ws_bytes, a))
+    return e;
+  if (a.M == 0) return A8W8_OK;
   A8W8_HIP(launch_decode_attention(a, static_cast<hipStream_t>(stream)));
   return A8W8_OK;
 }
