@@ -50,7 +50,10 @@ def parse():
                    help="time the QK-norm + RoPE + KV-cache write step (Qwen3-14B heads, M=1 and 16)")
     p.add_argument("--attention", action="store_true",
                    help="time decode attention over the paged cache (Qwen3-14B heads, M=1 and 16)")
-    p.add_argument("--context", type=int, default=1024, help="context length for --attention")
+    p.add_argument("--context", type=int, default=1024,
+                   help="context length for --attention and --decode-layer")
+    p.add_argument("--decode-layer", action="store_true",
+                   help="time the Qwen3-14B decode layer with real attention (M=1 and 16)")
     p.add_argument("--layer", action="store_true",
                    help="with --config 4: the whole prefill layer (QKV, O and the MLP block)")
     p.add_argument("--graph", type=int, default=1,
@@ -482,6 +485,103 @@ def bench_attention(args, torch, B) -> None:
         "cpu_baseline": cpu}))
 
 
+def bench_decode_layer(args, torch, B) -> None:
+    """The Qwen3-14B decode layer with real attention (QKV, QK-norm + RoPE + KV write,
+    paged attention at context L, O, MLP) at the decode batches 1 and 16: microseconds per
+    layer from HIP events over graph-replayed calls, and the bytes the layer must read
+    (INT8 weights and scales of the five GEMMs, K and V of every attended position) over
+    that time against HBM peak."""
+    from w8a8_quantized_decode_amd import synth
+    cfg = synth.CONFIGS[2]
+    H, I, nq, nkv, hd = cfg.H, cfg.I, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    L = args.context
+    rows, cpu = [], None
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    def upw(w, s):
+        rm = up(w)
+        tiled = torch.empty_like(rm)
+        B.a8w8_pack_weight(rm, tiled)
+        return (tiled, up(s), B.LAYOUT_TILED)
+
+    d0 = synth.layer_inputs(cfg, layer=0, M=16)
+    w = {k: upw(d0["w_" + k], d0["s_" + k]) for k in ("qkv", "o", "gate", "up", "down")}
+    wbytes = sum(d0["w_" + k].nbytes + d0["s_" + k].nbytes for k in ("qkv", "o", "gate", "up", "down"))
+    for M in (1, 16):
+        d = synth.layer_inputs(cfg, layer=0, M=M)
+        a = synth.attention_inputs(cfg, [L] * M, block_size=16)
+        x, gin, gpost = up(d["x"]), up(d["gamma_in"]), up(d["gamma_post"])
+        kc, vc = up(a["k_cache"]), up(a["v_cache"])
+        t = {k: up(a[k]) for k in ("q_gamma", "k_gamma", "cos", "sin", "positions",
+                                   "context_lens", "block_table")}
+        out = torch.empty_like(x)
+        q_rot = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
+        attn = torch.empty_like(q_rot)
+        ws = torch.zeros(B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, M, H, I, cfg.n_qkv,
+                                                cfg.split_k), dtype=torch.uint8, device="cuda")
+        nws = B.a8w8_decode_attention_workspace_bytes(M, nq, nkv, hd, a["block_table"].shape[1] * 16)
+        aws = torch.zeros((max(nws, 256),), dtype=torch.uint8, device="cuda")
+
+        def call():
+            B.a8w8_decode_layer(x, gin, gpost, cfg.eps, w["qkv"], w["o"], w["gate"], w["up"],
+                                w["down"], out, ws, nq, nkv, hd, q_gamma=t["q_gamma"],
+                                k_gamma=t["k_gamma"], qk_eps=cfg.eps, cos_table=t["cos"],
+                                sin_table=t["sin"], positions=t["positions"],
+                                context_lens=t["context_lens"], block_table=t["block_table"],
+                                k_cache=kc, v_cache=vc, scale=a["scale"], q_rot=q_rot,
+                                attn=attn, attn_workspace=aws, split_k=cfg.split_k)
+        for _ in range(args.warmup):
+            call()
+        gr = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for _ in range(10):
+                call()
+        gr.replay()
+        reps = max(1, args.steps // 10)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / (reps * 10) * 1e3
+        nbytes = wbytes + M * L * nkv * hd * 2 * 2
+        rows.append({"M": M, "context": L, "us_per_layer": round(us, 2), "bytes": nbytes,
+                     "gb_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        if M == 1 and not args.no_cpu_baseline:
+            import oracle as O
+            cpu = oracle_per_call(
+                lambda: O.decode_layer(d["x"], d["gamma_in"], d["gamma_post"], cfg.eps,
+                                       d["w_qkv"], d["s_qkv"], d["w_o"], d["s_o"], d["w_gate"],
+                                       d["s_gate"], d["w_up"], d["s_up"], d["w_down"],
+                                       d["s_down"], nq, nkv, hd, cfg.split_k, a["q_gamma"],
+                                       a["k_gamma"], cfg.eps, a["cos"], a["sin"],
+                                       a["positions"], a["context_lens"], a["block_table"],
+                                       a["k_cache"], a["v_cache"], a["scale"]),
+                min(args.cpu_seconds, 10.0), f"the same M=1 layer at context {L}")
+    r1 = rows[0]
+    print(json.dumps({
+        "metric": "Qwen3-14B A8W8 decode layer with paged attention, microseconds per layer",
+        "value": r1["us_per_layer"], "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r1["us_per_layer"] / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded PCG64, Qwen3-14B shapes, random INT8 weights and BF16 cache)",
+        "config": {"workload": f"Qwen3-14B decode layer, real attention at context {L}, M=1",
+                   "per_batch": rows},
+        "roofline": {"bound": "hbm", "achieved": r1["gb_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r1["gb_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole layer (QKV, QK-RoPE, attention split + merge, O, MLP)",
+                     "algorithmic_bytes_per_launch": r1["bytes"]},
+        "cpu_baseline": cpu}))
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -501,6 +601,9 @@ def main():
         return
     if args.attention:
         bench_attention(args, torch, B)
+        return
+    if args.decode_layer:
+        bench_decode_layer(args, torch, B)
         return
     cfg = synth.CONFIGS[args.config]
     if cfg.kind == "prefill" and args.layer:
