@@ -5,10 +5,12 @@
 // over all decode rows) and > Gate/Up INT8 path (the post-attention RMSNorm output is
 // quantized once per row; the codes carry an FP32 row scale).
 //
-// One workgroup per row; the row is read three times from L2 (sum of squares,
-// absolute maximum, codes), recomputing the normalized value each time with the same
-// operations so every pass sees identical bits.  Reductions use a fixed tree, so the
-// result does not depend on scheduling.
+// One workgroup per row.  A row of up to kRegChunks * 4096 values is read once into
+// registers (all its loads in flight together) and the three passes (sum of squares,
+// absolute maximum, codes) run on the registers; a longer row is read three times from
+// L2, recomputing the normalized value each time with the same operations.  Either way
+// every thread takes its values in the same order and the reductions use a fixed tree,
+// so the result does not depend on the variant or on scheduling.
 //
 // Per row (readings where the pages leave the formula open):
 //   S  = sum f(x_k)^2 in FP64 (squares of BF16 are exact in FP64)
@@ -62,6 +64,112 @@ __device__ __forceinline__ void load_gamma(const uint16_t* g, int64_t k, float (
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = bf16_lo(w[i]);
     v[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+constexpr int kRegChunks = 5;  // rows of up to 5 * 512 * 8 = 20480 values stay in registers
+
+template <bool kRms, bool kF32In>
+__global__ __launch_bounds__(kQuantThreads) void quant_rows_reg_kernel(QuantRowsArgs p) {
+  using L = RowLoader<kF32In>;
+  constexpr int V = L::kVec;
+  __shared__ double s_sum[kQuantWaves];
+  __shared__ float s_max[kQuantWaves];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int64_t row = blockIdx.x;
+  const int64_t K = p.K;
+  const char* xrow = static_cast<const char*>(p.x) +
+                     row * p.ldx * (kF32In ? sizeof(float) : sizeof(uint16_t));
+  // Chunk c of this thread starts at k = (c * kQuantThreads + tid) * V, the order the
+  // looping kernel visits them in.
+  float v[kRegChunks][V];
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int64_t k = (int64_t(c) * kQuantThreads + tid) * V;
+    if (k < K) L::load(xrow, k, v[c]);
+  }
+
+  if (kRms) {
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      const int64_t k = (int64_t(c) * kQuantThreads + tid) * V;
+      if (k >= K) break;
+#pragma unroll
+      for (int i = 0; i < V; ++i) ss += double(v[c][i]) * double(v[c][i]);
+    }
+    ss = wave_sum_f64(ss);
+    if (lane == 0) s_sum[wave] = ss;
+    __syncthreads();
+    double S = 0.0;
+    for (int w = 0; w < kQuantWaves; ++w) S += s_sum[w];
+    const float ms = static_cast<float>(S / static_cast<double>(K));
+    const float t = ms + p.eps;
+    const float sq = __builtin_sqrtf(t);
+    const float r = 1.0f / sq;
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      const int64_t k = (int64_t(c) * kQuantThreads + tid) * V;
+      if (k >= K) break;
+      float g[V];
+      load_gamma(p.gamma, k, g);
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[c][i] = (v[c][i] * r) * g[i];
+    }
+  }
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int64_t k = (int64_t(c) * kQuantThreads + tid) * V;
+    if (k >= K) break;
+#pragma unroll
+    for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+    if (p.xn_tap) {
+      f32x4* t = reinterpret_cast<f32x4*>(p.xn_tap + row * K + k);
+      t[0] = f32x4{v[c][0], v[c][1], v[c][2], v[c][3]};
+      t[1] = f32x4{v[c][4], v[c][5], v[c][6], v[c][7]};
+    }
+    if (p.a_bf16 || p.a_bf16_tap) {
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pk[i] = uint32_t(f32_to_bf16_rne(v[c][2 * i])) |
+                (uint32_t(f32_to_bf16_rne(v[c][2 * i + 1])) << 16);
+      if (p.a_bf16)
+        *reinterpret_cast<u32x4*>(p.a_bf16 + (p.a_bf16_tiled ? prefill_operand_index(row, k, K)
+                                                             : row * K + k)) = pk;
+      if (p.a_bf16_tap) *reinterpret_cast<u32x4*>(p.a_bf16_tap + row * K + k) = pk;
+    }
+  }
+  if (!p.write_codes) return;
+  amax = wave_max_f32(amax);
+  if (lane == 0) s_max[wave] = amax;
+  __syncthreads();
+  float a = 0.0f;
+  for (int w = 0; w < kQuantWaves; ++w) a = fmaxf(a, s_max[w]);
+  const float s = a / 127.0f;
+  if (tid == 0) {
+    p.s[row] = s;
+    if (p.s_tap) p.s_tap[row] = s;
+  }
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int64_t k = (int64_t(c) * kQuantThreads + tid) * V;
+    if (k >= K) break;
+    uint32_t lo = 0, hi = 0;
+    if (s != 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= (uint32_t(quant_code(v[c][i], s)) & 0xFFu) << (8 * i);
+        hi |= (uint32_t(quant_code(v[c][4 + i], s)) & 0xFFu) << (8 * i);
+      }
+    }
+    const u32x2 pk = {lo, hi};
+    *reinterpret_cast<u32x2*>(p.q + row * K + k) = pk;
+    if (p.q_tap) *reinterpret_cast<u32x2*>(p.q_tap + row * K + k) = pk;
   }
 }
 
@@ -179,6 +287,17 @@ hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t stream) {
   // One workgroup per row.
   const dim3 grid(static_cast<unsigned>(a.M)), block(kQuantThreads);
   const bool rms = a.gamma != nullptr;
+  if (a.K <= int64_t(kRegChunks) * kQuantThreads * 8) {
+    if (rms && !a.x_is_f32)
+      hipLaunchKernelGGL((quant_rows_reg_kernel<true, false>), grid, block, 0, stream, a);
+    else if (!rms && !a.x_is_f32)
+      hipLaunchKernelGGL((quant_rows_reg_kernel<false, false>), grid, block, 0, stream, a);
+    else if (!rms && a.x_is_f32)
+      hipLaunchKernelGGL((quant_rows_reg_kernel<false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((quant_rows_reg_kernel<true, true>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   if (rms && !a.x_is_f32)
     hipLaunchKernelGGL((quant_rows_kernel<true, false>), grid, block, 0, stream, a);
   else if (!rms && !a.x_is_f32)
