@@ -114,3 +114,63 @@ def test_mlp_graph_replay_qwen3_14b():
         call(xb, out_e)
         t.cuda.synchronize()
         np.testing.assert_array_equal(host(out_e, np.uint16), want_b, err_msg=f"eager {rep}")
+
+
+def test_decode_layer_graph_replay_qwen3_14b():
+    """The decode layer with real attention captured once and replayed: each replay
+    rewrites the new token's cache slot and the attention partials and must reproduce
+    the eager output bit for bit, with eager calls on another input in between."""
+    cfg, M = C2, 2
+    announce(f"decode layer graph replay {cfg.name} M={M}")
+    t = torch()
+    d = synth.layer_inputs(cfg, layer=0, M=M)
+    xb_h = synth.layer_inputs(cfg, layer=1, M=M)["x"]
+    a = synth.attention_inputs(cfg, [300, 1000], block_size=16)
+    lay = B.LAYOUT_TILED
+    w = {k: qw(d["w_" + k], d["s_" + k], lay) for k in ("qkv", "o", "gate", "up", "down")}
+    nq, nkv, hd = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    dv = {k: dev(a[k]) for k in ("q_gamma", "k_gamma", "cos", "sin", "positions",
+                                 "context_lens", "block_table")}
+    gin, gpost = dev(d["gamma_in"]), dev(d["gamma_post"])
+    xa, xb = dev(d["x"]), dev(xb_h)
+    ws = zeros((B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, M, cfg.H, cfg.I, cfg.n_qkv,
+                                       cfg.split_k),), np.uint8)
+    aws = zeros((B.a8w8_decode_attention_workspace_bytes(M, nq, nkv, hd,
+                                                         a["block_table"].shape[1] * 16),),
+                np.uint8)
+
+    def make_bufs():
+        return dict(k=dev(a["k_cache"]), v=dev(a["v_cache"]),
+                    q=empty((M, nq * hd), np.uint16), att=empty((M, nq * hd), np.uint16),
+                    out=empty((M, cfg.H), np.uint16))
+
+    def call(x, bf):
+        B.a8w8_decode_layer(x, gin, gpost, cfg.eps, w["qkv"], w["o"], w["gate"], w["up"],
+                            w["down"], bf["out"], ws, nq, nkv, hd, q_gamma=dv["q_gamma"],
+                            k_gamma=dv["k_gamma"], qk_eps=cfg.eps, cos_table=dv["cos"],
+                            sin_table=dv["sin"], positions=dv["positions"],
+                            context_lens=dv["context_lens"], block_table=dv["block_table"],
+                            k_cache=bf["k"], v_cache=bf["v"], scale=a["scale"], q_rot=bf["q"],
+                            attn=bf["att"], attn_workspace=aws, split_k=cfg.split_k)
+
+    ea, eb, g = make_bufs(), make_bufs(), make_bufs()
+    call(xa, ea)
+    call(xb, eb)
+    t.cuda.synchronize()
+    want_a, want_b = host(ea["out"], np.uint16), host(eb["out"], np.uint16)
+    gr = t.cuda.CUDAGraph()
+    with t.cuda.graph(gr):
+        call(xa, g)
+    for rep in range(3):
+        g["out"].zero_()
+        gr.replay()
+        t.cuda.synchronize()
+        np.testing.assert_array_equal(host(g["out"], np.uint16), want_a, err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(host(g["k"], np.uint16), host(ea["k"], np.uint16))
+        call(xb, eb)
+        t.cuda.synchronize()
+        np.testing.assert_array_equal(host(eb["out"], np.uint16), want_b, err_msg=f"eager {rep}")
+    gr.replay()
+    gr.replay()
+    t.cuda.synchronize()
+    np.testing.assert_array_equal(host(g["out"], np.uint16), want_a, err_msg="back-to-back")
