@@ -879,12 +879,14 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
   return A8W8_OK;
 }
 
-// Positions per split: one wave per 64 positions while that keeps the grid under
-// kAttnTargetWaves waves, otherwise whole multiples of 64 so that it does.
-constexpr int64_t kAttnTargetWaves = 4096;
+// Positions per split: one workgroup per 64 positions while that keeps the grid under
+// kAttnTargetGroups workgroups, otherwise whole multiples of 64 so that it does.  Grids
+// of fewer than kAttnFourWaveChunks chunks of 64 positions run four waves per split.
+constexpr int64_t kAttnTargetGroups = 4096;
+constexpr int64_t kAttnFourWaveChunks = 512;
 static int64_t attn_split_len(int64_t M, int n_kv, int64_t max_ctx) {
   const int64_t chunks = (max_ctx + 63) / 64;
-  int64_t per = (M * n_kv * chunks + kAttnTargetWaves - 1) / kAttnTargetWaves;
+  int64_t per = (M * n_kv * chunks + kAttnTargetGroups - 1) / kAttnTargetGroups;
   if (per < 1) per = 1;
   if (per > chunks) per = chunks;
   return per * 64;
@@ -957,6 +959,7 @@ static a8w8_status make_attn_args(const uint16_t* q_bf16, int64_t M, int n_q_hea
     a.split_len = attn_split_len(M, n_kv_heads, max_ctx);
   }
   a.n_split = (max_ctx + a.split_len - 1) / a.split_len;
+  a.waves = (M * n_kv_heads * ((max_ctx + 63) / 64) < kAttnFourWaveChunks) ? 4 : 1;
   if (a.n_split > 1) {
     const size_t need =
         a8w8_decode_attention_workspace_bytes(M, n_q_heads, n_kv_heads, head_dim, max_ctx);

@@ -3,9 +3,12 @@
 // with a block table).
 //
 // The context of each (row, KV head) is cut into splits of split_len positions; one
-// wave per (split, KV head, row) serves the group's Q heads (grouped-query attention:
-// Q head h reads KV head h / (n_q / n_kv)) and walks its split in chunks of 64
-// positions:
+// workgroup per (split, KV head, row) serves the group's Q heads (grouped-query
+// attention: Q head h reads KV head h / (n_q / n_kv)) and walks its split in chunks of
+// 64 positions.  A small grid uses four waves per workgroup, each taking a quarter of
+// every chunk with its own online-softmax state (shorter chains per wave when the chip
+// has waves to spare); a large grid uses one wave, which keeps every workgroup resident
+// at once:
 //   * scores: a key row of D BF16 values is read by D/8 lanes, 16 bytes each, so one
 //     load instruction covers 64/(D/8) rows.  Each lane keeps the matching 8 query
 //     values of every head in registers, forms 8-term partial dot products, and the
@@ -15,9 +18,9 @@
 //   * values: value rows are read like key rows; each lane accumulates its 8 output
 //     dimensions over the rows it reads, with the weights taken from a 64-entry LDS
 //     table, and the row groups are summed once at the end of the split.
-// With one split the wave writes rne_bf16(o / l) directly; otherwise it writes the
-// split's FP32 (max, normalizer, unnormalized output) and a second kernel merges the
-// splits of each (row, Q head).  FP32 throughout; the oracle is the exact definition.
+// The waves' states are merged through LDS.  With one split the workgroup writes
+// rne_bf16(o / l) directly; otherwise it writes the split's FP32 (max, normalizer,
+// unnormalized output) and a second kernel merges the splits of each (row, Q head).  FP32 throughout; the oracle is the exact definition.
 #include "device_common.h"
 #include "internal.h"
 
@@ -69,27 +72,35 @@ __device__ __forceinline__ void unpack8(const u32x4& w, float (&v)[8]) {
   }
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs p) {
+template <int D, int G, int kAttnWaves>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs p) {
   constexpr int LPR = D / 8;        // lanes per cache row
   constexpr int RG = kWave / LPR;   // rows per load instruction
   constexpr int T = LPR;            // load instructions per chunk (T * RG == 64)
+  constexpr int TW = T / kAttnWaves;  // load instructions of each wave per chunk
+  static_assert(TW * kAttnWaves == T, "the chunk's loads split evenly over the waves");
   __shared__ int64_t pslot[kWave];  // cache offset of each chunk position (-1: none)
-  __shared__ float pw[G][RG][LPR];  // softmax weight of chunk position RG * t + g at [g][t]
+  __shared__ float pw[kAttnWaves][G][RG][TW];  // weight of position RG * (w*TW + u) + g
+  __shared__ float st_m[kAttnWaves][G], st_l[kAttnWaves][G];
+  __shared__ float st_o[kAttnWaves][G][D];
 
   const int64_t m = blockIdx.z;
   const int kvh = static_cast<int>(blockIdx.y);
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = kAttnWaves == 1 ? 0 : tid / kWave;
+  const int lane = tid % kWave;
   const int r = lane % LPR, g = lane / LPR;
-  // The context length, the query and the block number of this lane's first position
-  // are requested together (the table entry exists whenever the position is below
+  const int t0 = wave * TW;         // this wave's first load instruction
+  const bool slot_thread = kAttnWaves == 1 || tid < kWave;  // fills the chunk's slots
+  // The context length, the query and the block number of the first position are
+  // requested together (the table entry exists whenever the position is below
   // blocks_per_seq * block_size, which the host keeps below 2^30).
   const int32_t bs = static_cast<int32_t>(p.block_size);
   const int32_t max_ctx = static_cast<int32_t>(p.blocks_per_seq * p.block_size);
   const int32_t* bt = p.block_table + m * p.blocks_per_seq;
   const int32_t begin = static_cast<int32_t>(int64_t(blockIdx.x) * p.split_len);
   const int32_t L = p.context_lens[m];
-  int32_t blk_next = (begin + lane < max_ctx) ? bt[(begin + lane) / bs] : -1;
+  int32_t blk_next = (slot_thread && begin + tid < max_ctx) ? bt[(begin + tid) / bs] : -1;
   u32x4 qraw[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -109,62 +120,64 @@ __global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs p) {
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.0f;
   }
   const int64_t row_stride = int64_t(p.n_kv) * D;
+  // Lane (g, r) of wave w holds the scores of position RG * r + g when w * TW <= r <
+  // (w + 1) * TW; its other lanes hold none.
+  const bool owner = r >= t0 && r < t0 + TW;
 
   for (int32_t base = begin; base < end; base += kWave) {
-    {
-      const int32_t j = base + lane;
+    if (slot_thread) {
+      const int32_t j = base + tid;
       const int32_t blk = blk_next;
       int64_t slot = -1;
       if (j < end && blk >= 0 && blk < p.num_blocks)
         slot = (int64_t(blk) * bs + j % bs) * row_stride + int64_t(kvh) * D;
-      pslot[lane] = slot;
+      pslot[tid] = slot;
       // the next chunk's block number is requested before this chunk's rows
       const int32_t jn = j + kWave;
-      blk_next = (base + kWave < end && jn < end) ? bt[jn / bs] : -1;
+      blk_next = (jn < end) ? bt[jn / bs] : -1;
     }
     __syncthreads();
 
-    // Scores.  Load instruction t reads chunk position RG * t + g; after the row sums
-    // lane (g, r) keeps the scores of position RG * r + g.  All T key loads are in
-    // flight together, and the value loads are issued as soon as the keys are used, so
-    // their latency overlaps the softmax.
+    // Scores.  Load instruction t = t0 + u reads chunk position RG * t + g; the key
+    // loads are in flight together, and the value loads are issued as soon as the keys
+    // are used, so their latency overlaps the softmax.
     float sel[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) sel[h] = 0.0f;
-    bool has[T];
-    u32x4 kv[T];
+    bool has[TW];
+    u32x4 kv[TW];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int64_t sl = pslot[RG * t + g];
-      has[t] = sl >= 0;
-      kv[t] = *reinterpret_cast<const u32x4*>(p.k_cache + (has[t] ? sl : 0) + r * 8);
+    for (int u = 0; u < TW; ++u) {
+      const int64_t sl = pslot[RG * (t0 + u) + g];
+      has[u] = sl >= 0;
+      kv[u] = *reinterpret_cast<const u32x4*>(p.k_cache + (has[u] ? sl : 0) + r * 8);
     }
-    u32x4 vv[T];
+    u32x4 vv[TW];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int u = 0; u < TW; ++u) {
       float kf[8];
-      unpack8(kv[t], kf);
+      unpack8(kv[u], kf);
       // the value row of the same position reuses this lane's address
-      const int64_t sl = pslot[RG * t + g];
-      vv[t] = *reinterpret_cast<const u32x4*>(p.v_cache + (has[t] ? sl : 0) + r * 8);
+      const int64_t sl = pslot[RG * (t0 + u) + g];
+      vv[u] = *reinterpret_cast<const u32x4*>(p.v_cache + (has[u] ? sl : 0) + r * 8);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float s = 0.0f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) s = fmaf(qf[h][c], kf[c], s);
         s = group_sum<LPR>(s);
-        sel[h] = (r == t) ? s : sel[h];
+        sel[h] = (r == t0 + u) ? s : sel[h];
       }
     }
-    const bool live = pslot[RG * r + g] >= 0;
+    const bool live = owner && pslot[RG * r + g] >= 0;
 
-    // Online softmax per head.
+    // Online softmax per head over this wave's positions.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float sh = live ? sel[h] * p.scale : -INFINITY;
       const float nm = fmaxf(run_m[h], wave_max(sh));
       const float w = live ? __expf(sh - nm) : 0.0f;
-      pw[h][g][r] = w;
+      if (owner) pw[wave][h][g][r - t0] = w;
       const float f = (run_m[h] == -INFINITY) ? 0.0f : __expf(run_m[h] - nm);
       run_l[h] = run_l[h] * f + wave_sum(w);
       run_m[h] = nm;
@@ -176,13 +189,13 @@ __global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs p) {
     // Values: a position without a slot contributes nothing (its row is not used,
     // whatever row 0 of the cache holds).
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      if (!has[t]) continue;
+    for (int u = 0; u < TW; ++u) {
+      if (!has[u]) continue;
       float vf[8];
-      unpack8(vv[t], vf);
+      unpack8(vv[u], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float w = pw[h][g][t];
+        const float w = pw[wave][h][g][u];
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(w, vf[c], acc[h][c]);
       }
@@ -190,40 +203,78 @@ __global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs p) {
     __syncthreads();
   }
 
-  // Sum the row groups (lanes with the same r hold the same output dimensions).
+  // Sum the row groups (lanes with the same r hold the same output dimensions), then
+  // hand each wave's state to LDS.
 #pragma unroll
   for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[h][c] += __shfl_xor(acc[h][c], o, kWave);
-
-  if (p.n_split == 1) {
+  if constexpr (kAttnWaves == 1) {
+    // One wave: its state is the split's; lanes 0 .. LPR-1 write it from registers.
     if (g != 0) return;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      u32x4 o;
+      if (p.n_split == 1) {
+        u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = run_l[h] > 0.0f ? acc[h][2 * i] / run_l[h] : 0.0f;
-        const float b = run_l[h] > 0.0f ? acc[h][2 * i + 1] / run_l[h] : 0.0f;
-        o[i] = uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
+        for (int i = 0; i < 4; ++i) {
+          const float a = run_l[h] > 0.0f ? acc[h][2 * i] / run_l[h] : 0.0f;
+          const float b = run_l[h] > 0.0f ? acc[h][2 * i + 1] / run_l[h] : 0.0f;
+          o[i] = uint32_t(f32_to_bf16_rne(a)) | (uint32_t(f32_to_bf16_rne(b)) << 16);
+        }
+        *reinterpret_cast<u32x4*>(p.out + m * p.ld_q + int64_t(kvh * G + h) * D + r * 8) = o;
+      } else {
+        const int64_t idx = (m * p.n_q + kvh * G + h) * p.n_split + blockIdx.x;
+        float* o = p.ws_o + idx * D + r * 8;
+        *reinterpret_cast<f32x4*>(o) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+        if (lane == 0) {
+          p.ws_ml[2 * idx] = run_m[h];
+          p.ws_ml[2 * idx + 1] = run_l[h];
+        }
       }
-      *reinterpret_cast<u32x4*>(p.out + m * p.ld_q + int64_t(kvh * G + h) * D + r * 8) = o;
     }
     return;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int64_t idx = (m * p.n_q + kvh * G + h) * p.n_split + blockIdx.x;
-    if (g == 0) {
-      float* o = p.ws_o + idx * D + r * 8;
-      *reinterpret_cast<f32x4*>(o) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-    }
     if (lane == 0) {
-      p.ws_ml[2 * idx] = run_m[h];
-      p.ws_ml[2 * idx + 1] = run_l[h];
+      st_m[wave][h] = run_m[h];
+      st_l[wave][h] = run_l[h];
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) st_o[wave][h][r * 8 + c] = acc[h][c];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves; with one split the result is the output, otherwise the split's
+  // partial (max, normalizer, unnormalized output).
+  for (int e = tid; e < G * D; e += kAttnWaves * kWave) {
+    const int h = e / D, i = e % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) mx = fmaxf(mx, st_m[w][h]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      if (st_m[w][h] == -INFINITY) continue;
+      const float f = __expf(st_m[w][h] - mx);
+      o = fmaf(st_o[w][h][i], f, o);
+      l = fmaf(st_l[w][h], f, l);
+    }
+    if (p.n_split == 1) {
+      p.out[m * p.ld_q + int64_t(kvh * G + h) * D + i] = f32_to_bf16_rne(l > 0.0f ? o / l : 0.0f);
+    } else {
+      const int64_t idx = (m * p.n_q + kvh * G + h) * p.n_split + blockIdx.x;
+      p.ws_o[idx * D + i] = o;
+      if (i == 0) {
+        p.ws_ml[2 * idx] = mx;
+        p.ws_ml[2 * idx + 1] = l;
+      }
     }
   }
 }
@@ -295,9 +346,14 @@ template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.n_split), static_cast<unsigned>(a.n_kv),
                   static_cast<unsigned>(a.M));
-  switch (a.group) {
-#define A8W8_ATTN_CASE(GG) \
-  case GG: hipLaunchKernelGGL((attn_split_kernel<D, GG>), grid, dim3(kWave), 0, stream, a); break;
+  switch (a.group * 16 + a.waves) {
+#define A8W8_ATTN_CASE(GG)                                                                  \
+  case GG * 16 + 1:                                                                         \
+    hipLaunchKernelGGL((attn_split_kernel<D, GG, 1>), grid, dim3(kWave), 0, stream, a);    \
+    break;                                                                                  \
+  case GG * 16 + 4:                                                                         \
+    hipLaunchKernelGGL((attn_split_kernel<D, GG, 4>), grid, dim3(4 * kWave), 0, stream, a); \
+    break;
     A8W8_ATTN_CASE(1) A8W8_ATTN_CASE(2) A8W8_ATTN_CASE(3) A8W8_ATTN_CASE(4)
     A8W8_ATTN_CASE(5) A8W8_ATTN_CASE(6) A8W8_ATTN_CASE(7) A8W8_ATTN_CASE(8)
 #undef A8W8_ATTN_CASE
