@@ -18,6 +18,7 @@
 #include <random>
 
 #include "../../include/a8w8.h"
+#include "attention_args.h"
 #include "internal.h"
 
 using namespace a8w8;

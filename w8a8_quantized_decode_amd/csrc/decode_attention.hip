@@ -22,6 +22,7 @@
 // rne_bf16(o / l) directly; otherwise it writes the split's FP32 (max, normalizer,
 // unnormalized output) and a second kernel merges the splits of each (row, Q head).  FP32 throughout; the oracle is the exact definition.
 #include "device_common.h"
+#include "attention_args.h"
 #include "internal.h"
 
 namespace a8w8 {

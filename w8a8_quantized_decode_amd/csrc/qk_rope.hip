@@ -10,6 +10,7 @@
 // is built without contraction), so the result is the oracle's bit for bit.  Rows whose
 // position or cache block lies outside the given tables are skipped.
 #include "device_common.h"
+#include "attention_args.h"
 #include "internal.h"
 
 namespace a8w8 {
