@@ -7,8 +7,9 @@ separate workgroups take, then merged) and without one (one workgroup walks the 
 context).  Cases: the Qwen3-14B head counts (40 Q, 8 KV heads of 128) at the decode
 batches 1 and 16 with context lengths that cross chunk and block boundaries, a context
 of 4096 at batch 1 (64 splits), a toy shape with a different group and head size, a row
-with an out-of-range length, which must leave its output untouched, and block tables with
-holes (block numbers out of range), whose positions are left out.
+with an out-of-range length, which must leave its output untouched, block tables with
+holes (block numbers out of range), whose positions are left out, and the group sizes 1,
+3 and 8 at both head sizes (the kernel is compiled per group size and head size).
 """
 
 import math
@@ -91,3 +92,11 @@ def test_attention_skips_out_of_range_rows(mode):
 def test_attention_block_table_holes(mode):
     announce(f"decode attention block-table holes {mode}")
     _run([300, 129, 64, 17], 16, 2, 128, bs=16, bps=20, seed=9, mode=mode, holes=6)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("nq,nkv,d", [(4, 4, 128), (6, 2, 64), (16, 2, 128), (24, 3, 64)],
+                         ids=["mha-d128", "group3-d64", "group8-d128", "group8-d64"])
+def test_attention_group_sizes(nq, nkv, d, mode):
+    announce(f"decode attention nq={nq} nkv={nkv} d={d} {mode}")
+    _run([1, 64, 100, 257, 700], nq, nkv, d, bs=16, bps=48, seed=nq + d, mode=mode)
