@@ -883,7 +883,7 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
 // Positions per split: one workgroup per 64 positions while that keeps the grid under
 // kAttnTargetGroups workgroups, otherwise whole multiples of 64 so that it does.  Grids
 // of fewer than kAttnFourWaveChunks chunks of 64 positions run four waves per split.
-constexpr int64_t kAttnTargetGroups = 4096;
+constexpr int64_t kAttnTargetGroups = 2048;
 constexpr int64_t kAttnFourWaveChunks = 512;
 static int64_t attn_split_len(int64_t M, int n_kv, int64_t max_ctx) {
   const int64_t chunks = (max_ctx + 63) / 64;
