@@ -335,13 +335,17 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
  * FP32 with an online softmax.  Shapes: n_q % n_kv == 0, n_q / n_kv <= 8, d in {64, 128},
  * M <= 65535, blocks_per_seq * block_size <= 2^30.  A row with L outside
  * [1, blocks_per_seq * block_size] is skipped (its output is not written); a position
- * whose block number is out of range is left out of the softmax.
+ * whose block number is out of range is left out of the softmax, and a row with no
+ * position left gets zeros.
  * workspace: NULL, or ws_bytes >= a8w8_decode_attention_workspace_bytes(M, n_q, n_kv,
  * d, blocks_per_seq * block_size), 256-byte aligned scratch (contents on entry do not
- * matter).  With a workspace the context of each row is cut into splits that separate
- * workgroups take (one kernel for the splits, one that merges them; the merge runs
- * only when there is more than one split); with NULL one workgroup per (row, KV head)
- * walks the whole context (one kernel; slow for long contexts at small M).
+ * matter; calls that share a workspace must not overlap in time).  The size query
+ * returns 0 for invalid shapes and when the context needs no split.  With a workspace
+ * the context of each row is cut into splits that separate workgroups take (one kernel
+ * for the splits, one that merges them; the merge runs only when there is more than
+ * one split); with NULL one workgroup per (row, KV head) walks the whole context (one
+ * kernel; slow for long contexts at small M).  Errors: A8W8_ERR_SHAPE, _NULL, _ALIGN
+ * (q, out, the caches or the workspace misaligned), _WORKSPACE (too small).
  */
 size_t a8w8_decode_attention_workspace_bytes(int64_t M, int n_q_heads, int n_kv_heads,
                                              int head_dim, int64_t max_context);
