@@ -1,6 +1,8 @@
 /*
  * a8w8.h -- C ABI of liba8w8: the A8W8 decode-step linears of a Qwen3-14B-shaped
- * transformer layer on MI355X (gfx950).
+ * transformer layer on MI355X (gfx950), with the attention side of the decode layer
+ * (QK-norm + RoPE + paged BF16 KV-cache write, decode attention over the paged cache)
+ * and the whole decode layer built from them.
  *
  * What is computed (sources: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode
  * scheduling and data paths", sections What changed > Decode scheduling and > Gate/Up
