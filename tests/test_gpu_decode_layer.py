@@ -105,3 +105,11 @@ def test_decode_layer_qwen3_14b_m16():
     announce("decode layer qwen3-14b M=16")
     ctx = np.random.default_rng(11).integers(1, 1024, size=16).tolist()
     _run(C2, ctx, True)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_layer_first_token(M):
+    """Context 1: attention reads only the slot the QK step has just written in the same
+    call, so the output depends on that write being visible to the attention kernel."""
+    announce(f"decode layer qwen3-14b first token M={M}")
+    _run(C2, [1] * M, True)
