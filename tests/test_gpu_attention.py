@@ -6,7 +6,8 @@ where |y| < 1.  Each case runs twice: with a workspace (the context cut into spl
 separate workgroups take, then merged) and without one (one workgroup walks the whole
 context).  Cases: the Qwen3-14B head counts (40 Q, 8 KV heads of 128) at the decode
 batches 1 and 16 with context lengths that cross chunk and block boundaries, a context
-of 4096 at batch 1 (64 splits), a toy shape with a different group and head size, a row
+of 4096 at batch 1 (64 splits) and of 16384 (256 splits, merged in groups of 64), a toy
+shape with a different group and head size, a row
 with an out-of-range length, which must leave its output untouched, block tables with
 holes (block numbers out of range), whose positions are left out, and the group sizes 1,
 3 and 8 at both head sizes (the kernel is compiled per group size and head size).
@@ -100,3 +101,10 @@ def test_attention_block_table_holes(mode):
 def test_attention_group_sizes(nq, nkv, d, mode):
     announce(f"decode attention nq={nq} nkv={nkv} d={d} {mode}")
     _run([1, 64, 100, 257, 700], nq, nkv, d, bs=16, bps=48, seed=nq + d, mode=mode)
+
+
+def test_attention_long_context_many_splits():
+    """Context 16384 at M=2: 256 splits per row, so the merge runs over several groups of
+    64 splits; the second row is ragged (a partial last split)."""
+    announce("decode attention qwen3-14b M=2 context 16384 split")
+    _run([16384, 12345], 40, 8, 128, bs=16, bps=1024, seed=11, mode="split")
