@@ -32,7 +32,9 @@ closed forms, invariants or error bounds.  The end-to-end compositions
 ``layer_linears_prefill``) are pinned only
 through their stage pins plus an error bound against exact (unquantized) FP64 math:
 the pages print no worked example of a whole block, so as compositions they are
-"parity unpinned" beyond those stage pins.
+"parity unpinned" beyond those stage pins.  ``decode_layer`` (the layer with real
+attention) is pinned beyond its stages by the one-position context, the
+identity-attention layer's QKV and h1, and the cache slot it writes.
 """
 
 from __future__ import annotations
