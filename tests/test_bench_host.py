@@ -1,0 +1,66 @@
+"""Host-side logic of bench.py, on the CPU: the one-GPU rule, the calibration of the
+HBM-traffic summary on the weight-packing copy, and the source-hash check that keeps
+counters taken on another kernel source out of the bench line."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from w8a8_quantized_decode_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PACK = "a8w8::(anonymous namespace)::pack_tiled_kernel(signed char const*, long, long, signed char*)"
+GATEUP = "void a8w8::(anonymous namespace)::streamk_kernel<2, 2, 8, 1, 1, 1>(a8w8::StreamKArgs)"
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+        for name, grid, kib in rows:
+            f.write(f'"{name}",{grid},{counter},{kib}\n')
+
+
+def test_pmc_summary_calibrates_on_the_pack_copy(tmp_path, monkeypatch):
+    cfg = synth.CONFIGS[2]
+    nbytes = cfg.I * cfg.H            # one Gate weight: the pack reads and writes it once
+    # FETCH_SIZE reports the copy at half its size, WRITE_SIZE at its size: factors 2 and 1
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                 [(PACK, nbytes // 16, nbytes / 1024 / 2), (GATEUP, 1, 1000.0), (GATEUP, 1, 1002.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                 [(PACK, nbytes // 16, nbytes / 1024), (GATEUP, 1, 10.0), (GATEUP, 1, 10.0)])
+    monkeypatch.setattr(bench, "PMC_FILE", str(tmp_path / "pmc.json"))
+    monkeypatch.setattr(bench, "PMC_MD", str(tmp_path / "pmc.md"))
+    bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), ["fetch", "write"], cfg)
+    s = json.load(open(tmp_path / "pmc.json"))
+    assert s["fetch_factor"] == pytest.approx(2.0)
+    assert s["write_factor"] == pytest.approx(1.0)
+    assert s["hbm_bytes_per_dispatch"] == round(1001.0 * 1024 * 2 + 10.0 * 1024)
+    assert s["kernel_source_hash"] == bench.kernel_source_hash()
+    # the bench line takes the traffic only while the kernel source is the one measured
+    assert bench.measured_traffic(0) == s["hbm_bytes_per_dispatch"]
+    s["kernel_source_hash"] = "0" * 16
+    with open(tmp_path / "pmc.json", "w") as f:
+        json.dump(s, f)
+    assert bench.measured_traffic(0) is None
+
+
+def test_pmc_summary_rejects_a_copy_of_unknown_size(tmp_path, monkeypatch):
+    cfg = synth.CONFIGS[2]
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(PACK, 12345, 1.0), (GATEUP, 1, 1.0)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(PACK, 12345, 1.0), (GATEUP, 1, 1.0)])
+    monkeypatch.setattr(bench, "PMC_FILE", str(tmp_path / "pmc.json"))
+    monkeypatch.setattr(bench, "PMC_MD", str(tmp_path / "pmc.md"))
+    with pytest.raises(SystemExit):
+        bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), ["f", "w"], cfg)
+    assert not os.path.exists(tmp_path / "pmc.json")
