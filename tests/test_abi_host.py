@@ -191,16 +191,19 @@ def test_attention_validation(L):
     assert call(kc=MIS) == 3
     assert call(q=FAKE + 8) == 3
     assert call(bt=FAKE + 2) == 3
-    # context 1024 at M=1 is cut into splits: the workspace must fit them and be aligned
-    need = B.a8w8_decode_attention_workspace_bytes(1, 40, 8, 128, 64 * 16)
-    assert need == 1 * 40 * 16 * (128 + 2) * 4
-    assert call(bps=64, ws=FAKE, wsb=need - 1) == 4
-    assert call(bps=64, ws=FAKE + 16, wsb=need) == 3
+    # context 4096 at M=1 is cut into splits: the workspace must fit them and be aligned
+    need = B.a8w8_decode_attention_workspace_bytes(1, 40, 8, 128, 256 * 16)
+    assert need == 1 * 40 * 64 * (128 + 2) * 4
+    assert call(bps=256, ws=FAKE, wsb=need - 1) == 4
+    assert call(bps=256, ws=FAKE + 16, wsb=need) == 3
 
 
 def test_attention_workspace_bytes(L):
     ws = B.a8w8_decode_attention_workspace_bytes
     assert ws(1, 40, 8, 128, 64) == 0            # one split: no workspace
+    assert ws(8, 40, 8, 128, 256) == 0           # 64 (row, KV head) pairs of 4 chunks: no split
+    assert ws(9, 40, 8, 128, 256) > 0            # more pairs: split
+    assert ws(1, 40, 8, 128, 320) > 0            # more chunks: split
     assert ws(1, 40, 8, 128, 4096) == 40 * 64 * 130 * 4
     # many rows: splits grow in whole chunks so the grid stays near 2048 workgroups
     assert ws(16, 40, 8, 128, 4096) == 16 * 40 * 16 * 130 * 4

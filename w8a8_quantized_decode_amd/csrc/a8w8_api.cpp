@@ -880,13 +880,22 @@ a8w8_status a8w8_qk_norm_rope_kv(const uint16_t* qkv_bf16, int64_t M, int n_q_he
   return A8W8_OK;
 }
 
-// Positions per split: one workgroup per 64 positions while that keeps the grid under
-// kAttnTargetGroups workgroups, otherwise whole multiples of 64 so that it does.  Grids
-// of fewer than kAttnFourWaveChunks chunks of 64 positions run four waves per split.
+// Small problems (at most kAttnWholeGroups (row, KV head) pairs of at most
+// kAttnWholeChunks chunks of 64 positions) run one workgroup of eight waves per pair,
+// each wave taking whole chunks, with no split and no merge.  Otherwise, positions per
+// split: one workgroup per 64 positions while that keeps the grid under
+// kAttnTargetGroups workgroups, otherwise whole multiples of 64 so that it does; grids of
+// fewer than kAttnFourWaveChunks chunks run four waves per split.
+constexpr int64_t kAttnWholeGroups = 64;
+constexpr int64_t kAttnWholeChunks = 4;
 constexpr int64_t kAttnTargetGroups = 2048;
 constexpr int64_t kAttnFourWaveChunks = 512;
+static bool attn_whole(int64_t M, int n_kv, int64_t max_ctx) {
+  return M * n_kv <= kAttnWholeGroups && (max_ctx + 63) / 64 <= kAttnWholeChunks;
+}
 static int64_t attn_split_len(int64_t M, int n_kv, int64_t max_ctx) {
   const int64_t chunks = (max_ctx + 63) / 64;
+  if (attn_whole(M, n_kv, max_ctx)) return chunks * 64;
   int64_t per = (M * n_kv * chunks + kAttnTargetGroups - 1) / kAttnTargetGroups;
   if (per < 1) per = 1;
   if (per > chunks) per = chunks;
@@ -960,7 +969,10 @@ static a8w8_status make_attn_args(const uint16_t* q_bf16, int64_t M, int n_q_hea
     a.split_len = attn_split_len(M, n_kv_heads, max_ctx);
   }
   a.n_split = (max_ctx + a.split_len - 1) / a.split_len;
-  a.waves = (M * n_kv_heads * ((max_ctx + 63) / 64) < kAttnFourWaveChunks) ? 4 : 1;
+  if (attn_whole(M, n_kv_heads, max_ctx))
+    a.waves = 8;  // eight waves on whole chunks
+  else
+    a.waves = (M * n_kv_heads * ((max_ctx + 63) / 64) < kAttnFourWaveChunks) ? 4 : 1;
   if (a.n_split > 1) {
     const size_t need =
         a8w8_decode_attention_workspace_bytes(M, n_q_heads, n_kv_heads, head_dim, max_ctx);

@@ -45,7 +45,7 @@ struct AttnArgs {
   uint16_t* out;            // [M, ld_q] BF16
   int64_t split_len;        // positions per split (a multiple of 64)
   int64_t n_split;          // splits per row: ceil(blocks_per_seq * block_size / split_len)
-  int waves;                // waves per split workgroup: 1 or 4
+  int waves;                // waves per workgroup: 1 or 4 sharing each chunk, 8 on whole chunks
   float* ws_o;              // [M, n_q, n_split, head_dim] FP32 partial outputs (n_split > 1)
   float* ws_ml;             // [M, n_q, n_split, 2] FP32 partial (max, normalizer)
 };

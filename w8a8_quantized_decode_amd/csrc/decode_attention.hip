@@ -73,14 +73,18 @@ __device__ __forceinline__ void unpack8(const u32x4& w, float (&v)[8]) {
   }
 }
 
-template <int D, int G, int kAttnWaves>
+// kWhole: each wave takes whole chunks (wave w the chunks w, w + W, ...), with its own
+// slot table and wave-level waits inside the chunk loop; otherwise the waves share each
+// chunk, a quarter of its load instructions each.
+template <int D, int G, int kAttnWaves, bool kWhole>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs p) {
   constexpr int LPR = D / 8;        // lanes per cache row
   constexpr int RG = kWave / LPR;   // rows per load instruction
   constexpr int T = LPR;            // load instructions per chunk (T * RG == 64)
-  constexpr int TW = T / kAttnWaves;  // load instructions of each wave per chunk
-  static_assert(TW * kAttnWaves == T, "the chunk's loads split evenly over the waves");
-  __shared__ int64_t pslot[kWave];  // cache offset of each chunk position (-1: none)
+  constexpr int TW = kWhole ? T : T / kAttnWaves;  // load instructions of each wave per chunk
+  static_assert(kWhole || TW * kAttnWaves == T, "the chunk's loads split evenly over the waves");
+  constexpr int kStride = kWhole ? kAttnWaves * kWave : kWave;  // positions between a wave's chunks
+  __shared__ int64_t pslot[kWhole ? kAttnWaves : 1][kWave];  // cache offset of each chunk position (-1: none)
   __shared__ float pw[kAttnWaves][G][RG][TW];  // weight of position RG * (w*TW + u) + g
   __shared__ float st_m[kAttnWaves][G], st_l[kAttnWaves][G];
   __shared__ float st_o[kAttnWaves][G][D];
@@ -91,8 +95,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
   const int wave = kAttnWaves == 1 ? 0 : tid / kWave;
   const int lane = tid % kWave;
   const int r = lane % LPR, g = lane / LPR;
-  const int t0 = wave * TW;         // this wave's first load instruction
-  const bool slot_thread = kAttnWaves == 1 || tid < kWave;  // fills the chunk's slots
+  const int t0 = kWhole ? 0 : wave * TW;  // this wave's first load instruction
+  const bool slot_thread = kWhole || kAttnWaves == 1 || tid < kWave;  // fills the chunk's slots
+  const int ps = kWhole ? wave : 0;       // this wave's slot table
   // The context length, the query and the block number of the first position are
   // requested together (the table entry exists whenever the position is below
   // blocks_per_seq * block_size, which the host keeps below 2^30).
@@ -100,8 +105,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
   const int32_t max_ctx = static_cast<int32_t>(p.blocks_per_seq * p.block_size);
   const int32_t* bt = p.block_table + m * p.blocks_per_seq;
   const int32_t begin = static_cast<int32_t>(int64_t(blockIdx.x) * p.split_len);
+  const int32_t first = kWhole ? begin + wave * kWave : begin;  // this wave's first chunk
   const int32_t L = p.context_lens[m];
-  int32_t blk_next = (slot_thread && begin + tid < max_ctx) ? bt[(begin + tid) / bs] : -1;
+  int32_t blk_next = (slot_thread && first + lane < max_ctx) ? bt[(first + lane) / bs] : -1;
   u32x4 qraw[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -123,21 +129,32 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
   const int64_t row_stride = int64_t(p.n_kv) * D;
   // Lane (g, r) of wave w holds the scores of position RG * r + g when w * TW <= r <
   // (w + 1) * TW; its other lanes hold none.
-  const bool owner = r >= t0 && r < t0 + TW;
+  const bool owner = kWhole || (r >= t0 && r < t0 + TW);
+  // Waits between a chunk's LDS writes and reads: the whole workgroup when the waves
+  // share the chunk; the wave alone when it has the chunk to itself (the waves then run
+  // different numbers of chunks).
+  auto chunk_sync = [] {
+    if constexpr (kWhole) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      __syncthreads();
+    }
+  };
 
-  for (int32_t base = begin; base < end; base += kWave) {
+  for (int32_t base = first; base < end; base += kStride) {
     if (slot_thread) {
-      const int32_t j = base + tid;
+      const int32_t j = base + lane;
       const int32_t blk = blk_next;
       int64_t slot = -1;
       if (j < end && blk >= 0 && blk < p.num_blocks)
         slot = (int64_t(blk) * bs + j % bs) * row_stride + int64_t(kvh) * D;
-      pslot[tid] = slot;
+      pslot[ps][lane] = slot;
       // the next chunk's block number is requested before this chunk's rows
-      const int32_t jn = j + kWave;
+      const int32_t jn = j + kStride;
       blk_next = (jn < end) ? bt[jn / bs] : -1;
     }
-    __syncthreads();
+    chunk_sync();
 
     // Scores.  Load instruction t = t0 + u reads chunk position RG * t + g; the key
     // loads are in flight together, and the value loads are issued as soon as the keys
@@ -149,7 +166,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
     u32x4 kv[TW];
 #pragma unroll
     for (int u = 0; u < TW; ++u) {
-      const int64_t sl = pslot[RG * (t0 + u) + g];
+      const int64_t sl = pslot[ps][RG * (t0 + u) + g];
       has[u] = sl >= 0;
       kv[u] = *reinterpret_cast<const u32x4*>(p.k_cache + (has[u] ? sl : 0) + r * 8);
     }
@@ -159,7 +176,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
       float kf[8];
       unpack8(kv[u], kf);
       // the value row of the same position reuses this lane's address
-      const int64_t sl = pslot[RG * (t0 + u) + g];
+      const int64_t sl = pslot[ps][RG * (t0 + u) + g];
       vv[u] = *reinterpret_cast<const u32x4*>(p.v_cache + (has[u] ? sl : 0) + r * 8);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
         sel[h] = (r == t0 + u) ? s : sel[h];
       }
     }
-    const bool live = owner && pslot[RG * r + g] >= 0;
+    const bool live = owner && pslot[ps][RG * r + g] >= 0;
 
     // Online softmax per head over this wave's positions.
 #pragma unroll
@@ -185,7 +202,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[h][c] *= f;
     }
-    __syncthreads();
+    chunk_sync();
 
     // Values: a position without a slot contributes nothing (its row is not used,
     // whatever row 0 of the cache holds).
@@ -201,7 +218,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
         for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(w, vf[c], acc[h][c]);
       }
     }
-    __syncthreads();
+    chunk_sync();
   }
 
   // Sum the row groups (lanes with the same r hold the same output dimensions), then
@@ -350,10 +367,13 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
   switch (a.group * 16 + a.waves) {
 #define A8W8_ATTN_CASE(GG)                                                                  \
   case GG * 16 + 1:                                                                         \
-    hipLaunchKernelGGL((attn_split_kernel<D, GG, 1>), grid, dim3(kWave), 0, stream, a);    \
+    hipLaunchKernelGGL((attn_split_kernel<D, GG, 1, false>), grid, dim3(kWave), 0, stream, a); \
     break;                                                                                  \
   case GG * 16 + 4:                                                                         \
-    hipLaunchKernelGGL((attn_split_kernel<D, GG, 4>), grid, dim3(4 * kWave), 0, stream, a); \
+    hipLaunchKernelGGL((attn_split_kernel<D, GG, 4, false>), grid, dim3(4 * kWave), 0, stream, a); \
+    break;                                                                                  \
+  case GG * 16 + 8:                                                                         \
+    hipLaunchKernelGGL((attn_split_kernel<D, GG, 8, true>), grid, dim3(8 * kWave), 0, stream, a); \
     break;
     A8W8_ATTN_CASE(1) A8W8_ATTN_CASE(2) A8W8_ATTN_CASE(3) A8W8_ATTN_CASE(4)
     A8W8_ATTN_CASE(5) A8W8_ATTN_CASE(6) A8W8_ATTN_CASE(7) A8W8_ATTN_CASE(8)
