@@ -5,10 +5,13 @@
 // The context of each (row, KV head) is cut into splits of split_len positions; one
 // workgroup per (split, KV head, row) serves the group's Q heads (grouped-query
 // attention: Q head h reads KV head h / (n_q / n_kv)) and walks its split in chunks of
-// 64 positions.  A small grid uses four waves per workgroup, each taking a quarter of
-// every chunk with its own online-softmax state (shorter chains per wave when the chip
-// has waves to spare); a large grid uses one wave, which keeps every workgroup resident
-// at once:
+// 64 positions.  Three shapes of workgroup, chosen by the host from the problem size:
+//   * one wave (large grids: every workgroup stays resident at once);
+//   * four waves, each taking a quarter of every chunk with its own online-softmax
+//     state (small grids: shorter dependent chains per wave);
+//   * eight waves on whole chunks of one unsplit context (short contexts: no partials
+//     and no merge kernel).
+// Per chunk:
 //   * scores: a key row of D BF16 values is read by D/8 lanes, 16 bytes each, so one
 //     load instruction covers 64/(D/8) rows.  Each lane keeps the matching 8 query
 //     values of every head in registers, forms 8-term partial dot products, and the
@@ -20,7 +23,8 @@
 //     table, and the row groups are summed once at the end of the split.
 // The waves' states are merged through LDS.  With one split the workgroup writes
 // rne_bf16(o / l) directly; otherwise it writes the split's FP32 (max, normalizer,
-// unnormalized output) and a second kernel merges the splits of each (row, Q head).  FP32 throughout; the oracle is the exact definition.
+// unnormalized output) and a second kernel merges the splits of each (row, Q head).
+// FP32 throughout; the oracle is the exact definition.
 #include "device_common.h"
 #include "attention_args.h"
 #include "internal.h"
