@@ -113,3 +113,12 @@ def test_decode_layer_first_token(M):
     call, so the output depends on that write being visible to the attention kernel."""
     announce(f"decode layer qwen3-14b first token M={M}")
     _run(C2, [1] * M, True)
+
+
+@pytest.mark.parametrize("with_ws", [True, False], ids=["split", "whole"])
+def test_decode_layer_toy_head_dim_64(with_ws):
+    """Head size 64 through the whole layer (4 Q and 2 KV heads, H = 256)."""
+    cfg = synth.Config(0, "toy layer d64", 2, 256, 768, "layer", n_q_heads=4, n_kv_heads=2,
+                       head_dim=64)
+    announce(f"decode layer toy d=64 {with_ws}")
+    _run(cfg, [300, 45], with_ws)
