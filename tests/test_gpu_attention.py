@@ -108,3 +108,12 @@ def test_attention_long_context_many_splits():
     64 splits; the second row is ragged (a partial last split)."""
     announce("decode attention qwen3-14b M=2 context 16384 split")
     _run([16384, 12345], 40, 8, 128, bs=16, bps=1024, seed=11, mode="split")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_attention_many_rows(mode):
+    """100 rows with ragged contexts (1 .. 300): a large batch of rows, where the grid's
+    row dimension and the split choice for many (row, KV head) pairs are exercised."""
+    announce(f"decode attention qwen3-14b M=100 {mode}")
+    lens = np.random.default_rng(21).integers(1, 301, size=100)
+    _run(lens, 40, 8, 128, bs=16, bps=19, seed=21, mode=mode)
