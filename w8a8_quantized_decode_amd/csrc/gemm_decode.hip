@@ -1,0 +1,904 @@
+// Decode GEMM with one 16-wave workgroup per CU: INT8 x INT8 -> INT32 on gfx950 matrix
+// cores with the fused input quantization (RMSNorm + per-row quantization, or the
+// requantization of h for Down) and the fused dequant / SiLU / residual / split-K
+// epilogues.  It serves the layer chain and the MLP block at decode batch sizes
+// (M <= kFuseMaxRows) for the shapes it covers (plan_decode); the stream-K kernel in
+// gemm_streamk.hip serves the others.
+//
+// Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
+// paths", What changed > Gate/Up INT8 path (INT8 x INT8 -> INT32 Gate/Up matmuls with
+// the activation-row and weight-channel scales applied at dequantization, the
+// post-attention RMSNorm output quantized once per row) and > Decode scheduling (Down
+// split two ways along K into independent accumulators), with the CodeRabbit walkthrough
+// row "Split down projection accumulation" (FP32 partials summed, the residual added,
+// the sum narrowed with round-to-nearest-even).  QKV and O reuse the pattern.
+//
+// Why this shape.  At decode batch sizes the kernel is a weight stream: every weight
+// byte is read once.  What a plain stream does not have is the dependency of every
+// matrix instruction on the input row's statistics.  Measured on MI355X: a row read by
+// a wave that has weight loads queued (its own or other waves' on the same CU) waits
+// behind them, 2.5-7 us; the same row read before any weight load by waves that issue
+// none arrives in 0.5-1 us.  So the 16 waves are split by role:
+//   * waves 0-3 (control): request the input row(s) before anything else, then compute
+//     the row statistics and the INT8 codes of the whole row into LDS; then prefetch the
+//     epilogue inputs into LDS and, for the "leftover" tiles (below), stream their
+//     quarter of a shared tile and publish it;
+//   * waves 4-15 (stream): wait at one barrier until the row requests are out, issue two
+//     deep batches of weight loads, wait for the codes, then stream the workgroup's whole
+//     tiles through the matrix cores.
+// Every workgroup owns whole tiles (16 output channels over all of K), so a tile's partial
+// sums meet in LDS and the kernel's tail has no exchange between workgroups.  When the
+// tile count is G*q + G/4 (Gate/Up: 1088 = 256*4 + 64; Down: 320 = 256 + 64), the last
+// G/4 tiles are cut into K quarters, one per workgroup; each quarter is computed early by
+// the control waves and published as tagged words, and the owner of quarter 0 adds the
+// four and runs that tile's epilogue long before the stream ends.  Otherwise the tiles
+// are dealt whole, q or q + 1 per workgroup (QKV: 448 tiles, O: 320 tiles).
+#include "device_common.h"
+#include "internal.h"
+
+namespace a8w8 {
+namespace {
+
+constexpr int kDcWaves = 16;
+constexpr int kDcCtl = 4;                        // control waves
+constexpr int kDcStream = kDcWaves - kDcCtl;     // stream waves
+constexpr int kDcThreads = kDcWaves * kWave;
+constexpr int kDcCtlThreads = kDcCtl * kWave;
+constexpr int kDcMaxGrid = 256;
+constexpr int kDcMaxTiles = 5;                   // whole tiles per workgroup
+constexpr int kBfUnits = 3;                      // BF16 row: 8-value units per control thread
+constexpr int kF32Units = 18;                    // FP32 row: 4-value units per control thread
+constexpr int64_t kBfMaxK = int64_t(kBfUnits) * 8 * kDcCtlThreads;   // 6144
+constexpr int64_t kF32MaxK = int64_t(kF32Units) * 4 * kDcCtlThreads; // 18432
+constexpr int kSlotWords = 4 * kWave;            // tagged 64-bit words per matrix per piece
+constexpr size_t kDcMaxLds = 150 * 1024;
+
+struct DcSmem {
+  double sum_slot[kFuseMaxRows][kDcCtl];
+  float max_slot[kFuseMaxRows][kDcCtl];
+  float row_scale[kFuseMaxRows];
+  int ctl_sync;        // control-wave barrier counter
+  int lo_arrive;       // control waves done with their share of the leftover quarter
+  float sw[kDcMaxTiles + 1][2][16];                 // channel scales (slot kDcMaxTiles: leftover)
+  uint16_t res[kDcMaxTiles + 1][kFuseMaxRows][16];  // residual
+};
+
+// Barrier of the four control waves only (the stream waves are in their loop): an LDS
+// counter that every control wave advances once per use; waits until all have.
+__device__ __forceinline__ void ctl_sync(DcSmem& sm, int& gen) {
+  gen += kDcCtl;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    __hip_atomic_fetch_add(&sm.ctl_sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  while (__hip_atomic_load(&sm.ctl_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < gen)
+    __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// INT8 codes clamp(rint(v / s), -127, 127) of N values, s > 0, with the correctly rounded
+// quotient computed only where it can matter.  rs = fl32(1/s) and t = fl32(v * rs) carry
+// two roundings, a relative error of at most 2^-23, so |t - v/s| <= |t| * 2^-22.9 and
+// fl32(v/s) lies within |t| * 2^-24 of v/s.  If t is farther than |t| * 2^-21 from the
+// midpoint n + 1/2 of its neighbours, fl32(v/s) rounds to the same integer as t and is no
+// tie.  Otherwise (or when t is not finite: s subnormal) the exact quotient decides; that
+// path runs only when some lane of the wave needs it.
+template <int N>
+__device__ __forceinline__ void quant_codes(const float (&v)[N], float s, float rs, int (&q)[N]) {
+  bool need = false;
+  float qf[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float t = v[i] * rs;
+    qf[i] = rintf(t);
+    const float d = fabsf(t - qf[i]);
+    need = need || !(d < 0.5f - fabsf(t) * 4.76837158203125e-7f);
+  }
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float t = v[i] * rs;
+      const float d = fabsf(t - rintf(t));
+      if (!(d < 0.5f - fabsf(t) * 4.76837158203125e-7f)) qf[i] = rintf(v[i] / s);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) q[i] = static_cast<int>(fminf(fmaxf(qf[i], -127.0f), 127.0f));
+}
+
+__device__ __forceinline__ u32x2 codes8_fast(const float (&v)[8], float s, float rs) {
+  int q[8];
+  quant_codes<8>(v, s, rs, q);
+  uint32_t lo = 0, hi = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= (uint32_t(q[i]) & 0xFFu) << (8 * i);
+      hi |= (uint32_t(q[4 + i]) & 0xFFu) << (8 * i);
+    }
+  }
+  return u32x2{lo, hi};
+}
+
+__device__ __forceinline__ uint32_t codes4_fast(const f32x4& h, float s, float rs) {
+  const float v[4] = {h[0], h[1], h[2], h[3]};
+  int q[4];
+  quant_codes<4>(v, s, rs, q);
+  uint32_t w = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= (uint32_t(q[i]) & 0xFFu) << (8 * i);
+  }
+  return w;
+}
+
+// Wave reductions in registers: four DPP steps leave every lane of a 16-lane row with the
+// row's result (each step combines a lane with a partner that holds the mirrored partial,
+// and addition and maximum are commutative, so both partners get identical bits), then
+// the four rows are combined from lanes 0, 16, 32 and 48 in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(uint32_t(u)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(uint32_t(u >> 32)), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+}
+constexpr int kDppQuad1032 = 0xB1, kDppQuad2301 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(uint32_t(u)), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(uint32_t(u >> 32)), l);
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuad1032>(v));
+  v = fmaxf(v, dpp_f32<kDppQuad2301>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+               fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+  v = v + dpp_f64<kDppQuad1032>(v);
+  v = v + dpp_f64<kDppQuad2301>(v);
+  v = v + dpp_f64<kDppHalfMirror>(v);
+  v = v + dpp_f64<kDppMirror>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
+// ------------------------------------------------------------------ control-wave prologues
+// The input row is copied straight into an LDS staging area by the control waves (direct
+// global-to-LDS loads take no registers), in 16-byte chunks: chunk c = u * 256 + ct of
+// control thread ct lands at stage + 16 * c.  The staging area overlaps the partial-sum
+// areas, which are used only after the prologue.
+__device__ __forceinline__ void stage_chunks(const void* src, int64_t nbytes, int8_t* stage,
+                                             int units) {
+  const int ct = threadIdx.x, w = ct / kWave, l = ct & (kWave - 1);
+  const int8_t* s8 = static_cast<const int8_t*>(src);
+  for (int u = 0; u < units; ++u) {
+    const int64_t c = int64_t(u) * kDcCtlThreads + ct;
+    const int64_t off = c * 16 < nbytes ? c * 16 : 0;   // chunks past the row re-read chunk 0
+    // Lane l of the wave writes stage + 16 * (u * 256 + 64 * w + l).
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(s8 + off),
+                                     reinterpret_cast<__shared__ uint32_t*>(
+                                         stage + (int64_t(u) * kDcCtlThreads + w * kWave) * 16),
+                                     16, 0, 0);
+    (void)l;
+  }
+}
+
+// RMSNorm (when gamma) and quantization of one BF16 row staged at xs (and the gain at gs)
+// into codes act[0..K), scale into sm.row_scale[m]; taps (xn, q, s) when requested.
+// Values k = u * 2048 + ct * 8 + i.  The passes are loops that re-read the staged row from
+// LDS: this code runs once per workgroup at the start of the kernel, when every line of it
+// is fetched into the instruction cache behind the weight stream, so it is kept short.
+__device__ __forceinline__ void bf_vals(const int8_t* xs, int u, int ct, int64_t K, float (&v)[8]) {
+  const bool in = int64_t(u) * 8 * kDcCtlThreads + ct * 8 < K;
+  const u32x4 xr = *reinterpret_cast<const u32x4*>(xs + (int64_t(u) * kDcCtlThreads + ct) * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = in ? bf16_lo(xr[i]) : 0.0f;
+    v[2 * i + 1] = in ? bf16_hi(xr[i]) : 0.0f;
+  }
+}
+
+__device__ void ctl_row_bf16(const StreamKArgs& p, DcSmem& sm, int8_t* act, int m,
+                             const int8_t* xs, const int8_t* gs, bool taps, int& gen) {
+  const int ct = threadIdx.x, wave = ct / kWave;
+  const int64_t K = p.K;
+  float r = 1.0f;
+  if (p.gamma) {
+    // Sum of squares in FP64; the square of a BF16 value is exact in FP64, so a fused
+    // multiply-add rounds exactly as the product followed by the sum.  Then
+    // r = 1 / sqrt(fl32(S / K) + eps) with correctly rounded steps.
+    double ss = 0.0;
+#pragma unroll 1
+    for (int u = 0; u < kBfUnits; ++u) {
+      float v[8];
+      bf_vals(xs, u, ct, K, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = __builtin_fma(double(v[i]), double(v[i]), ss);
+    }
+    ss = wave_sum_dpp(ss);
+    if ((ct & (kWave - 1)) == 0) sm.sum_slot[m][wave] = ss;
+    ctl_sync(sm, gen);
+    double S = 0.0;
+#pragma unroll
+    for (int w = 0; w < kDcCtl; ++w) S += sm.sum_slot[m][w];
+    const float ms = static_cast<float>(S / static_cast<double>(K));
+    const float t = ms + p.eps;
+    r = 1.0f / __builtin_sqrtf(t);
+  }
+  auto norm = [&](int u, float (&v)[8]) {
+    bf_vals(xs, u, ct, K, v);
+    if (p.gamma) {
+      const u32x4 gr = *reinterpret_cast<const u32x4*>(gs + (int64_t(u) * kDcCtlThreads + ct) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = (v[2 * i] * r) * bf16_lo(gr[i]);
+        v[2 * i + 1] = (v[2 * i + 1] * r) * bf16_hi(gr[i]);
+      }
+    }
+  };
+  float amax = 0.0f;
+#pragma unroll 1
+  for (int u = 0; u < kBfUnits; ++u) {
+    float v[8];
+    norm(u, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  amax = wave_max_dpp(amax);
+  if ((ct & (kWave - 1)) == 0) sm.max_slot[m][wave] = amax;
+  ctl_sync(sm, gen);
+  float a = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDcCtl; ++w) a = fmaxf(a, sm.max_slot[m][w]);
+  const float s = a / 127.0f;
+  const float rs = 1.0f / s;
+  if (ct == 0) sm.row_scale[m] = s;
+  if (taps && ct == 0 && p.tap_s) p.tap_s[m] = s;
+#pragma unroll 1
+  for (int u = 0; u < kBfUnits; ++u) {
+    const int64_t k = int64_t(u) * 8 * kDcCtlThreads + ct * 8;
+    if (k < K) {
+      float v[8];
+      norm(u, v);
+      const u32x2 c = codes8_fast(v, s, rs);
+      *reinterpret_cast<u32x2*>(act + k) = c;
+      if (taps && p.tap_q) *reinterpret_cast<u32x2*>(p.tap_q + int64_t(m) * K + k) = c;
+      if (taps && p.tap_xn) {
+        f32x4* tx = reinterpret_cast<f32x4*>(p.tap_xn + int64_t(m) * K + k);
+        tx[0] = f32x4{v[0], v[1], v[2], v[3]};
+        tx[1] = f32x4{v[4], v[5], v[6], v[7]};
+      }
+    }
+  }
+}
+
+// Partial maxima of |h| per 16-channel tile of the producing GEMM: [npmax, M].
+constexpr int kPmUnits = 2;  // 4-value units per control thread (8 * 256 = 2048 words)
+struct PmRegs {
+  f32x4 v[kPmUnits];
+};
+
+__device__ __forceinline__ void fetch_pmax(const StreamKArgs& p, PmRegs& r) {
+  const int ct = threadIdx.x;
+  const int64_t n = p.npmax * p.M;
+#pragma unroll
+  for (int u = 0; u < kPmUnits; ++u) {
+    const int64_t e = int64_t(u) * 4 * kDcCtlThreads + ct * 4;
+    r.v[u] = *reinterpret_cast<const f32x4*>(p.pmax + (e < n ? e : 0));
+  }
+}
+
+// Row scales of the requantized input from the partial maxima (all rows at once).
+__device__ void ctl_requant_scales(const StreamKArgs& p, DcSmem& sm, const PmRegs& r, bool taps,
+                                   int& gen) {
+  const int ct = threadIdx.x, wave = ct / kWave;
+  const int64_t n = p.npmax * p.M;
+  float mx[kFuseMaxRows];
+#pragma unroll
+  for (int m = 0; m < kFuseMaxRows; ++m) mx[m] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kPmUnits; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t e = int64_t(u) * 4 * kDcCtlThreads + ct * 4 + i;
+      if (e < n) {
+        const int m = static_cast<int>(e % p.M);
+#pragma unroll
+        for (int mm = 0; mm < kFuseMaxRows; ++mm)
+          if (mm == m) mx[mm] = fmaxf(mx[mm], r.v[u][i]);
+      }
+    }
+  // partial maxima beyond the prefetched words (npmax * M > 2048)
+  for (int64_t e = int64_t(kPmUnits) * 4 * kDcCtlThreads + ct; e < n; e += kDcCtlThreads) {
+    const int m = static_cast<int>(e % p.M);
+    const float v = p.pmax[e];
+#pragma unroll
+    for (int mm = 0; mm < kFuseMaxRows; ++mm)
+      if (mm == m) mx[mm] = fmaxf(mx[mm], v);
+  }
+#pragma unroll
+  for (int m = 0; m < kFuseMaxRows; ++m) {
+    const float w = wave_max_dpp(mx[m]);
+    if ((ct & (kWave - 1)) == 0) sm.max_slot[m][wave] = w;
+  }
+  ctl_sync(sm, gen);
+  if (ct < p.M) {
+    float a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDcCtl; ++w) a = fmaxf(a, sm.max_slot[ct][w]);
+    const float s = a / 127.0f;
+    sm.row_scale[ct] = s;
+    if (taps && p.tap_s) p.tap_s[ct] = s;
+  }
+  ctl_sync(sm, gen);
+}
+
+// Codes of one FP32 row staged at hs into act[0..K): values k = u * 1024 + ct * 4 + i.
+__device__ void ctl_row_f32(const StreamKArgs& p, const DcSmem& sm, int8_t* act, int m,
+                            const int8_t* hs, bool taps) {
+  const int ct = threadIdx.x;
+  const float s = sm.row_scale[m];
+  const float rs = 1.0f / s;
+#pragma unroll 1
+  for (int u = 0; u < kF32Units; ++u) {
+    const int64_t k = int64_t(u) * 4 * kDcCtlThreads + ct * 4;
+    if (k < p.K) {
+      const f32x4 h = *reinterpret_cast<const f32x4*>(hs + (int64_t(u) * kDcCtlThreads + ct) * 16);
+      const uint32_t c = codes4_fast(h, s, rs);
+      *reinterpret_cast<uint32_t*>(act + k) = c;
+      if (taps && p.tap_q) *reinterpret_cast<uint32_t*>(p.tap_q + int64_t(m) * p.K + k) = c;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ epilogue
+// Element-wise: lane l handles output channel l % 16 of one (tile, row) pair, pair index
+// pq = base + l / 16; pairs enumerate (local tile j, row m) with m fastest.  sums(j, part,
+// mat, m, n) yields the INT32 sum of K partition part (EPI_DOWN) or of the whole K, for
+// weight matrix mat, row m and channel n of local tile j.  tile_of(j) is the global tile and
+// slot_of(j) its LDS slot of epilogue inputs.  The 16 lanes of a pair form one DPP row, so
+// the tile's absolute maximum of h (Gate/Up) is a row reduction.
+template <int EPI, int NMAT, typename Sums, typename TileOf, typename SlotOf>
+__device__ void dc_epilogue(const StreamKArgs& p, const DcSmem& sm, int32_t npairs, int32_t pq,
+                            int nparts, Sums&& sums, TileOf&& tile_of, SlotOf&& slot_of) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = lane & 15;
+  const bool act_pair = pq < npairs;
+  const int32_t j = act_pair ? pq / static_cast<int32_t>(p.M) : 0;
+  const int64_t m = act_pair ? pq - int64_t(j) * p.M : 0;
+  const int32_t t = tile_of(j);
+  const int slot = slot_of(j);
+  const int64_t en = int64_t(t) * 16 + n;
+  const float sa = sm.row_scale[m];
+  const float sw0 = sm.sw[slot][0][n], sw1 = sm.sw[slot][NMAT - 1][n];
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_BF16_RES) {
+    if (!act_pair) return;
+    const int32_t acc = sums(j, 0, 0, m, n);
+    if (p.tap_acc0) p.tap_acc0[m * p.N + en] = acc;
+    float y = dq(acc, sa, sw0);
+    if constexpr (EPI == EPI_BF16_RES) y = y + bf16_bits_to_f32(sm.res[slot][m][n]);
+    p.out[m * p.ldo + en] = f32_to_bf16_rne(y);
+  } else if constexpr (EPI == EPI_SILU) {
+    float h = 0.0f;
+    if (act_pair) {
+      const int32_t ag = sums(j, 0, 0, m, n), au = sums(j, 0, NMAT - 1, m, n);
+      if (p.tap_acc0) p.tap_acc0[m * p.N + en] = ag;
+      if (p.tap_acc1) p.tap_acc1[m * p.N + en] = au;
+      h = silu_mul(dq(ag, sa, sw0), dq(au, sa, sw1));
+      p.h[m * p.ldh + en] = h;
+      if (p.tap_h) p.tap_h[m * p.N + en] = h;
+    }
+    // Absolute maximum over the tile's 16 channels of row m, for the next requantization.
+    float mx = fabsf(h);
+    mx = fmaxf(mx, dpp_f32<kDppQuad1032>(mx));
+    mx = fmaxf(mx, dpp_f32<kDppQuad2301>(mx));
+    mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
+    mx = fmaxf(mx, dpp_f32<kDppMirror>(mx));
+    if (p.pmax_out && act_pair && n == 0) p.pmax_out[int64_t(t) * p.M + m] = mx;
+  } else {  // EPI_DOWN: partitions dequantized one by one and summed in order, then the residual
+    if (!act_pair) return;
+    const int64_t MN = p.M * p.N;
+    float tot = 0.0f;
+    for (int q = 0; q < nparts; ++q) {
+      const int32_t acc = sums(j, q, 0, m, n);
+      const float pv = dq(acc, sa, sw0);
+      if (p.tap_acc0) p.tap_acc0[q * MN + m * p.N + en] = acc;
+      if (p.tap_p) p.tap_p[q * MN + m * p.N + en] = pv;
+      tot = (q == 0) ? pv : tot + pv;
+    }
+    p.out[m * p.ldo + en] = f32_to_bf16_rne(tot + bf16_bits_to_f32(sm.res[slot][m][n]));
+  }
+}
+
+// INT32 sum of a segment accumulator kept in LDS in the matrix-instruction layout: row m,
+// channel n is lane 16 * (n / 4) + m, component n % 4.
+__device__ __forceinline__ int32_t acc_elem(const int32_t* seg_acc, int mat, int64_t m, int n) {
+  return seg_acc[mat * kWave * 4 + ((n >> 2) * 16 + m) * 4 + (n & 3)];
+}
+
+// ------------------------------------------------------------------ the kernel
+template <int EPI, int NMAT, int LAYOUT>
+__global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, DecodeGeom dg) {
+  constexpr bool kReq = EPI == EPI_DOWN;   // FP32 input requantized with partial maxima
+  constexpr int U = NMAT == 2 ? 4 : 8;      // K steps per batch (8 loads of 16 bytes per lane)
+  __shared__ DcSmem sm;
+  extern __shared__ __align__(16) int8_t lds[];
+  int8_t* act = lds;                                               // [M][act_ld] codes
+  int32_t* accum = reinterpret_cast<int32_t*>(lds + dg.acc_off);   // per segment, INT32 sums
+  int32_t* lred = reinterpret_cast<int32_t*>(lds + dg.lred_off);   // control waves' partials
+  constexpr int kPart = NMAT * 4 * kWave;                          // INT32 per partial
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int row16 = lane & 15, kg = lane >> 4;
+  const int32_t b = static_cast<int32_t>(blockIdx.x);
+  const int32_t St = dg.steps_tile, Ss = dg.steps_seg, P = St / Ss;
+  int32_t tb0, nt;
+  if (dg.leftover) {
+    tb0 = b * dg.whole_q;
+    nt = dg.whole_q;
+  } else {
+    tb0 = b * dg.whole_q + (b < dg.whole_r ? b : dg.whole_r);
+    nt = dg.whole_q + (b < dg.whole_r ? 1 : 0);
+  }
+  const int64_t act_ld = dg.act_ld;
+  const bool taps = b == 0;
+  if (tid == 0) {
+    sm.ctl_sync = 0;
+    sm.lo_arrive = 0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the counters are set before barrier #1
+  }
+
+  // ---- phase 1: the control waves request row 0 of the input first, into LDS.
+  int8_t* stage = lds + dg.acc_off;        // overlaps the accumulators (zeroed after it)
+  int8_t* stage_g = stage + dg.stage_g;    // the RMSNorm gain
+  PmRegs pm;
+  uint32_t epoch = 0;
+  if (wave < kDcCtl) {
+    if constexpr (kReq) {
+      fetch_pmax(p, pm);
+      stage_chunks(p.hin, p.K * 4, stage, kF32Units);
+    } else {
+      stage_chunks(p.x, p.K * 2, stage, kBfUnits);
+      if (p.gamma) stage_chunks(p.gamma, p.K * 2, stage_g, kBfUnits);
+    }
+    epoch = *p.epoch_in;
+  }
+  // #1: every row request of the workgroup precedes every weight request.  A plain
+  // barrier: a release fence here would also wait for the staged row to land.
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __asm__ __volatile__("" ::: "memory");
+
+  // ---- the weight stream.  The workgroup's whole tiles are flattened into W = nt * St K
+  // steps (tile-major); the stream waves take equal contiguous ranges of the first W - 4 cs
+  // steps, the control waves cs steps each of the rest once their prologue work is done.
+  // A wave keeps its INT32 sums in registers and adds them into the LDS accumulator of the
+  // K segment (a tile, or a tile's K partition) when its range leaves that segment
+  // (integer addition: exact in any order).  Loads run two batches of U steps ahead; they
+  // are unconditional (past the range's end a wave re-reads its last step), so the
+  // compiler's waits for one batch never cover the other.
+  const int32_t W = nt * St;
+  const int32_t cs = dg.ctl_steps < W / kDcCtl ? dg.ctl_steps : W / kDcCtl;
+  const int32_t Wst = W - kDcCtl * cs;
+  const int32_t ss = (Wst + kDcStream - 1) / kDcStream;
+  int32_t r0, rn;
+  if (wave >= kDcCtl) {
+    const int32_t sw = wave - kDcCtl;
+    r0 = sw * ss < Wst ? sw * ss : Wst;
+    rn = (r0 + ss < Wst ? r0 + ss : Wst) - r0;
+  } else {
+    r0 = Wst + wave * cs;
+    rn = cs;
+  }
+  const int32_t nb = (rn + U - 1) / U;
+  const int32_t rlast = rn > 0 ? r0 + rn - 1 : 0;
+  const bool aval = row16 < p.M;
+  const int64_t aoff = (aval ? row16 : 0) * act_ld + kg * 16;
+  const int64_t lane_off = (LAYOUT == LAYOUT_TILED) ? int64_t(lane) * 16
+                                                    : int64_t(row16) * p.K + kg * 16;
+  const int8_t* w0l = p.w0 + lane_off;
+  const int8_t* w1l = (NMAT == 2) ? p.w1 + lane_off : nullptr;
+  auto wofs = [&](int32_t f) -> int64_t {
+    if constexpr (LAYOUT == LAYOUT_TILED) return (int64_t(tb0) * St + f) * 1024;
+    const int32_t tl = f / St;
+    return (int64_t(tb0) + tl) * 16 * p.K + int64_t(f - tl * St) * 64;
+  };
+  auto load_batch = [&](i32x4 (&wv)[U][NMAT], int32_t i) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t f = r0 + i * U + u;
+      const int64_t o = wofs(f < rlast ? f : rlast);
+      wv[u][0] = ld16_stream(w0l + o);
+      if constexpr (NMAT == 2) wv[u][1] = ld16_stream(w1l + o);
+    }
+  };
+  // Step cursor (wave-uniform): next step, its segment, the segment's end, its K step.
+  int32_t cf = r0, csg = Ss > 0 ? r0 / Ss : 0, cend = (csg + 1) * Ss, ck = r0 % St;
+  const int32_t rend = r0 + rn;
+  i32x4 acc[NMAT];
+#pragma unroll
+  for (int i = 0; i < NMAT; ++i) acc[i] = i32x4{0, 0, 0, 0};
+  auto flush = [&]() {
+    int32_t* dst = accum + csg * kPart + lane * 4;
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        __hip_atomic_fetch_add(dst + i * kWave * 4 + c, acc[i][c], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i) acc[i] = i32x4{0, 0, 0, 0};
+  };
+  auto compute = [&](const i32x4 (&wv)[U][NMAT]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (cf < rend) {
+        if (cf == cend) {
+          flush();
+          ++csg;
+          cend += Ss;
+        }
+        if (ck == St) ck = 0;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ck) * 64);
+        const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NMAT; ++i) acc[i] = mfma_i8(wv[u][i], bv, acc[i]);
+        ++cf;
+        ++ck;
+      }
+    }
+  };
+  // Batches 0 and 1 are requested by the caller; this streams the rest and flushes.
+  auto stream_rest = [&](i32x4 (&wA)[U][NMAT], i32x4 (&wB)[U][NMAT]) {
+    int32_t i = 0;
+    for (; i + 3 < nb; i += 2) {
+      compute(wA);
+      __builtin_amdgcn_sched_barrier(0);
+      load_batch(wA, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wB);
+      __builtin_amdgcn_sched_barrier(0);
+      load_batch(wB, i + 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (nb - i == 3) {
+      compute(wA);
+      __builtin_amdgcn_sched_barrier(0);
+      load_batch(wA, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wB);
+      compute(wA);
+    } else {
+      compute(wA);
+      compute(wB);
+    }
+    if (rn > 0) flush();
+  };
+
+  if (wave >= kDcCtl) {
+    // ================================================================= stream waves
+    i32x4 wA[U][NMAT], wB[U][NMAT];
+    load_batch(wA, 0);
+    load_batch(wB, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();  // #2: the codes are in LDS and the accumulators are cleared
+    __builtin_amdgcn_sched_barrier(0);
+    stream_rest(wA, wB);
+  } else {
+    // ================================================================= control waves
+    int gen = 0;
+    wait_memory_done();   // this wave's staged chunks (and the partial maxima) have landed
+    ctl_sync(sm, gen);    // ... and every control wave's
+    if constexpr (kReq) {
+      ctl_requant_scales(p, sm, pm, taps, gen);
+      ctl_row_f32(p, sm, act, 0, stage, taps);
+      for (int m = 1; m < p.M; ++m) {
+        ctl_sync(sm, gen);  // row m - 1 read by every control wave
+        stage_chunks(p.hin + int64_t(m) * p.ldhin, p.K * 4, stage, kF32Units);
+        wait_memory_done();
+        ctl_sync(sm, gen);
+        ctl_row_f32(p, sm, act + m * act_ld, m, stage, taps);
+      }
+    } else {
+      ctl_row_bf16(p, sm, act, 0, stage, stage_g, taps, gen);
+      for (int m = 1; m < p.M; ++m) {
+        ctl_sync(sm, gen);
+        stage_chunks(p.x + int64_t(m) * p.ldx, p.K * 2, stage, kBfUnits);
+        wait_memory_done();
+        ctl_sync(sm, gen);
+        ctl_row_bf16(p, sm, act + m * act_ld, m, stage, stage_g, taps, gen);
+      }
+    }
+    // The staged row is dead once every control wave has read it: clear the accumulators.
+    ctl_sync(sm, gen);
+    for (int e = tid; e < nt * P * kPart / 4; e += kDcCtlThreads)
+      reinterpret_cast<i32x4*>(accum)[e] = i32x4{0, 0, 0, 0};
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();  // #2: codes, row scales and cleared accumulators ready
+
+    // Epilogue inputs of the workgroup's tiles (and of its leftover tile) into LDS: every
+    // load is issued before the first store, so they cost one memory round trip.
+    const int32_t lt = dg.leftover ? dg.grid * dg.whole_q + b / 4 : -1;
+    {
+      const int ct = tid;
+      constexpr int kSwN = (kDcMaxTiles + 1) * 16 * NMAT;                  // <= 192
+      constexpr int kResN = (kDcMaxTiles + 1) * kFuseMaxRows * 16;         // 384
+      constexpr int kResIt = (kResN + kDcCtlThreads - 1) / kDcCtlThreads;  // 2
+      float swv = 0.0f;
+      int32_t sw_t = -1;
+      int sw_slot = 0, sw_mat = 0, sw_c = 0;
+      if (ct < kSwN) {
+        sw_slot = ct / (16 * NMAT);
+        const int rem = ct % (16 * NMAT);
+        sw_mat = rem / 16;
+        sw_c = rem % 16;
+        sw_t = sw_slot < kDcMaxTiles ? (sw_slot < nt ? tb0 + sw_slot : -1) : lt;
+        if (sw_t >= 0) swv = (sw_mat == 0 ? p.sw0 : p.sw1)[int64_t(sw_t) * 16 + sw_c];
+      }
+      uint16_t rv[kResIt];
+      int32_t r_t[kResIt];
+      int r_slot[kResIt], r_m[kResIt], r_c[kResIt];
+#pragma unroll
+      for (int it = 0; it < kResIt; ++it) {
+        const int e = ct + it * kDcCtlThreads;
+        r_slot[it] = e / (kFuseMaxRows * 16);
+        const int rem = e % (kFuseMaxRows * 16);
+        r_m[it] = rem / 16;
+        r_c[it] = rem % 16;
+        r_t[it] = -1;
+        rv[it] = 0;
+        if constexpr (EPI == EPI_BF16_RES || EPI == EPI_DOWN) {
+          if (e < kResN && r_m[it] < p.M) {
+            r_t[it] = r_slot[it] < kDcMaxTiles ? (r_slot[it] < nt ? tb0 + r_slot[it] : -1) : lt;
+            if (r_t[it] >= 0) rv[it] = p.res[int64_t(r_m[it]) * p.ldr + int64_t(r_t[it]) * 16 + r_c[it]];
+          }
+        }
+      }
+      if (sw_t >= 0) sm.sw[sw_slot][sw_mat][sw_c] = swv;
+#pragma unroll
+      for (int it = 0; it < kResIt; ++it)
+        if (r_t[it] >= 0) sm.res[r_slot[it]][r_m[it]][r_c[it]] = rv[it];
+    }
+
+    if (dg.leftover) {
+      // A K quarter of tile lt, shared with the three neighbouring workgroups: the four
+      // control waves take a quarter of it each.
+      const int32_t Q = St / 4, qq = b & 3;
+      const int32_t cw = wave;
+      const int32_t ql = Q / kDcCtl, qr = Q % kDcCtl;
+      const int32_t s0 = qq * Q + cw * ql + (cw < qr ? cw : qr);
+      const int32_t s1 = s0 + ql + (cw < qr ? 1 : 0);
+      i32x4 lacc[NMAT];
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i) lacc[i] = i32x4{0, 0, 0, 0};
+      // All of the wave's steps in one batch (5 of Gate/Up, 17 of Down at Qwen3-14B).
+      constexpr int V = NMAT == 2 ? 8 : 20;
+      for (int32_t s = s0; s < s1; s += V) {
+        i32x4 wv[V][NMAT];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+          const int32_t sq = (s + u < s1) ? s + u : s1 - 1;
+          const int64_t o = (LAYOUT == LAYOUT_TILED) ? (int64_t(lt) * St + sq) * 1024
+                                                     : int64_t(lt) * 16 * p.K + int64_t(sq) * 64;
+          wv[u][0] = ld16_stream(p.w0 + lane_off + o);
+          if constexpr (NMAT == 2) wv[u][1] = ld16_stream(p.w1 + lane_off + o);
+        }
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+          if (s + u < s1) {
+            const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(s + u) * 64);
+            const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i) lacc[i] = mfma_i8(wv[u][i], bv, lacc[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i)
+        *reinterpret_cast<i32x4*>(lred + cw * kPart + (i * kWave + lane) * 4) = lacc[i];
+      // The last of the four control waves to finish adds their partials and publishes
+      // the quarter; the owner of quarter 0 then gathers the other three.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      int prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_fetch_add(&sm.lo_arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      if (prev == kDcCtl - 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        i32x4 piece[NMAT];
+#pragma unroll
+        for (int i = 0; i < NMAT; ++i) {
+          piece[i] = i32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int w = 0; w < kDcCtl; ++w)
+            piece[i] += *reinterpret_cast<const i32x4*>(lred + w * kPart + (i * kWave + lane) * 4);
+        }
+        const uint32_t tag32 = epoch ^ (uint32_t(EPI + 1) << 29);
+        uint64_t* slots = reinterpret_cast<uint64_t*>(p.slots);
+        if (qq != 0) {
+#pragma unroll
+          for (int i = 0; i < NMAT; ++i)
+            store_tagged(slots + (int64_t(b) * NMAT + i) * kSlotWords + lane * 4, piece[i], tag32);
+        } else {
+          // Gather quarters 1..3 (workgroups b + 1 .. b + 3); they are published early in
+          // those workgroups, so this usually succeeds at the first read.  The wait is
+          // bounded; past the bound the tile's output is left unwritten.
+          const int32_t qpp = Ss / Q;   // quarters per K partition
+          bool ok = false;
+          i32x4 got[3][NMAT];
+          for (int attempt = 0; attempt < (1 << 16) && !ok; ++attempt) {
+            bool all = true;
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+              for (int i = 0; i < NMAT; ++i) {
+                const TaggedX4 tw =
+                    load_tagged(slots + (int64_t(b + 1 + j) * NMAT + i) * kSlotWords + lane * 4);
+                got[j][i] = i32x4{0, 0, 0, 0};
+                add_tagged(got[j][i], tw, tag32, all);
+              }
+            ok = __builtin_amdgcn_ballot_w64(!all) == 0;
+            if (!ok) __builtin_amdgcn_s_sleep(8);
+          }
+          if (ok) {
+            // The tile's sums per K partition into LDS (the partials just read are dead):
+            // quarter j lies in partition j / qpp; quarter 0 is this workgroup's piece.
+            for (int q = 0; q < P; ++q)
+#pragma unroll
+              for (int i = 0; i < NMAT; ++i) {
+                i32x4 a = q == 0 ? piece[i] : i32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < 3; ++j) a += ((j + 1) / qpp == q) ? got[j][i] : i32x4{0, 0, 0, 0};
+                *reinterpret_cast<i32x4*>(lred + q * kPart + (i * kWave + lane) * 4) = a;
+              }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+            for (int32_t pq0 = 0; pq0 < p.M; pq0 += 4)
+              dc_epilogue<EPI, NMAT>(
+                  p, sm, static_cast<int32_t>(p.M), pq0 + lane / 16, P,
+                  [&](int32_t, int q, int mat, int64_t m, int n) {
+                    return acc_elem(lred + q * kPart, mat, m, n);
+                  },
+                  [&](int32_t) { return lt; }, [&](int32_t) { return kDcMaxTiles; });
+          }
+        }
+      }
+    }
+
+    // Then the control waves take their share of the weight stream.
+    if (rn > 0) {
+      i32x4 wA[U][NMAT], wB[U][NMAT];
+      load_batch(wA, 0);
+      load_batch(wB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_rest(wA, wB);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();  // #3: every range is added into its segments' accumulators
+
+  // ---- epilogue of the whole tiles, one (tile, row) pair per 16 lanes.
+  {
+    const int32_t npairs = nt * static_cast<int32_t>(p.M);
+    for (int32_t pq0 = wave * 4; pq0 < npairs; pq0 += kDcWaves * 4)
+      dc_epilogue<EPI, NMAT>(
+          p, sm, npairs, pq0 + lane / 16, P,
+          [&](int32_t j, int q, int mat, int64_t m, int n) {
+            return acc_elem(accum + (j * P + q) * kPart, mat, m, n);
+          },
+          [&](int32_t j) { return tb0 + j; }, [&](int32_t j) { return static_cast<int>(j); });
+  }
+  if (b == 0 && tid == 0) *p.epoch_out = epoch + 1;
+}
+
+template <int EPI, int NMAT, int LAYOUT>
+hipError_t launch_t(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
+  const auto kern = decode_kernel<EPI, NMAT, LAYOUT>;
+  if (g.lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, g.lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(g.grid)), dim3(kDcThreads),
+                     static_cast<size_t>(g.lds), s, a, g);
+  return hipGetLastError();
+}
+
+template <int EPI, int NMAT>
+hipError_t launch_l(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
+  if (a.layout == LAYOUT_TILED) return launch_t<EPI, NMAT, LAYOUT_TILED>(a, g, s);
+  return launch_t<EPI, NMAT, LAYOUT_ROWMAJOR>(a, g, s);
+}
+
+}  // namespace
+
+#ifndef A8W8_DC_CTL_SHARE
+#define A8W8_DC_CTL_SHARE 0, 0, 0, 0
+#endif
+// Control-wave share of the stream per epilogue kind (BF16, BF16 + residual, SiLU, Down),
+// in sixteenths of a stream wave's.
+constexpr int kCtlShare16[4] = {A8W8_DC_CTL_SHARE};
+
+bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom& g) {
+  g = DecodeGeom{};
+  if (M < 1 || M > kFuseMaxRows || N % 16 || K % 64 || N <= 0) return false;
+  const int nmat = epi == EPI_SILU ? 2 : 1;
+  const int P = epi == EPI_DOWN ? parts : 1;
+  const int64_t T = N / 16, St = K / 64;
+  if (St % P) return false;
+  const int64_t Ss = St / P;
+  if (P > 8) return false;
+  // Prologue registers: the control waves hold a whole input row.
+  if (epi == EPI_DOWN ? K > kF32MaxK : K > kBfMaxK) return false;
+  if (T >= (int64_t(1) << 24) || St >= (int64_t(1) << 20)) return false;
+  const int64_t G = T < kDcMaxGrid ? T : kDcMaxGrid;
+  const int64_t q = T / G, r = T % G;
+  // Leftover quarters: the last G/4 tiles are split in K quarters, one per workgroup,
+  // each inside one K partition.
+  const bool left = r != 0 && G % 4 == 0 && 4 * r == G && St % 4 == 0 && (St / 4) % kDcCtl == 0 &&
+                    Ss % (St / 4) == 0 && P <= kDcCtl;
+  const int64_t ntmax = left ? q : q + (r ? 1 : 0);
+  if (ntmax > kDcMaxTiles) return false;
+  g.tiles = static_cast<int32_t>(T);
+  g.steps_tile = static_cast<int32_t>(St);
+  g.steps_seg = static_cast<int32_t>(Ss);
+  g.grid = static_cast<int32_t>(G);
+  g.whole_q = static_cast<int32_t>(q);
+  g.whole_r = static_cast<int32_t>(left ? 0 : r);
+  g.leftover = left ? 1 : 0;
+  g.act_ld = static_cast<int32_t>(K);
+  // Steps per control wave: the control waves may join the stream after their prologue
+  // (and leftover quarter) with a share weighted kCtlShare / 16 of a stream wave's.  On
+  // MI355X at Qwen3-14B shapes every nonzero weight measured slower (the stream waves
+  // already keep the CU's memory pipeline full), so the default is none.
+  const int64_t W = ntmax * St;
+  const int64_t wq = kCtlShare16[epi];
+  g.ctl_steps = static_cast<int32_t>(W * wq / (16 * kDcStream + kDcCtl * wq));
+  const size_t codes = (size_t(M) * size_t(K) + 255) / 256 * 256;
+  const size_t part = size_t(nmat) * 4 * kWave * 4;   // bytes of one segment's sums
+  g.acc_off = static_cast<int32_t>(codes);
+  g.lred_off = static_cast<int32_t>(codes + size_t(ntmax) * P * part);
+  // Staging of the input row at acc_off: FP32 h (Down) or BF16 x followed by the gain.
+  const size_t unit_bytes = size_t(kDcCtlThreads) * 16;
+  const size_t stage = epi == EPI_DOWN ? kF32Units * unit_bytes : 2 * kBfUnits * unit_bytes;
+  g.stage_g = static_cast<int32_t>(kBfUnits * unit_bytes);
+  size_t lds = size_t(g.lred_off) + size_t(kDcCtl) * part;
+  if (codes + stage > lds) lds = codes + stage;
+  if (lds > kDcMaxLds) return false;
+  g.lds = static_cast<int32_t>(lds);
+  return true;
+}
+
+size_t decode_slot_elems(const DecodeGeom& g, int nmat) {
+  // One tagged 64-bit word (two INT32 elements) per partial sum of each published quarter.
+  return g.leftover ? 2 * size_t(g.grid) * size_t(nmat) * kSlotWords : 0;
+}
+
+hipError_t launch_decode(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  switch (a.epi) {
+    case EPI_BF16: return launch_l<EPI_BF16, 1>(a, g, s);
+    case EPI_BF16_RES: return launch_l<EPI_BF16_RES, 1>(a, g, s);
+    case EPI_SILU: return launch_l<EPI_SILU, 2>(a, g, s);
+    case EPI_DOWN: return launch_l<EPI_DOWN, 1>(a, g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace a8w8

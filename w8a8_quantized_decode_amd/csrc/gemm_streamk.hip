@@ -214,7 +214,7 @@ __device__ void sk_prologue(const StreamKArgs& p, SM& sm, int8_t* act, int64_t a
 // Row 0's first partial maxima and values are fetched before any weight load
 // (RequantRegs), so the wait for them never covers weight loads; the rest is loaded here.
 constexpr int kReqPm = 3;  // partial maxima of row 0 per thread fetched ahead
-constexpr int kReqHv = 3;  // 8-value groups of row 0 per thread fetched ahead
+constexpr int kReqHv = 5;  // 8-value groups of row 0 per thread fetched ahead (17408 values)
 
 struct RequantRegs {
   float pm[kReqPm];
@@ -300,7 +300,10 @@ template <int EPI, int NMAT, int NW, int MB, int LAYOUT, int PRO>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4)))
 void streamk_kernel(StreamKArgs p) {
   constexpr bool kFused = PRO != PRO_CODES;
-  constexpr int kU0 = kFused ? (NMAT == 2 ? 4 : 6) : 4 / (NMAT * MB);
+  // QKV and O (BF16 prologue, one weight) issue both batches before the prologue: five
+  // steps each cover a wave's ten steps of a 5120-deep tile split over eight waves.
+  constexpr bool kEarlyB = PRO == PRO_QUANT_BF16 && NMAT == 1;
+  constexpr int kU0 = kFused ? (NMAT == 2 ? 4 : (kEarlyB ? 5 : 6)) : 4 / (NMAT * MB);
   constexpr int U = kU0 > 0 ? kU0 : 1;         // k steps per load batch
   constexpr int kSlot = NMAT * MB * 4 * kWave;  // tagged 64-bit words per slot
   constexpr int kGroup = 4 / (NMAT * MB) > 0 ? 4 / (NMAT * MB) : 1;  // pieces per round trip
@@ -308,9 +311,6 @@ void streamk_kernel(StreamKArgs p) {
   extern __shared__ __align__(16) int8_t act[];
 
   const int tid = threadIdx.x;
-  // This GEMM's tag; the next GEMM on the workspace reads the advanced value.
-  const uint32_t epoch = *p.epoch_in;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *p.epoch_out = epoch + 1;
   // The wave index lives in a scalar register so that every branch around a matrix
   // instruction is wave-uniform (a matrix instruction ignores a partial lane mask).
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -378,7 +378,6 @@ void streamk_kernel(StreamKArgs p) {
         resp[mb] = *reinterpret_cast<const u32x2*>(p.res + (aval[mb] ? em : 0) * p.ldr + en);
     }
   };
-  fetch_epilogue_inputs(sg0 <= sB ? sg0 : sA);
 
   // The range [f0, f1) covers at most two segments (the planner deals at least one
   // wave per segment): steps f < fx belong to segment segA, the others to segA + 1.
@@ -471,30 +470,39 @@ void streamk_kernel(StreamKArgs p) {
 
   i32x4 wA[U][NMAT], bA[U][MB], wB[U][NMAT], bB[U][MB];
   const int32_t nb = (flive - f0 + U - 1) / U;
-  // Row 0 of the prologue's input is fetched first, then one weight batch, which is in
-  // flight while the prologue runs (its waits then cover no weight load); the second
-  // batch is issued right after it.  All unconditionally: a guard here would let the
-  // compiler assume the batches may arrive out of order.
+  // Issue order, all unconditional (a guard here would let the compiler assume the
+  // loads may arrive out of order, and its waits would then cover later batches):
+  //  1. row 0 of the prologue's input: requested before any weight, so the prologue's
+  //     waits cover no weight load and the row is not queued behind the weight stream;
+  //  2. the first weight batch (both batches for QKV and O, whose whole per-wave range
+  //     then is in flight during the prologue);
+  //  3. the call's tag and the epilogue inputs (channel scales, residual), which are
+  //     used only after the stream;
+  //  4. the prologue itself, then the second batch.
   const bool taps = blockIdx.x == 0;
-  if constexpr (PRO == PRO_REQUANT_F32) {
-    RequantRegs rq;
-    sk_requant_fetch<NW>(p, klo, alen, rq);
-    __builtin_amdgcn_sched_barrier(0);
-    load_batch(wA, bA);
-    __builtin_amdgcn_sched_barrier(0);
-    sk_requant_prologue<NW>(p, sm, act, act_ld, klo, alen, taps, rq);
-    if (taps && p.tap_q) sk_requant_taps<NW>(p, sm.row_scale);
-    __builtin_amdgcn_sched_barrier(0);
-    load_batch(wB, bB);
-  }
+  RequantRegs rq;
   PrologueRegs pre;
+  if constexpr (PRO == PRO_REQUANT_F32) sk_requant_fetch<NW>(p, klo, alen, rq);
   if constexpr (PRO == PRO_QUANT_BF16) sk_prologue_fetch<NW, PRO>(p, klo, alen, pre);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (PRO != PRO_REQUANT_F32) load_batch(wA, bA);
+  load_batch(wA, bA);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kEarlyB) {
+    load_batch(wB, bB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // This GEMM's tag; the next GEMM on the workspace reads the advanced value (written
+  // after the stream by workgroup (0, 0)).
+  const uint32_t epoch = *p.epoch_in;
+  fetch_epilogue_inputs(sg0 <= sB ? sg0 : sA);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (PRO == PRO_REQUANT_F32) {
+    sk_requant_prologue<NW>(p, sm, act, act_ld, klo, alen, taps, rq);
+    if (taps && p.tap_q) sk_requant_taps<NW>(p, sm.row_scale);
+  }
   if constexpr (PRO == PRO_QUANT_BF16) sk_prologue<NW, PRO>(p, sm, act, act_ld, klo, alen, taps, pre);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (PRO != PRO_REQUANT_F32) load_batch(wB, bB);
+  if constexpr (!kEarlyB) load_batch(wB, bB);
   __builtin_amdgcn_sched_barrier(0);
   // Pairs of batches with no branch inside the body (a branch would let the compiler
   // sink the next batch's loads behind the other batch's compute) and scheduling
@@ -528,6 +536,8 @@ void streamk_kernel(StreamKArgs p) {
   } else if (bi < nb) {
     compute(wA, bA);
   }
+
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *p.epoch_out = epoch + 1;
 
   // Workgroup combine.  Each wave leaves the partial sums of its (at most two) segments
   // in LDS; after one barrier the workgroup's segments are dealt to its waves, and a
@@ -950,11 +960,18 @@ StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bo
   // Tagged slots: one 64-bit word (two INT32 elements) per partial sum.
   pl.slot_elems = 2 * size_t(pl.mgroups) * size_t(T * C + wgs) * size_t(nmat) * pl.mb * 4 * kWave;
   pl.done_elems = size_t(pl.mgroups) * size_t(T);
+  // Fused prologues at shapes the one-workgroup-per-CU kernel covers run on it.
+  if (fused && plan_decode(epi, M, N, K, P, pl.dec)) {
+    pl.use_decode = 1;
+    const size_t se = decode_slot_elems(pl.dec, nmat);
+    if (se > pl.slot_elems) pl.slot_elems = se;
+  }
   return pl;
 }
 
 bool streamk_fusable(const StreamKPlan& pl, int64_t M, int64_t K_in, bool bf16_rows) {
   if (M > kFuseMaxRows) return false;
+  if (pl.use_decode) return true;
   if (pl.lds > kSkMaxLds) return false;
   // The BF16 prologue holds its rows in registers; the requantization one does not.
   return !bf16_rows || K_in <= kPrologueMax;
@@ -962,6 +979,7 @@ bool streamk_fusable(const StreamKPlan& pl, int64_t M, int64_t K_in, bool bf16_r
 
 hipError_t launch_streamk(const StreamKArgs& a_in, const StreamKPlan& pl, hipStream_t stream) {
   if (a_in.M == 0) return hipSuccess;
+  if (pl.use_decode) return launch_decode(a_in, pl.dec, stream);
   StreamKArgs a = a_in;
   a.red_off = static_cast<int64_t>(pl.red_off);
   switch (a.epi) {

@@ -167,7 +167,26 @@ struct StreamKArgs {
   float* tap_s;             // fused prologue: [M] row scales
 };
 
+// Decode GEMM with one 16-wave workgroup per CU and whole tiles per workgroup
+// (gemm_decode.hip), used for fused-prologue shapes it covers.
+struct DecodeGeom {
+  int32_t tiles, steps_tile, steps_seg, grid;
+  int32_t whole_q, whole_r;  // workgroup b: q (+1 if b < r) whole tiles from b*q + min(b, r)
+  int32_t leftover;          // 1: tiles grid*q .. grid*q + grid/4 - 1 are cut in K quarters,
+                             // quarter b % 4 of tile grid*q + b/4 computed by workgroup b
+  int32_t act_ld;            // bytes of codes per row in LDS (= K)
+  int32_t acc_off, lred_off; // LDS offsets of the segment accumulators and the control waves' partials
+  int32_t stage_g;           // offset of the staged RMSNorm gain from acc_off (the staging area)
+  int32_t ctl_steps;         // K steps of the stream taken by each control wave
+  int32_t lds;               // dynamic LDS bytes
+};
+// False when the shape is not covered (then the stream-K kernel runs).
+bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom& g);
+size_t decode_slot_elems(const DecodeGeom& g, int nmat);
+
 struct StreamKPlan {
+  int use_decode;      // 1: launch the decode kernel of gemm_decode.hip with `dec`
+  DecodeGeom dec;
   int waves;           // waves per workgroup
   int wgs;             // grid.x: workgroups per 64-row group
   int mgroups;         // grid.y
@@ -186,6 +205,7 @@ StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bo
 // length a BF16 prologue normalizes (bf16_rows), else the requantized row.
 bool streamk_fusable(const StreamKPlan& pl, int64_t M, int64_t K_in, bool bf16_rows);
 hipError_t launch_streamk(const StreamKArgs& a, const StreamKPlan& pl, hipStream_t stream);
+hipError_t launch_decode(const StreamKArgs& a, const DecodeGeom& g, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill GEMM
 // W8A16 GEMM over tiles of 256 rows x 64 (Gate/Up: 64 Gate + the same 64 Up channels)
