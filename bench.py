@@ -31,7 +31,7 @@ METRIC = "µs/layer and INT8-weight HBM GB/s (% of peak), A8W8 decode linears at
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 GATEUP_KERNEL = 5     # kernel number of the Gate/Up GEMM inside a8w8_layer_linears
-GATEUP_NAME = "streamk_kernel<2, 2,"       # its symbol in rocprofv3 counter tables
+GATEUP_NAME = "decode_kernel<2, 2,"        # its symbol in rocprofv3 counter tables
 PACK_NAME = "pack_tiled_kernel"            # plain permuting copy: the counter calibration
 PMC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_pmc.json")
 PMC_MD = os.path.join(ROOT, "profiles", "layer_linears_m1_pmc.md")
@@ -69,7 +69,7 @@ def parse():
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemm_streamk.hip", "device_common.h", "internal.h"):
+    for f in ("gemm_decode.hip", "gemm_streamk.hip", "device_common.h", "internal.h"):
         with open(os.path.join(ROOT, "w8a8_quantized_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -731,7 +731,7 @@ def main():
     traffic = measured_traffic(gu_bytes)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "streamk_kernel<EPI_SILU> (Gate/Up)", "kernel_us": round(k_ms * 1e3, 2),
+            "kernel": "decode_kernel<EPI_SILU> (Gate/Up)", "kernel_us": round(k_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": gu_bytes}
 
     cpu = None

@@ -52,6 +52,11 @@ constexpr int64_t kBfMaxK = int64_t(kBfUnits) * 8 * kDcCtlThreads;   // 6144
 constexpr int64_t kF32MaxK = int64_t(kF32Units) * 4 * kDcCtlThreads; // 18432
 constexpr int kSlotWords = 4 * kWave;            // tagged 64-bit words per matrix per piece
 constexpr size_t kDcMaxLds = 150 * 1024;
+// Leftover-quarter steps a control wave requests before its prologue and holds in
+// registers meanwhile (the rest of its share follows after the prologue), sized within
+// the register budget of a 1024-thread workgroup: Qwen3-14B has 5 steps per control wave
+// (K = 5120) and 17 for Down (K = 17408).
+constexpr int lo_steps(int epi) { return epi == EPI_DOWN ? 12 : (epi == EPI_SILU ? 5 : 8); }
 
 struct DcSmem {
   double sum_slot[kFuseMaxRows][kDcCtl];
@@ -59,26 +64,57 @@ struct DcSmem {
   float row_scale[kFuseMaxRows];
   int ctl_sync;        // control-wave barrier counter
   int lo_arrive;       // control waves done with their share of the leftover quarter
+  int pf_done;         // control waves done storing the epilogue inputs
+  int codes_ready;     // set by the control waves once the codes are in LDS
   float sw[kDcMaxTiles + 1][2][16];                 // channel scales (slot kDcMaxTiles: leftover)
   uint16_t res[kDcMaxTiles + 1][kFuseMaxRows][16];  // residual
 };
+
+// LDS hand-offs between waves that may have global loads in flight.  The workgroup-scope
+// fences and atomic loads of the memory model also wait for every outstanding global load
+// (vmcnt(0)), which would drain a wave's weight stream or its early leftover loads.  The
+// LDS operations of one wave execute in order, so waiting for this wave's LDS operations
+// (lgkmcnt(0)) before raising a flag is the whole release, and a volatile read through an
+// LDS pointer followed by a compiler barrier is the whole acquire.
+__device__ __forceinline__ void lds_release_only() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __asm__ __volatile__("" ::: "memory");
+}
+__device__ __forceinline__ void lds_wait_flag(int* flag, int at_least) {
+  const volatile __attribute__((address_space(3))) int* f =
+      (const volatile __attribute__((address_space(3))) int*)(flag);
+  while (*f < at_least) __builtin_amdgcn_s_sleep(1);
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Adds to an LDS counter (waiting for the add to complete) and stores an LDS flag, both
+// out of sight of the compiler's memory-counter tracking, which would otherwise place a
+// vmcnt(0) before them while the control waves' early leftover loads are in flight.
+__device__ __forceinline__ uint32_t lds_addr(int* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)(p)));
+}
+__device__ __forceinline__ void lds_add_sync(int* p, int v) {
+  __asm__ __volatile__("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_set_flag(int* p, int v) {
+  __asm__ __volatile__("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
 
 // Barrier of the four control waves only (the stream waves are in their loop): an LDS
 // counter that every control wave advances once per use; waits until all have.
 __device__ __forceinline__ void ctl_sync(DcSmem& sm, int& gen) {
   gen += kDcCtl;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  if ((threadIdx.x & (kWave - 1)) == 0)
-    __hip_atomic_fetch_add(&sm.ctl_sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  while (__hip_atomic_load(&sm.ctl_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < gen)
-    __builtin_amdgcn_s_sleep(1);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  lds_release_only();
+  if ((threadIdx.x & (kWave - 1)) == 0) lds_add_sync(&sm.ctl_sync, 1);
+  lds_wait_flag(&sm.ctl_sync, gen);
 }
 
-// INT8 codes clamp(rint(v / s), -127, 127) of N values, s > 0, with the correctly rounded
-// quotient computed only where it can matter.  rs = fl32(1/s) and t = fl32(v * rs) carry
-// two roundings, a relative error of at most 2^-23, so |t - v/s| <= |t| * 2^-22.9 and
-// fl32(v/s) lies within |t| * 2^-24 of v/s.  If t is farther than |t| * 2^-21 from the
+// INT8 codes clamp(rint(v / s), -127, 127) of N values, s > 0, |v| <= 127 s (s is the
+// row's absolute maximum over 127), with the correctly rounded quotient computed only
+// where it can matter.  rs = fl32(1/s) and t = fl32(v * rs) carry two roundings, a
+// relative error of at most 2^-23, so |t - v/s| <= |t| * 2^-22.9 and fl32(v/s) lies within
+// |t| * 2^-24 of v/s.  |t| < 128, so if t is farther than 2^-14 (> |t| * 2^-21) from the
 // midpoint n + 1/2 of its neighbours, fl32(v/s) rounds to the same integer as t and is no
 // tie.  Otherwise (or when t is not finite: s subnormal) the exact quotient decides; that
 // path runs only when some lane of the wave needs it.
@@ -90,15 +126,13 @@ __device__ __forceinline__ void quant_codes(const float (&v)[N], float s, float 
   for (int i = 0; i < N; ++i) {
     const float t = v[i] * rs;
     qf[i] = rintf(t);
-    const float d = fabsf(t - qf[i]);
-    need = need || !(d < 0.5f - fabsf(t) * 4.76837158203125e-7f);
+    need = need || !(fabsf(t - qf[i]) < 0.5f - 6.103515625e-5f);
   }
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const float t = v[i] * rs;
-      const float d = fabsf(t - rintf(t));
-      if (!(d < 0.5f - fabsf(t) * 4.76837158203125e-7f)) qf[i] = rintf(v[i] / s);
+      if (!(fabsf(t - rintf(t)) < 0.5f - 6.103515625e-5f)) qf[i] = rintf(v[i] / s);
     }
   }
 #pragma unroll
@@ -180,11 +214,14 @@ __device__ __forceinline__ double wave_sum_dpp(double v) {
 // global-to-LDS loads take no registers), in 16-byte chunks: chunk c = u * 256 + ct of
 // control thread ct lands at stage + 16 * c.  The staging area overlaps the partial-sum
 // areas, which are used only after the prologue.
-__device__ __forceinline__ void stage_chunks(const void* src, int64_t nbytes, int8_t* stage,
-                                             int units) {
-  const int ct = threadIdx.x, w = ct / kWave, l = ct & (kWave - 1);
+template <int UNITS>
+__device__ __forceinline__ void stage_chunks(const void* src, int64_t nbytes, int8_t* stage) {
+  // Unrolled, so the compiler counts these loads exactly when it places waits for loads
+  // issued before them.
+  const int ct = threadIdx.x, w = ct / kWave;
   const int8_t* s8 = static_cast<const int8_t*>(src);
-  for (int u = 0; u < units; ++u) {
+#pragma unroll
+  for (int u = 0; u < UNITS; ++u) {
     const int64_t c = int64_t(u) * kDcCtlThreads + ct;
     const int64_t off = c * 16 < nbytes ? c * 16 : 0;   // chunks past the row re-read chunk 0
     // Lane l of the wave writes stage + 16 * (u * 256 + 64 * w + l).
@@ -192,15 +229,12 @@ __device__ __forceinline__ void stage_chunks(const void* src, int64_t nbytes, in
                                      reinterpret_cast<__shared__ uint32_t*>(
                                          stage + (int64_t(u) * kDcCtlThreads + w * kWave) * 16),
                                      16, 0, 0);
-    (void)l;
   }
 }
 
 // RMSNorm (when gamma) and quantization of one BF16 row staged at xs (and the gain at gs)
 // into codes act[0..K), scale into sm.row_scale[m]; taps (xn, q, s) when requested.
-// Values k = u * 2048 + ct * 8 + i.  The passes are loops that re-read the staged row from
-// LDS: this code runs once per workgroup at the start of the kernel, when every line of it
-// is fetched into the instruction cache behind the weight stream, so it is kept short.
+// Values k = u * 2048 + ct * 8 + i; each pass re-reads the staged row from LDS.
 __device__ __forceinline__ void bf_vals(const int8_t* xs, int u, int ct, int64_t K, float (&v)[8]) {
   const bool in = int64_t(u) * 8 * kDcCtlThreads + ct * 8 < K;
   const u32x4 xr = *reinterpret_cast<const u32x4*>(xs + (int64_t(u) * kDcCtlThreads + ct) * 16);
@@ -221,7 +255,7 @@ __device__ void ctl_row_bf16(const StreamKArgs& p, DcSmem& sm, int8_t* act, int 
     // multiply-add rounds exactly as the product followed by the sum.  Then
     // r = 1 / sqrt(fl32(S / K) + eps) with correctly rounded steps.
     double ss = 0.0;
-#pragma unroll 1
+#pragma unroll
     for (int u = 0; u < kBfUnits; ++u) {
       float v[8];
       bf_vals(xs, u, ct, K, v);
@@ -250,7 +284,7 @@ __device__ void ctl_row_bf16(const StreamKArgs& p, DcSmem& sm, int8_t* act, int 
     }
   };
   float amax = 0.0f;
-#pragma unroll 1
+#pragma unroll
   for (int u = 0; u < kBfUnits; ++u) {
     float v[8];
     norm(u, v);
@@ -267,7 +301,7 @@ __device__ void ctl_row_bf16(const StreamKArgs& p, DcSmem& sm, int8_t* act, int 
   const float rs = 1.0f / s;
   if (ct == 0) sm.row_scale[m] = s;
   if (taps && ct == 0 && p.tap_s) p.tap_s[m] = s;
-#pragma unroll 1
+#pragma unroll
   for (int u = 0; u < kBfUnits; ++u) {
     const int64_t k = int64_t(u) * 8 * kDcCtlThreads + ct * 8;
     if (k < K) {
@@ -305,29 +339,32 @@ __device__ __forceinline__ void fetch_pmax(const StreamKArgs& p, PmRegs& r) {
 __device__ void ctl_requant_scales(const StreamKArgs& p, DcSmem& sm, const PmRegs& r, bool taps,
                                    int& gen) {
   const int ct = threadIdx.x, wave = ct / kWave;
-  const int64_t n = p.npmax * p.M;
+  // Word e of the [npmax, M] table belongs to row e % M (32-bit: npmax * M < 2^26).
+  const uint32_t n = static_cast<uint32_t>(p.npmax * p.M), Mu = static_cast<uint32_t>(p.M);
   float mx[kFuseMaxRows];
 #pragma unroll
   for (int m = 0; m < kFuseMaxRows; ++m) mx[m] = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kPmUnits; ++u)
+  for (int u = 0; u < kPmUnits; ++u) {
+    const uint32_t e0 = uint32_t(u) * 4 * kDcCtlThreads + uint32_t(ct) * 4;
+    uint32_t m = e0 % Mu;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t e = int64_t(u) * 4 * kDcCtlThreads + ct * 4 + i;
-      if (e < n) {
-        const int m = static_cast<int>(e % p.M);
+      if (e0 + i < n) {
 #pragma unroll
         for (int mm = 0; mm < kFuseMaxRows; ++mm)
-          if (mm == m) mx[mm] = fmaxf(mx[mm], r.v[u][i]);
+          if (uint32_t(mm) == m) mx[mm] = fmaxf(mx[mm], r.v[u][i]);
       }
+      m = m + 1 == Mu ? 0 : m + 1;
     }
+  }
   // partial maxima beyond the prefetched words (npmax * M > 2048)
-  for (int64_t e = int64_t(kPmUnits) * 4 * kDcCtlThreads + ct; e < n; e += kDcCtlThreads) {
-    const int m = static_cast<int>(e % p.M);
+  for (uint32_t e = uint32_t(kPmUnits) * 4 * kDcCtlThreads + ct; e < n; e += kDcCtlThreads) {
+    const uint32_t m = e % Mu;
     const float v = p.pmax[e];
 #pragma unroll
     for (int mm = 0; mm < kFuseMaxRows; ++mm)
-      if (mm == m) mx[mm] = fmaxf(mx[mm], v);
+      if (uint32_t(mm) == m) mx[mm] = fmaxf(mx[mm], v);
   }
 #pragma unroll
   for (int m = 0; m < kFuseMaxRows; ++m) {
@@ -352,12 +389,14 @@ __device__ void ctl_row_f32(const StreamKArgs& p, const DcSmem& sm, int8_t* act,
   const int ct = threadIdx.x;
   const float s = sm.row_scale[m];
   const float rs = 1.0f / s;
-#pragma unroll 1
+  // Unrolled by three so that the LDS reads of a group overlap; every unit of the staging
+  // area is in bounds (units past the row hold re-read data and are not stored).
+#pragma unroll 3
   for (int u = 0; u < kF32Units; ++u) {
     const int64_t k = int64_t(u) * 4 * kDcCtlThreads + ct * 4;
+    const f32x4 h = *reinterpret_cast<const f32x4*>(hs + (int64_t(u) * kDcCtlThreads + ct) * 16);
+    const uint32_t c = codes4_fast(h, s, rs);
     if (k < p.K) {
-      const f32x4 h = *reinterpret_cast<const f32x4*>(hs + (int64_t(u) * kDcCtlThreads + ct) * 16);
-      const uint32_t c = codes4_fast(h, s, rs);
       *reinterpret_cast<uint32_t*>(act + k) = c;
       if (taps && p.tap_q) *reinterpret_cast<uint32_t*>(p.tap_q + int64_t(m) * p.K + k) = c;
     }
@@ -460,6 +499,8 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   if (tid == 0) {
     sm.ctl_sync = 0;
     sm.lo_arrive = 0;
+    sm.pf_done = 0;
+    sm.codes_ready = 0;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the counters are set before barrier #1
   }
 
@@ -471,10 +512,10 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   if (wave < kDcCtl) {
     if constexpr (kReq) {
       fetch_pmax(p, pm);
-      stage_chunks(p.hin, p.K * 4, stage, kF32Units);
+      stage_chunks<kF32Units>(p.hin, p.K * 4, stage);
     } else {
-      stage_chunks(p.x, p.K * 2, stage, kBfUnits);
-      if (p.gamma) stage_chunks(p.gamma, p.K * 2, stage_g, kBfUnits);
+      stage_chunks<kBfUnits>(p.x, p.K * 2, stage);
+      if (p.gamma) stage_chunks<kBfUnits>(p.gamma, p.K * 2, stage_g);
     }
     epoch = *p.epoch_in;
   }
@@ -487,25 +528,21 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   __asm__ __volatile__("" ::: "memory");
 
   // ---- the weight stream.  The workgroup's whole tiles are flattened into W = nt * St K
-  // steps (tile-major); the stream waves take equal contiguous ranges of the first W - 4 cs
-  // steps, the control waves cs steps each of the rest once their prologue work is done.
-  // A wave keeps its INT32 sums in registers and adds them into the LDS accumulator of the
+  // steps (tile-major); the stream waves take equal contiguous ranges of them.  (Measured
+  // on MI355X at Qwen3-14B shapes: letting the control waves take a share once their
+  // prologue work is done was slower at every size tried; the stream waves already keep
+  // the CU's memory pipeline full.)  A wave keeps its INT32 sums in registers and adds them into the LDS accumulator of the
   // K segment (a tile, or a tile's K partition) when its range leaves that segment
   // (integer addition: exact in any order).  Loads run two batches of U steps ahead; they
   // are unconditional (past the range's end a wave re-reads its last step), so the
   // compiler's waits for one batch never cover the other.
   const int32_t W = nt * St;
-  const int32_t cs = dg.ctl_steps < W / kDcCtl ? dg.ctl_steps : W / kDcCtl;
-  const int32_t Wst = W - kDcCtl * cs;
-  const int32_t ss = (Wst + kDcStream - 1) / kDcStream;
-  int32_t r0, rn;
+  const int32_t ss = (W + kDcStream - 1) / kDcStream;
+  int32_t r0 = 0, rn = 0;
   if (wave >= kDcCtl) {
     const int32_t sw = wave - kDcCtl;
-    r0 = sw * ss < Wst ? sw * ss : Wst;
-    rn = (r0 + ss < Wst ? r0 + ss : Wst) - r0;
-  } else {
-    r0 = Wst + wave * cs;
-    rn = cs;
+    r0 = sw * ss < W ? sw * ss : W;
+    rn = (r0 + ss < W ? r0 + ss : W) - r0;
   }
   const int32_t nb = (rn + U - 1) / U;
   const int32_t rlast = rn > 0 ? r0 + rn - 1 : 0;
@@ -598,20 +635,55 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     load_batch(wA, 0);
     load_batch(wB, 1);
     __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();  // #2: the codes are in LDS and the accumulators are cleared
+    lds_wait_flag(&sm.codes_ready, 1);   // the codes are in LDS, the accumulators cleared
     __builtin_amdgcn_sched_barrier(0);
     stream_rest(wA, wB);
   } else {
     // ================================================================= control waves
+    // The leftover quarter's weights are requested right behind the row: the control waves
+    // are the oldest of the workgroup, so these loads are queued ahead of most of the
+    // stream and have landed by the time the codes are ready.  Each control wave takes a
+    // quarter of the quarter; the first V steps of it are requested here.
+    constexpr int V = lo_steps(EPI);
+    const int32_t Q = St / 4, qq = b & 3;
+    const int32_t lt = dg.leftover ? dg.grid * dg.whole_q + b / 4 : -1;
+    const int32_t ql = Q / kDcCtl, qr = Q % kDcCtl;
+    const int32_t ls0 = qq * Q + wave * ql + (wave < qr ? wave : qr);
+    const int32_t ls1 = ls0 + ql + (wave < qr ? 1 : 0);
+    i32x4 lw[V][NMAT];
+    auto load_lo = [&](int32_t s0) {
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const int32_t sq = (s0 + u < ls1) ? s0 + u : ls1 - 1;
+        const int64_t o = (LAYOUT == LAYOUT_TILED) ? (int64_t(lt) * St + sq) * 1024
+                                                   : int64_t(lt) * 16 * p.K + int64_t(sq) * 64;
+        lw[u][0] = ld16_stream(w0l + o);
+        if constexpr (NMAT == 2) lw[u][1] = ld16_stream(w1l + o);
+      }
+    };
+    // (Down: after the row scales, which need the partial maxima loaded before the row: the
+    // compiler's waits for those would otherwise also cover these loads.)
+    if (!kReq && dg.leftover) {
+      load_lo(ls0);
+      __builtin_amdgcn_sched_barrier(0);
+      // The row (requested before these V * NMAT loads, which complete in order) has landed.
+      __asm__ __volatile__("" ::: "memory");
+      constexpr int kAfter = V * NMAT;   // vmcnt(kAfter); expcnt and lgkmcnt unconstrained
+      __builtin_amdgcn_s_waitcnt((kAfter & 0xF) | 0x0F70 | ((kAfter >> 4) << 14));
+      __asm__ __volatile__("" ::: "memory");
+    } else {
+      wait_memory_done();   // this wave's staged chunks (and the partial maxima) have landed
+    }
     int gen = 0;
-    wait_memory_done();   // this wave's staged chunks (and the partial maxima) have landed
     ctl_sync(sm, gen);    // ... and every control wave's
     if constexpr (kReq) {
       ctl_requant_scales(p, sm, pm, taps, gen);
+      if (dg.leftover) load_lo(ls0);
+      __builtin_amdgcn_sched_barrier(0);
       ctl_row_f32(p, sm, act, 0, stage, taps);
       for (int m = 1; m < p.M; ++m) {
         ctl_sync(sm, gen);  // row m - 1 read by every control wave
-        stage_chunks(p.hin + int64_t(m) * p.ldhin, p.K * 4, stage, kF32Units);
+        stage_chunks<kF32Units>(p.hin + int64_t(m) * p.ldhin, p.K * 4, stage);
         wait_memory_done();
         ctl_sync(sm, gen);
         ctl_row_f32(p, sm, act + m * act_ld, m, stage, taps);
@@ -620,174 +692,154 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
       ctl_row_bf16(p, sm, act, 0, stage, stage_g, taps, gen);
       for (int m = 1; m < p.M; ++m) {
         ctl_sync(sm, gen);
-        stage_chunks(p.x + int64_t(m) * p.ldx, p.K * 2, stage, kBfUnits);
+        stage_chunks<kBfUnits>(p.x + int64_t(m) * p.ldx, p.K * 2, stage);
         wait_memory_done();
         ctl_sync(sm, gen);
         ctl_row_bf16(p, sm, act + m * act_ld, m, stage, stage_g, taps, gen);
       }
     }
-    // The staged row is dead once every control wave has read it: clear the accumulators.
+    // The staged row is dead once every control wave has read it: clear the accumulators,
+    // then release the stream waves.
     ctl_sync(sm, gen);
     for (int e = tid; e < nt * P * kPart / 4; e += kDcCtlThreads)
       reinterpret_cast<i32x4*>(accum)[e] = i32x4{0, 0, 0, 0};
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();  // #2: codes, row scales and cleared accumulators ready
+    ctl_sync(sm, gen);
+    if (tid == 0) lds_set_flag(&sm.codes_ready, 1);
 
-    // Epilogue inputs of the workgroup's tiles (and of its leftover tile) into LDS: every
-    // load is issued before the first store, so they cost one memory round trip.
-    const int32_t lt = dg.leftover ? dg.grid * dg.whole_q + b / 4 : -1;
-    {
-      const int ct = tid;
-      constexpr int kSwN = (kDcMaxTiles + 1) * 16 * NMAT;                  // <= 192
-      constexpr int kResN = (kDcMaxTiles + 1) * kFuseMaxRows * 16;         // 384
-      constexpr int kResIt = (kResN + kDcCtlThreads - 1) / kDcCtlThreads;  // 2
-      float swv = 0.0f;
-      int32_t sw_t = -1;
-      int sw_slot = 0, sw_mat = 0, sw_c = 0;
-      if (ct < kSwN) {
-        sw_slot = ct / (16 * NMAT);
-        const int rem = ct % (16 * NMAT);
-        sw_mat = rem / 16;
-        sw_c = rem % 16;
-        sw_t = sw_slot < kDcMaxTiles ? (sw_slot < nt ? tb0 + sw_slot : -1) : lt;
-        if (sw_t >= 0) swv = (sw_mat == 0 ? p.sw0 : p.sw1)[int64_t(sw_t) * 16 + sw_c];
-      }
-      uint16_t rv[kResIt];
-      int32_t r_t[kResIt];
-      int r_slot[kResIt], r_m[kResIt], r_c[kResIt];
-#pragma unroll
-      for (int it = 0; it < kResIt; ++it) {
-        const int e = ct + it * kDcCtlThreads;
-        r_slot[it] = e / (kFuseMaxRows * 16);
-        const int rem = e % (kFuseMaxRows * 16);
-        r_m[it] = rem / 16;
-        r_c[it] = rem % 16;
-        r_t[it] = -1;
-        rv[it] = 0;
-        if constexpr (EPI == EPI_BF16_RES || EPI == EPI_DOWN) {
-          if (e < kResN && r_m[it] < p.M) {
-            r_t[it] = r_slot[it] < kDcMaxTiles ? (r_slot[it] < nt ? tb0 + r_slot[it] : -1) : lt;
-            if (r_t[it] >= 0) rv[it] = p.res[int64_t(r_m[it]) * p.ldr + int64_t(r_t[it]) * 16 + r_c[it]];
-          }
-        }
-      }
-      if (sw_t >= 0) sm.sw[sw_slot][sw_mat][sw_c] = swv;
-#pragma unroll
-      for (int it = 0; it < kResIt; ++it)
-        if (r_t[it] >= 0) sm.res[r_slot[it]][r_m[it]][r_c[it]] = rv[it];
-    }
-
+    // The leftover quarter's matrix work (its first V steps have landed by now).
+    int prev = -1;
     if (dg.leftover) {
-      // A K quarter of tile lt, shared with the three neighbouring workgroups: the four
-      // control waves take a quarter of it each.
-      const int32_t Q = St / 4, qq = b & 3;
-      const int32_t cw = wave;
-      const int32_t ql = Q / kDcCtl, qr = Q % kDcCtl;
-      const int32_t s0 = qq * Q + cw * ql + (cw < qr ? cw : qr);
-      const int32_t s1 = s0 + ql + (cw < qr ? 1 : 0);
       i32x4 lacc[NMAT];
 #pragma unroll
       for (int i = 0; i < NMAT; ++i) lacc[i] = i32x4{0, 0, 0, 0};
-      // All of the wave's steps in one batch (5 of Gate/Up, 17 of Down at Qwen3-14B).
-      constexpr int V = NMAT == 2 ? 8 : 20;
-      for (int32_t s = s0; s < s1; s += V) {
-        i32x4 wv[V][NMAT];
+      for (int32_t s0 = ls0; s0 < ls1; s0 += V) {
+        if (s0 != ls0) load_lo(s0);
 #pragma unroll
         for (int u = 0; u < V; ++u) {
-          const int32_t sq = (s + u < s1) ? s + u : s1 - 1;
-          const int64_t o = (LAYOUT == LAYOUT_TILED) ? (int64_t(lt) * St + sq) * 1024
-                                                     : int64_t(lt) * 16 * p.K + int64_t(sq) * 64;
-          wv[u][0] = ld16_stream(p.w0 + lane_off + o);
-          if constexpr (NMAT == 2) wv[u][1] = ld16_stream(p.w1 + lane_off + o);
-        }
-#pragma unroll
-        for (int u = 0; u < V; ++u) {
-          if (s + u < s1) {
-            const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(s + u) * 64);
+          if (s0 + u < ls1) {
+            const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(s0 + u) * 64);
             const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < NMAT; ++i) lacc[i] = mfma_i8(wv[u][i], bv, lacc[i]);
+            for (int i = 0; i < NMAT; ++i) lacc[i] = mfma_i8(lw[u][i], bv, lacc[i]);
           }
         }
       }
 #pragma unroll
       for (int i = 0; i < NMAT; ++i)
-        *reinterpret_cast<i32x4*>(lred + cw * kPart + (i * kWave + lane) * 4) = lacc[i];
-      // The last of the four control waves to finish adds their partials and publishes
-      // the quarter; the owner of quarter 0 then gathers the other three.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      int prev = 0;
+        *reinterpret_cast<i32x4*>(lred + wave * kPart + (i * kWave + lane) * 4) = lacc[i];
+      lds_release_only();
       if (lane == 0)
         prev = __hip_atomic_fetch_add(&sm.lo_arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       prev = __builtin_amdgcn_readfirstlane(prev);
-      if (prev == kDcCtl - 1) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        i32x4 piece[NMAT];
+    }
+    const bool last = prev == kDcCtl - 1;   // the last control wave to finish its part
+
+    // Epilogue inputs of the workgroup's tiles (and of its leftover tile) into LDS: every
+    // load is issued before the first store, so they cost one memory round trip.
+    const int ct = tid;
+    constexpr int kSwN = (kDcMaxTiles + 1) * 16 * NMAT;                  // <= 192
+    constexpr int kResN = (kDcMaxTiles + 1) * kFuseMaxRows * 16;         // 384
+    constexpr int kResIt = (kResN + kDcCtlThreads - 1) / kDcCtlThreads;  // 2
+    float swv = 0.0f;
+    int32_t sw_t = -1;
+    int sw_slot = 0, sw_mat = 0, sw_c = 0;
+    if (ct < kSwN) {
+      sw_slot = ct / (16 * NMAT);
+      const int rem = ct % (16 * NMAT);
+      sw_mat = rem / 16;
+      sw_c = rem % 16;
+      sw_t = sw_slot < kDcMaxTiles ? (sw_slot < nt ? tb0 + sw_slot : -1) : lt;
+      if (sw_t >= 0) swv = (sw_mat == 0 ? p.sw0 : p.sw1)[int64_t(sw_t) * 16 + sw_c];
+    }
+    uint16_t rv[kResIt];
+    int32_t r_t[kResIt];
+    int r_slot[kResIt], r_m[kResIt], r_c[kResIt];
 #pragma unroll
-        for (int i = 0; i < NMAT; ++i) {
-          piece[i] = i32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int w = 0; w < kDcCtl; ++w)
-            piece[i] += *reinterpret_cast<const i32x4*>(lred + w * kPart + (i * kWave + lane) * 4);
-        }
-        const uint32_t tag32 = epoch ^ (uint32_t(EPI + 1) << 29);
-        uint64_t* slots = reinterpret_cast<uint64_t*>(p.slots);
-        if (qq != 0) {
-#pragma unroll
-          for (int i = 0; i < NMAT; ++i)
-            store_tagged(slots + (int64_t(b) * NMAT + i) * kSlotWords + lane * 4, piece[i], tag32);
-        } else {
-          // Gather quarters 1..3 (workgroups b + 1 .. b + 3); they are published early in
-          // those workgroups, so this usually succeeds at the first read.  The wait is
-          // bounded; past the bound the tile's output is left unwritten.
-          const int32_t qpp = Ss / Q;   // quarters per K partition
-          bool ok = false;
-          i32x4 got[3][NMAT];
-          for (int attempt = 0; attempt < (1 << 16) && !ok; ++attempt) {
-            bool all = true;
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-#pragma unroll
-              for (int i = 0; i < NMAT; ++i) {
-                const TaggedX4 tw =
-                    load_tagged(slots + (int64_t(b + 1 + j) * NMAT + i) * kSlotWords + lane * 4);
-                got[j][i] = i32x4{0, 0, 0, 0};
-                add_tagged(got[j][i], tw, tag32, all);
-              }
-            ok = __builtin_amdgcn_ballot_w64(!all) == 0;
-            if (!ok) __builtin_amdgcn_s_sleep(8);
-          }
-          if (ok) {
-            // The tile's sums per K partition into LDS (the partials just read are dead):
-            // quarter j lies in partition j / qpp; quarter 0 is this workgroup's piece.
-            for (int q = 0; q < P; ++q)
-#pragma unroll
-              for (int i = 0; i < NMAT; ++i) {
-                i32x4 a = q == 0 ? piece[i] : i32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int j = 0; j < 3; ++j) a += ((j + 1) / qpp == q) ? got[j][i] : i32x4{0, 0, 0, 0};
-                *reinterpret_cast<i32x4*>(lred + q * kPart + (i * kWave + lane) * 4) = a;
-              }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
-            for (int32_t pq0 = 0; pq0 < p.M; pq0 += 4)
-              dc_epilogue<EPI, NMAT>(
-                  p, sm, static_cast<int32_t>(p.M), pq0 + lane / 16, P,
-                  [&](int32_t, int q, int mat, int64_t m, int n) {
-                    return acc_elem(lred + q * kPart, mat, m, n);
-                  },
-                  [&](int32_t) { return lt; }, [&](int32_t) { return kDcMaxTiles; });
-          }
+    for (int it = 0; it < kResIt; ++it) {
+      const int e = ct + it * kDcCtlThreads;
+      r_slot[it] = e / (kFuseMaxRows * 16);
+      const int rem = e % (kFuseMaxRows * 16);
+      r_m[it] = rem / 16;
+      r_c[it] = rem % 16;
+      r_t[it] = -1;
+      rv[it] = 0;
+      if constexpr (EPI == EPI_BF16_RES || EPI == EPI_DOWN) {
+        if (e < kResN && r_m[it] < p.M) {
+          r_t[it] = r_slot[it] < kDcMaxTiles ? (r_slot[it] < nt ? tb0 + r_slot[it] : -1) : lt;
+          if (r_t[it] >= 0) rv[it] = p.res[int64_t(r_m[it]) * p.ldr + int64_t(r_t[it]) * 16 + r_c[it]];
         }
       }
     }
 
-    // Then the control waves take their share of the weight stream.
-    if (rn > 0) {
-      i32x4 wA[U][NMAT], wB[U][NMAT];
-      load_batch(wA, 0);
-      load_batch(wB, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      stream_rest(wA, wB);
+    // The last control wave adds the four partials and publishes the quarter; the owner of
+    // quarter 0 gathers the other three instead (they are published early in workgroups
+    // b + 1 .. b + 3, so this usually succeeds within a few reads).  The wait is bounded;
+    // past the bound the tile's output is left unwritten.
+    const uint32_t tag32 = epoch ^ (uint32_t(EPI + 1) << 29);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(p.slots);
+    i32x4 piece[NMAT], got[3][NMAT];
+    bool ok = false;
+    if (last) {
+      __asm__ __volatile__("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < NMAT; ++i) {
+        piece[i] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < kDcCtl; ++w)
+          piece[i] += *reinterpret_cast<const i32x4*>(lred + w * kPart + (i * kWave + lane) * 4);
+      }
+      if (qq != 0) {
+#pragma unroll
+        for (int i = 0; i < NMAT; ++i)
+          store_tagged(slots + (int64_t(b) * NMAT + i) * kSlotWords + lane * 4, piece[i], tag32);
+      } else {
+        for (int attempt = 0; attempt < (1 << 16) && !ok; ++attempt) {
+          bool all = true;
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int i = 0; i < NMAT; ++i) {
+              const TaggedX4 tw =
+                  load_tagged(slots + (int64_t(b + 1 + j) * NMAT + i) * kSlotWords + lane * 4);
+              got[j][i] = i32x4{0, 0, 0, 0};
+              add_tagged(got[j][i], tw, tag32, all);
+            }
+          ok = __builtin_amdgcn_ballot_w64(!all) == 0;
+          if (!ok) __builtin_amdgcn_s_sleep(8);
+        }
+      }
+    }
+
+    // The epilogue inputs to LDS.
+    if (sw_t >= 0) sm.sw[sw_slot][sw_mat][sw_c] = swv;
+#pragma unroll
+    for (int it = 0; it < kResIt; ++it)
+      if (r_t[it] >= 0) sm.res[r_slot[it]][r_m[it]][r_c[it]] = rv[it];
+
+    if (dg.leftover) {
+      lds_release_only();
+      if (lane == 0) lds_add_sync(&sm.pf_done, 1);
+      if (last && qq == 0 && ok) {
+        // The tile's sums per K partition into LDS (the partials just read are dead):
+        // quarter j lies in partition j / qpp; quarter 0 is this workgroup's piece.
+        const int32_t qpp = Ss / Q;   // quarters per K partition
+        for (int q = 0; q < P; ++q)
+#pragma unroll
+          for (int i = 0; i < NMAT; ++i) {
+            i32x4 a = q == 0 ? piece[i] : i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 3; ++j) a += ((j + 1) / qpp == q) ? got[j][i] : i32x4{0, 0, 0, 0};
+            *reinterpret_cast<i32x4*>(lred + q * kPart + (i * kWave + lane) * 4) = a;
+          }
+        lds_wait_flag(&sm.pf_done, kDcCtl);   // every control wave's epilogue inputs
+        for (int32_t pq0 = 0; pq0 < p.M; pq0 += 4)
+          dc_epilogue<EPI, NMAT>(
+              p, sm, static_cast<int32_t>(p.M), pq0 + lane / 16, P,
+              [&](int32_t, int q, int mat, int64_t m, int n) {
+                return acc_elem(lred + q * kPart, mat, m, n);
+              },
+              [&](int32_t) { return lt; }, [&](int32_t) { return kDcMaxTiles; });
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -828,13 +880,6 @@ hipError_t launch_l(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
 
 }  // namespace
 
-#ifndef A8W8_DC_CTL_SHARE
-#define A8W8_DC_CTL_SHARE 0, 0, 0, 0
-#endif
-// Control-wave share of the stream per epilogue kind (BF16, BF16 + residual, SiLU, Down),
-// in sixteenths of a stream wave's.
-constexpr int kCtlShare16[4] = {A8W8_DC_CTL_SHARE};
-
 bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom& g) {
   g = DecodeGeom{};
   if (M < 1 || M > kFuseMaxRows || N % 16 || K % 64 || N <= 0) return false;
@@ -863,13 +908,6 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom
   g.whole_r = static_cast<int32_t>(left ? 0 : r);
   g.leftover = left ? 1 : 0;
   g.act_ld = static_cast<int32_t>(K);
-  // Steps per control wave: the control waves may join the stream after their prologue
-  // (and leftover quarter) with a share weighted kCtlShare / 16 of a stream wave's.  On
-  // MI355X at Qwen3-14B shapes every nonzero weight measured slower (the stream waves
-  // already keep the CU's memory pipeline full), so the default is none.
-  const int64_t W = ntmax * St;
-  const int64_t wq = kCtlShare16[epi];
-  g.ctl_steps = static_cast<int32_t>(W * wq / (16 * kDcStream + kDcCtl * wq));
   const size_t codes = (size_t(M) * size_t(K) + 255) / 256 * 256;
   const size_t part = size_t(nmat) * 4 * kWave * 4;   // bytes of one segment's sums
   g.acc_off = static_cast<int32_t>(codes);

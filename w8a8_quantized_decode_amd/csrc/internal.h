@@ -177,7 +177,6 @@ struct DecodeGeom {
   int32_t act_ld;            // bytes of codes per row in LDS (= K)
   int32_t acc_off, lred_off; // LDS offsets of the segment accumulators and the control waves' partials
   int32_t stage_g;           // offset of the staged RMSNorm gain from acc_off (the staging area)
-  int32_t ctl_steps;         // K steps of the stream taken by each control wave
   int32_t lds;               // dynamic LDS bytes
 };
 // False when the shape is not covered (then the stream-K kernel runs).
