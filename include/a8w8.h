@@ -269,6 +269,29 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
                                const a8w8_layer_taps* taps, void* stream);
 
 /*
+ * a8w8_layer_linears without a workspace argument, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and errors as a8w8_layer_linears;
+ * the workspace is a device array inside the library, one per GPU, of
+ * a8w8_layer_linears_static_max_workspace() bytes (16 MiB: Qwen3-14B shapes up to
+ * M = 16 need about 8.7 MB), kept until the process ends.  A call whose workspace
+ * would exceed it returns A8W8_ERR_WORKSPACE before anything is enqueued.  The call
+ * itself allocates nothing; its first call on a device looks up that device's array
+ * (A8W8_ERR_HIP if the lookup fails).  Every call on one GPU shares the array, which
+ * keeps the previous call's contents (none of which need clearing, as for any
+ * workspace): calls that overlap in time on one GPU race and must be serialized by
+ * the caller, e.g. by issuing them on one stream.
+ */
+size_t a8w8_layer_linears_static_max_workspace(void);
+a8w8_status a8w8_layer_linears_static(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                                      const uint16_t* gamma_post_bf16, float eps,
+                                      a8w8_qweight qkv, a8w8_qweight o, a8w8_qweight gate,
+                                      a8w8_qweight up, a8w8_qweight down, int64_t M, int64_t H,
+                                      int64_t I, int n_q_heads, int n_kv_heads, int head_dim,
+                                      int split_k, uint16_t* qkv_out_bf16, uint16_t* out_bf16,
+                                      const a8w8_layer_taps* taps, void* stream);
+
+/*
  * All linears of one prefill layer, W8A16 on the shared INT8 weights (pypto-lib PR #810,
  * What changed > Gate/Up INT8 path: prefill dequantizes each weight tile to BF16; the
  * layer composition is the decode layer's with that linear).  Same shapes as

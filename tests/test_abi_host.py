@@ -125,6 +125,25 @@ def test_mlp_block_validation(L):
     assert call(x=MIS) == 3
 
 
+def test_layer_static_validation(L):
+    """The allocation-free layer entry validates like a8w8_layer_linears and refuses a call
+    whose workspace would not fit its static one, all before touching a device."""
+    f = L.a8w8_layer_linears_static
+
+    def call(M=1, H=256, I=768, nq=2, nkv=1, hd=128, x=FAKE):
+        return f(x, FAKE, FAKE, 1e-6, QW, QW, QW, QW, QW, M, H, I, nq, nkv, hd, 2, None, FAKE,
+                 None, None)
+    assert B.a8w8_layer_linears_static_max_workspace() == 16 << 20
+    assert call(M=0) == 0
+    assert call(nq=3) == 2                   # n_q * head_dim != H
+    assert call(hd=0) == 2
+    assert call(x=None) == 1
+    assert call(x=MIS) == 3
+    # Qwen3-14B shapes: 8.7 MB of workspace at M = 16 fits, 139 MB at M = 256 does not
+    assert B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 16, 5120, 17408, 7168, 2) <= 16 << 20
+    assert call(M=256, H=5120, I=17408, nq=40, nkv=8, hd=128) == 4
+
+
 def test_layer_validation(L):
     f = L.a8w8_layer_linears
     ws = B.a8w8_workspace_bytes(B.OP_LAYER_LINEARS, 1, 256, 768, 512, 2)

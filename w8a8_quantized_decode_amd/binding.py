@@ -102,6 +102,14 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, _vp, _vp, _vp, ctypes.c_size_t,
                                          ctypes.POINTER(LayerTaps), _vp]
+        L.a8w8_layer_linears_static.restype = ctypes.c_int
+        L.a8w8_layer_linears_static.argtypes = [_vp, _vp, _vp, ctypes.c_float, QWeight,
+                                                QWeight, QWeight, QWeight, QWeight, _c_i64,
+                                                _c_i64, _c_i64, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, ctypes.c_int, _vp, _vp,
+                                                ctypes.POINTER(LayerTaps), _vp]
+        L.a8w8_layer_linears_static_max_workspace.restype = ctypes.c_size_t
+        L.a8w8_layer_linears_static_max_workspace.argtypes = []
         L.a8w8_layer_linears_prefill.restype = ctypes.c_int
         L.a8w8_layer_linears_prefill.argtypes = [_vp, _vp, _vp, ctypes.c_float, QWeight,
                                                  QWeight, QWeight, QWeight, QWeight, _c_i64,
@@ -248,6 +256,30 @@ def a8w8_layer_linears(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out
                                   _ptr(workspace), workspace.numel(),
                                   ctypes.byref(t) if t is not None else None, _stream(stream))
     _check(st, "a8w8_layer_linears")
+
+
+def a8w8_layer_linears_static(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out,
+                              n_q_heads: int, n_kv_heads: int, head_dim: int, split_k: int = 2,
+                              qkv_out=None, taps: Optional[dict] = None, stream=None) -> None:
+    """a8w8_layer_linears with the library's own per-GPU workspace (no allocation)."""
+    M, H = x.shape
+    I = gate[1].shape[0]
+    t = None
+    if taps:
+        t = LayerTaps()
+        t.mlp.ev_kernel = -1
+        _fill_taps(t, taps)
+    st = lib().a8w8_layer_linears_static(_ptr(x), _ptr(gamma_in), _ptr(gamma_post), float(eps),
+                                         _qw(qkv), _qw(o), _qw(gate), _qw(up), _qw(down), M, H, I,
+                                         int(n_q_heads), int(n_kv_heads), int(head_dim),
+                                         int(split_k), _ptr(qkv_out), _ptr(out),
+                                         ctypes.byref(t) if t is not None else None,
+                                         _stream(stream))
+    _check(st, "a8w8_layer_linears_static")
+
+
+def a8w8_layer_linears_static_max_workspace() -> int:
+    return int(lib().a8w8_layer_linears_static_max_workspace())
 
 
 def a8w8_decode_layer(x, gamma_in, gamma_post, eps, qkv, o, gate, up, down, out, workspace,

@@ -15,6 +15,7 @@
 #include <chrono>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <random>
 
 #include "../../include/a8w8.h"
@@ -558,6 +559,35 @@ static a8w8_status make_attn_args(const uint16_t*, int64_t, int, int, int, const
 
 // The decode layer: QKV, then either the identity attention on the Q slice (att ==
 // nullptr) or QK-norm + RoPE + KV write and decode attention, then O (+ x) and the MLP.
+// ------------------------------------------------------------------ allocation-free entry
+// Workspace of a8w8_layer_linears_static: a file-scope device array, one copy per GPU, held
+// until the process ends.  Host code never passes the array's name to a kernel (on the
+// host it only stands for the symbol); the device address of each GPU's copy is looked up
+// once per device and kept here.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`; A8W8_ERR_HIP if it cannot be resolved.
+a8w8_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return A8W8_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return A8W8_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return A8W8_OK;
+}
+
 static a8w8_status layer_decode(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
                                 const uint16_t* gamma_post_bf16, float eps, a8w8_qweight qkv,
                                 a8w8_qweight o, a8w8_qweight gate, a8w8_qweight up,
@@ -565,7 +595,8 @@ static a8w8_status layer_decode(const uint16_t* x_bf16, const uint16_t* gamma_in
                                 int n_q_heads, int n_kv_heads, int head_dim, int split_k,
                                 const a8w8_attention_step* att, uint16_t* qkv_out_bf16,
                                 uint16_t* h1_out_bf16, uint16_t* out_bf16, void* workspace,
-                                size_t ws_bytes, const a8w8_layer_taps* taps, void* stream) {
+                                size_t ws_bytes, const a8w8_layer_taps* taps, void* stream,
+                                bool static_ws = false) {
   if (a8w8_status s = check_mlp_shapes(M, H, I, split_k)) return s;
   if (n_q_heads <= 0 || n_kv_heads < 0 || head_dim <= 0) return A8W8_ERR_SHAPE;
   if (int64_t(n_q_heads) * head_dim != H) return A8W8_ERR_SHAPE;
@@ -581,6 +612,13 @@ static a8w8_status layer_decode(const uint16_t* x_bf16, const uint16_t* gamma_in
     return A8W8_ERR_ALIGN;
   const size_t need = a8w8_workspace_bytes(A8W8_OP_LAYER_LINEARS, M, H, I, n_qkv, split_k,
                                            A8W8_MODE_DECODE_A8W8);
+  if (static_ws) {
+    // The library's own workspace: checked against its size, then looked up (the first
+    // call on a device resolves that device's copy).
+    if (need > kStaticScratchBytes) return A8W8_ERR_WORKSPACE;
+    if (a8w8_status e = static_scratch(&workspace)) return e;
+    ws_bytes = kStaticScratchBytes;
+  }
   if (!workspace || ws_bytes < need) return A8W8_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return A8W8_ERR_ALIGN;
   const ChainPlan pl = make_plan(M, H, I, n_qkv, split_k, true);
@@ -697,6 +735,20 @@ a8w8_status a8w8_layer_linears(const uint16_t* x_bf16, const uint16_t* gamma_in_
   return layer_decode(x_bf16, gamma_in_bf16, gamma_post_bf16, eps, qkv, o, gate, up, down, M,
                       H, I, n_q_heads, n_kv_heads, head_dim, split_k, nullptr, qkv_out_bf16,
                       nullptr, out_bf16, workspace, ws_bytes, taps, stream);
+}
+
+size_t a8w8_layer_linears_static_max_workspace(void) { return kStaticScratchBytes; }
+
+a8w8_status a8w8_layer_linears_static(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
+                                      const uint16_t* gamma_post_bf16, float eps,
+                                      a8w8_qweight qkv, a8w8_qweight o, a8w8_qweight gate,
+                                      a8w8_qweight up, a8w8_qweight down, int64_t M, int64_t H,
+                                      int64_t I, int n_q_heads, int n_kv_heads, int head_dim,
+                                      int split_k, uint16_t* qkv_out_bf16, uint16_t* out_bf16,
+                                      const a8w8_layer_taps* taps, void* stream) {
+  return layer_decode(x_bf16, gamma_in_bf16, gamma_post_bf16, eps, qkv, o, gate, up, down, M,
+                      H, I, n_q_heads, n_kv_heads, head_dim, split_k, nullptr, qkv_out_bf16,
+                      nullptr, out_bf16, nullptr, 0, taps, stream, /*static_ws=*/true);
 }
 
 a8w8_status a8w8_decode_layer(const uint16_t* x_bf16, const uint16_t* gamma_in_bf16,
