@@ -195,8 +195,12 @@ a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx,
  *   residual_bf16 [M, N] BF16 or NULL; y_bf16 [M, N] BF16 output;
  *   acc_i32_tap [M, N] INT32 or NULL.
  * y = rne_bf16((f32(acc) * row_scale[m]) * scale[n] [+ residual]).
- * K % 64 == 0, 0 < K <= 131072 (INT32 accumulators cannot overflow), N % 16 == 0.
- * y may alias residual_bf16.  One kernel.
+ * K % 64 == 0, 0 < K <= 131072 (INT32 accumulators cannot overflow), N % 16 == 0,
+ * M <= 65535 * 64 (one grid row per 64 rows).  y may alias residual_bf16.  One kernel.
+ * (pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data paths",
+ * What changed > Gate/Up INT8 path: INT8 x INT8 -> INT32 with the activation-row and
+ * weight-channel scales applied at dequantization; the decode layer's QKV and output
+ * projections use the same arithmetic, What changed > Decode scheduling.)
  */
 a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
                         const uint16_t* residual_bf16, int64_t M, int64_t N,
@@ -206,7 +210,9 @@ a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
 /*
  * Workspace size in bytes for a8w8_mlp_block (op = A8W8_OP_MLP_BLOCK, n_qkv ignored)
  * or a8w8_layer_linears (op = A8W8_OP_LAYER_LINEARS).  Returns 0 for invalid
- * arguments.  The workspace is scratch: its contents on entry do not matter and are
+ * arguments.  (Caller-owned device scratch, allocated once and reused across calls, the
+ * way the runner of pypto-serving PR #61 "Add Qwen3 A8W8 L2 runner foundation", Summary,
+ * caches its worker-side tensor allocations.)  The workspace is scratch: its contents on entry do not matter and are
  * unspecified on return.  Its first 256 bytes hold two tag words that the decode GEMMs
  * advance on the device (each GEMM reads one and writes the next value to the other);
  * partial sums exchanged between workgroups carry that tag, so nothing is cleared
@@ -231,7 +237,8 @@ size_t a8w8_workspace_bytes(int op, int64_t M, int64_t H, int64_t I, int64_t n_q
  *   for its numerics: Down is one FP32-accumulated sum).
  *   workspace: ws_bytes >= a8w8_workspace_bytes(A8W8_OP_MLP_BLOCK, ...), 256-byte
  *   aligned scratch.  taps: a8w8_mlp_taps or NULL.
- * Shapes: H % 64 == 0, I % (64 * split_k) == 0, H and I <= 131072.  out may alias
+ * Shapes: H % 64 == 0, I % (64 * split_k) == 0, H and I <= 131072, M <= 65535 * 64.
+ * out may alias
  * residual_bf16 or x_bf16.
  * Prefill mode (any M; built for M in the hundreds): a = rne_bf16(RMSNorm(x)); every
  * weight tile is dequantized to W' = rne_bf16(fl32(w * s)) on the fly; Gate/Up
@@ -255,6 +262,10 @@ a8w8_status a8w8_mlp_block(const uint16_t* x_bf16, const uint16_t* gamma_bf16, f
  * Steps: RMSNorm(gamma_in) -> quant -> QKV -> qkv = rne_bf16(dequant) -> the Q slice
  * qkv[:, :H] stands in for the attention output -> quant -> O -> h1 = rne_bf16(dequant
  * + x) -> MLP block with input h1 and residual h1.
+ * (pypto-serving issue #52 "[Feature] Add native Qwen3-14B A8W8 serving path", Proposed
+ * behavior: the A8W8 decode layer; its linears in the order of the CodeRabbit
+ * walkthrough of pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and
+ * data paths".)
  *   qkv_out_bf16 [M, n_qkv] receives qkv, or NULL to keep it in the workspace;
  *   out_bf16 [M, H]; workspace from a8w8_workspace_bytes(A8W8_OP_LAYER_LINEARS, ...).
  * out may alias x_bf16.

@@ -318,9 +318,10 @@ def layer_linears_decode(x_bits, gamma_in_bits, gamma_post_bits, eps, w_qkv, s_q
 def dequant_weight_bf16(w, s) -> np.ndarray:
     """``W'[n,k] = rne_bf16(fl32(f(w[n,k]) * s[n]))`` (uint16 bits).
 
-    [PR810] What changed > Gate/Up INT8 path: prefill stays on the shared INT8 weights
-    by dequantizing each weight tile to BF16.  The double rounding (FP32 product, then
-    BF16) is part of the definition.
+    [PR810] What changed > Gate/Up INT8 path.  The prefill GEMMs read the same INT8
+    weights as decode; each weight becomes a BF16 value on the way in: the weight times
+    its channel scale as one FP32 product, then rounded to BF16 with ties to even.
+    Both roundings belong to the definition.
     """
     wf = np.asarray(w, dtype=np.int8).astype(np.float32)
     return rne_bf16(wf * np.asarray(s, dtype=np.float32)[:, None])

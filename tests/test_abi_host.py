@@ -99,6 +99,7 @@ def test_linear_validation(L):
     assert f(FAKE, FAKE, QW, None, 1, 16, 100, FAKE, None, None) == 2           # K % 64
     assert f(FAKE, FAKE, QW, None, 1, 24, 64, FAKE, None, None) == 2            # N % 16
     assert f(FAKE, FAKE, QW, None, 1, 16, 131072 + 64, FAKE, None, None) == 2   # K too large
+    assert f(FAKE, FAKE, QW, None, 65535 * 64 + 1, 16, 64, FAKE, None, None) == 2  # grid rows
     assert f(FAKE, FAKE, B.QWeight(FAKE, None, 0), None, 1, 16, 64, FAKE, None, None) == 1
     assert f(FAKE, FAKE, QW, None, 1, 16, 64, None, None, None) == 1
     assert f(FAKE, FAKE, B.QWeight(MIS, FAKE, 0), None, 1, 16, 64, FAKE, None, None) == 3
@@ -116,6 +117,7 @@ def test_mlp_block_validation(L):
     assert call(H=200) == 2
     assert call(I=768 + 64) == 2            # I % (64 * split_k)
     assert call(split=3) == 2
+    assert call(M=65535 * 64 + 1) == 2       # more 64-row groups than a grid dimension holds
     assert call(mode=5) == 2
     assert call(x=None) == 1
     assert call(gate=B.QWeight(None, FAKE, 0)) == 1

@@ -14,7 +14,7 @@ from w8a8_quantized_decode_amd import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PACK = "a8w8::(anonymous namespace)::pack_tiled_kernel(signed char const*, long, long, signed char*)"
-GATEUP = "void a8w8::(anonymous namespace)::streamk_kernel<2, 2, 8, 1, 1, 1>(a8w8::StreamKArgs)"
+GATEUP = "void a8w8::(anonymous namespace)::decode_kernel<2, 2, 1>(a8w8::StreamKArgs, a8w8::DecodeGeom)"
 
 
 def test_more_than_one_gpu_is_refused():

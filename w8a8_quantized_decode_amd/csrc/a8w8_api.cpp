@@ -12,11 +12,9 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <chrono>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
-#include <random>
 
 #include "../../include/a8w8.h"
 #include "attention_args.h"
@@ -27,6 +25,9 @@ using namespace a8w8;
 namespace {
 
 constexpr int64_t kMaxK = 131072;  // 128 * 127 * K stays below 2^31
+// The stream-K GEMM runs one grid row per 64 activation rows, and a grid dimension holds
+// at most 65535 of them.
+constexpr int64_t kMaxM = int64_t(65535) * 64;
 constexpr size_t kAlign = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -171,7 +172,7 @@ a8w8_status check_mlp_shapes(int64_t M, int64_t H, int64_t I, int split_k) {
   if (!valid_split(split_k)) return A8W8_ERR_SHAPE;
   if (H % 64 || I % (64 * int64_t(split_k))) return A8W8_ERR_SHAPE;
   if (H > kMaxK || I > kMaxK) return A8W8_ERR_SHAPE;
-  if (M > (int64_t(1) << 24)) return A8W8_ERR_SHAPE;
+  if (M > kMaxM) return A8W8_ERR_SHAPE;
   return A8W8_OK;
 }
 
@@ -455,7 +456,7 @@ a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx, const uint16
 a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
                         const uint16_t* residual_bf16, int64_t M, int64_t N, int64_t K,
                         uint16_t* y_bf16, int32_t* acc_i32_tap, void* stream) {
-  if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 16 || K > kMaxK || M > (int64_t(1) << 24))
+  if (M < 0 || N <= 0 || K <= 0 || K % 64 || N % 16 || K > kMaxK || M > kMaxM)
     return A8W8_ERR_SHAPE;
   if (M == 0) return A8W8_OK;
   if (!q || !row_scale || !y_bf16) return A8W8_ERR_NULL;
