@@ -31,10 +31,20 @@ METRIC = "µs/layer and INT8-weight HBM GB/s (% of peak), A8W8 decode linears at
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 GATEUP_KERNEL = 5     # kernel number of the Gate/Up GEMM inside a8w8_layer_linears
-GATEUP_NAME = "decode_kernel<2, 2,"        # its symbol in rocprofv3 counter tables
+GATEUP_NAME = "decode_kernel<2, 2,"        # its symbol in rocprofv3 counter tables (M <= 4)
+GATEUP_NAME_SK = "streamk_kernel<2, 2,"    # ... with more rows (M = 16: the stream-K kernel)
 PACK_NAME = "pack_tiled_kernel"            # plain permuting copy: the counter calibration
 PMC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_pmc.json")
 PMC_MD = os.path.join(ROOT, "profiles", "layer_linears_m1_pmc.md")
+PMC_FILE_M16 = os.path.join(ROOT, "profiles", "gateup_gemm_m16_pmc.json")
+PMC_MD_M16 = os.path.join(ROOT, "profiles", "stack40_m16_pmc.md")
+
+
+def pmc_target(cfg):
+    """(summary json, summary markdown, Gate/Up kernel symbol) of a config's counters."""
+    if cfg.M > 4:
+        return PMC_FILE_M16, PMC_MD_M16, GATEUP_NAME_SK
+    return PMC_FILE, PMC_MD, GATEUP_NAME
 
 
 def parse():
@@ -44,7 +54,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--sets", type=int, default=4, help="weight sets rotated across steps")
     p.add_argument("--config", type=int, default=2,
-                   help="2: layer M=1; 3: 40-layer M=16 stack; 4: W8A16 prefill MLP M=256")
+                   help="0: toy MLP block; 1: Qwen3-14B MLP block M=1; 2: layer M=1; "
+                        "3: 40-layer M=16 stack; 4: W8A16 prefill MLP M=256")
+    p.add_argument("--stream-ceiling", action="store_true",
+                   help="time a plain streaming read of the layer's weight bytes (the "
+                        "achievable HBM read rate the decode GEMMs are measured against)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--qk-rope", action="store_true",
                    help="time the QK-norm + RoPE + KV-cache write step (Qwen3-14B heads, M=1 and 16)")
@@ -67,6 +81,37 @@ def parse():
     return p.parse_args()
 
 
+def event_stats(torch, run, n: int) -> dict:
+    """Calls run(i) n times back to back on the current stream with a HIP event after
+    each call: per-call microseconds as median, 10th and 90th percentile and mean."""
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        run(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)])
+    return pct_stats(d)
+
+
+def pct_stats(d) -> dict:
+    d = np.asarray(d, dtype=np.float64)
+    return {"median": round(float(np.median(d)), 2), "p10": round(float(np.percentile(d, 10)), 2),
+            "p90": round(float(np.percentile(d, 90)), 2), "mean": round(float(d.mean()), 2)}
+
+
+def emit(line: dict) -> None:
+    """Prints the bench line; a roofline fraction above 1 means the timing bracketed the
+    wrong work, so the run then fails."""
+    print(json.dumps(line))
+    frac = (line.get("roofline") or {}).get("frac")
+    if frac is not None and frac > 1.0:
+        print(f"[bench] roofline fraction {frac} > 1: the timed interval cannot hold that "
+              f"kernel's bytes; failing", file=sys.stderr)
+        sys.exit(3)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("gemm_decode.hip", "gemm_streamk.hip", "device_common.h", "internal.h"):
@@ -75,11 +120,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes_alg: float):
+def measured_traffic(cfg):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, or None if the
     summary is missing or was taken on a different kernel source."""
     try:
-        with open(PMC_FILE) as f:
+        with open(pmc_target(cfg)[0]) as f:
             pmc = json.load(f)
     except (OSError, ValueError):
         return None
@@ -97,8 +142,9 @@ def pmc_summary(fetch_csv: str, write_csv: str, commands, cfg) -> None:
     import csv
     from collections import defaultdict
 
-    H, I, n_qkv = cfg.H, cfg.I, cfg.n_qkv
+    H, I, n_qkv, M = cfg.H, cfg.I, cfg.n_qkv, cfg.M
     pack_sizes = {n_qkv * H, H * H, I * H}
+    pmc_file, pmc_md, gu_name = pmc_target(cfg)
 
     def load(path, counter):
         per_kernel, pack_alg, pack_cnt = defaultdict(list), 0.0, 0.0
@@ -127,17 +173,17 @@ def pmc_summary(fetch_csv: str, write_csv: str, commands, cfg) -> None:
         hbm = fk * 1024 * f_fetch + wk * 1024 * f_write
         short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")[:90]
         rows.append((short, len(fetch[name]), fk, wk, hbm))
-        if GATEUP_NAME in name:
+        if gu_name in name:
             gu = dict(fetch_kib=fk, write_kib=wk, hbm_bytes_per_dispatch=round(hbm))
     if gu is None:
-        raise SystemExit(f"no {GATEUP_NAME} dispatch in the counter tables")
-    gu_alg = 2 * I * H + 2 * I * 4 + H + 4 + I * 4
-    summary = dict(kernel=GATEUP_NAME, workload=cfg.name, kernel_source_hash=kernel_source_hash(),
+        raise SystemExit(f"no {gu_name} dispatch in the counter tables")
+    gu_alg = 2 * I * H + 2 * I * 4 + M * H + M * 4 + M * I * 4
+    summary = dict(kernel=gu_name, workload=cfg.name, kernel_source_hash=kernel_source_hash(),
                    fetch_factor=round(f_fetch, 5), write_factor=round(f_write, 5),
                    algorithmic_bytes_per_dispatch=gu_alg,
                    traffic_over_algorithmic=round(gu["hbm_bytes_per_dispatch"] / gu_alg, 4),
                    commands=list(commands), **gu)
-    with open(PMC_FILE, "w") as f:
+    with open(pmc_file, "w") as f:
         json.dump(summary, f, indent=1)
         f.write("\n")
     lines = [f"# HBM traffic per dispatch, {cfg.name}", "",
@@ -152,7 +198,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, commands, cfg) -> None:
     lines += ["", f"Gate/Up GEMM: {gu['hbm_bytes_per_dispatch'] / 1e6:.2f} MB per dispatch against "
               f"{gu_alg / 1e6:.2f} MB algorithmic ({summary['traffic_over_algorithmic']:.4f}x).",
               f"Kernel source hash: {summary['kernel_source_hash']}.", ""]
-    with open(PMC_MD, "w") as f:
+    with open(pmc_md, "w") as f:
         f.write("\n".join(lines))
     print(json.dumps(summary))
 
@@ -276,7 +322,7 @@ def bench_prefill(args, cfg, torch, B) -> None:
             lambda: O.prefill_mlp(d["x"], d["gamma_post"], cfg.eps, d["w_gate"], d["s_gate"],
                                   d["w_up"], d["s_up"], d["w_down"], d["s_down"], d["res"]),
             args.cpu_seconds, f"the same M={M} prefill MLP block")
-    print(json.dumps(out_line))
+    emit((out_line))
 
 
 def bench_prefill_layer(args, torch, B) -> None:
@@ -328,7 +374,7 @@ def bench_prefill_layer(args, torch, B) -> None:
                                             d["w_down"], d["s_down"], cfg.n_q_heads,
                                             cfg.head_dim),
             args.cpu_seconds, f"the same M={M} prefill layer")
-    print(json.dumps({
+    emit(({
         "metric": "W8A16 prefill layer TFLOP/s (QKV, O, Gate/Up, Down GEMMs), BF16 matrix cores",
         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
@@ -398,7 +444,7 @@ def bench_qk_rope(args, torch, B) -> None:
         rows.append({"M": M, "us_per_call": round(us, 2), "bytes_per_call": nbytes,
                      "gb_s": round(nbytes / (us * 1e-6) / 1e9, 2)})
     r16 = rows[-1]
-    print(json.dumps({
+    emit(({
         "metric": "QK-norm + RoPE + paged BF16 KV-cache write, microseconds per call",
         "value": r16["us_per_call"], "unit": "us", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r16["us_per_call"] / 1e3, 5),
@@ -470,7 +516,7 @@ def bench_attention(args, torch, B) -> None:
                      "us_per_call": round(us, 2), "bytes_per_call": nbytes,
                      "gb_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
     r16 = rows[-1]
-    print(json.dumps({
+    emit(({
         "metric": "decode attention over the paged BF16 KV cache, microseconds per call",
         "value": r16["us_per_call"], "unit": "us", "n_gpus": 1, "steps": args.steps,
         "warmup": 3, "ms_per_step": round(r16["us_per_call"] / 1e3, 5),
@@ -567,7 +613,7 @@ def bench_decode_layer(args, torch, B) -> None:
                                        a["k_cache"], a["v_cache"], a["scale"]),
                 min(args.cpu_seconds, 10.0), f"the same M=1 layer at context {L}")
     r1 = rows[0]
-    print(json.dumps({
+    emit(({
         "metric": "Qwen3-14B A8W8 decode layer with paged attention, microseconds per layer",
         "value": r1["us_per_layer"], "unit": "us", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r1["us_per_layer"] / 1e3, 5),
@@ -580,6 +626,163 @@ def bench_decode_layer(args, torch, B) -> None:
                      "kernel": "whole layer (QKV, QK-RoPE, attention split + merge, O, MLP)",
                      "algorithmic_bytes_per_launch": r1["bytes"]},
         "cpu_baseline": cpu}))
+
+
+def bench_mlp(args, cfg, torch, B) -> None:
+    """Configs 0 and 1: the decode MLP block (RMSNorm, quantization, Gate/Up, SiLU * up,
+    requantization, split Down + residual) at M = 1.  Value: INT8-weight GB/s; roofline:
+    the Gate/Up GEMM from HIP events around its launch.  Weight sets rotate across steps
+    so the last-level cache cannot serve them, except for the toy block (0.6 MB of
+    weights), which stays cache-resident and is flagged so."""
+    from w8a8_quantized_decode_amd import synth
+    M, H, I = cfg.M, cfg.H, cfg.I
+    toy = cfg.index == 0
+    nsets = 1 if toy else max(1, args.sets)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    def upw(w, s_):
+        rm = up(w)
+        tiled = torch.empty_like(rm)
+        B.a8w8_pack_weight(rm, tiled)
+        return (tiled, up(s_), B.LAYOUT_TILED)
+
+    sets = []
+    for si in range(nsets):
+        d = synth.mlp_inputs(cfg, layer=si, M=M)
+        sets.append(dict(g=up(d["gamma_post"]), gate=upw(d["w_gate"], d["s_gate"]),
+                         up=upw(d["w_up"], d["s_up"]), down=upw(d["w_down"], d["s_down"])))
+        if si == 0:
+            x0, res0, d0 = up(d["x"]), up(d["res"]), d
+    out = torch.empty_like(res0)
+    ws = torch.zeros(B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, M, H, I, 0, cfg.split_k),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i, taps=None):
+        w = sets[i % nsets]
+        B.a8w8_mlp_block(x0, w["g"], cfg.eps, w["gate"], w["up"], w["down"], res0, out, ws,
+                         split_k=cfg.split_k, taps=taps)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / args.steps * 1e6
+    per_step = event_stats(torch, step, min(args.steps, 200))
+    wbytes = 3 * I * H
+    gbs = wbytes / (us * 1e-6) / 1e9
+
+    n_ev = min(args.steps, 100)
+    evs = []
+    for _ in range(n_ev):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        step(i, {"ev_start": a.cuda_event, "ev_stop": b.cuda_event, "ev_kernel": GATEUP_KERNEL})
+    torch.cuda.synchronize()
+    k_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    gu_bytes = 2 * I * H + 2 * I * 4 + M * H * 2 + H * 2 + M * I * 4
+    achieved = gu_bytes / (float(np.mean(k_us)) * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        cpu = oracle_per_call(
+            lambda: O.mlp_block_decode(d0["x"], d0["gamma_post"], cfg.eps, d0["w_gate"],
+                                       d0["s_gate"], d0["w_up"], d0["s_up"], d0["w_down"],
+                                       d0["s_down"], d0["res"], split_k=cfg.split_k),
+            args.cpu_seconds, f"the same M={M} MLP block")
+    emit({
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic (seeded PCG64, " + ("toy shapes; weights stay cache-resident)"
+                                               if toy else "Qwen3-14B shapes, random INT8 weights)"),
+        "us_per_block": round(us, 2), "us_per_step_events": per_step,
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "config": {"workload": cfg.name, "M": M, "hidden": H, "intermediate": I,
+                   "split_k": cfg.split_k, "weight_sets": nsets, "int8_weight_bytes": wbytes,
+                   "cache_resident": toy, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<EPI_SILU> (Gate/Up)",
+                     "kernel_us": round(float(np.mean(k_us)), 2),
+                     "kernel_us_stats": pct_stats(k_us),
+                     "algorithmic_bytes_per_launch": gu_bytes},
+        "cpu_baseline": cpu})
+
+
+def bench_stream_ceiling(args, torch) -> None:
+    """A plain streaming read (measure/stream_read.hip: one 16-wave workgroup per CU, each
+    wave reading a contiguous run, 1 KB loads, eight in flight) over the byte counts of
+    the layer's weights: the whole layer in one read, and its four GEMMs' weight bytes
+    as four reads back to back.  Buffers rotate so the last-level cache cannot serve
+    them.  This is the achievable HBM read rate the decode GEMMs are compared against."""
+    import ctypes
+    from w8a8_quantized_decode_amd import build as BD
+    from w8a8_quantized_decode_amd import synth
+    if not os.path.exists(BD.MEASURE_LIB):
+        raise SystemExit(f"{BD.MEASURE_LIB} is missing: build first")
+    L = ctypes.CDLL(BD.MEASURE_LIB)
+    L.a8w8m_stream_read.restype = ctypes.c_int
+    L.a8w8m_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_void_p]
+    cfg = synth.CONFIGS[2]
+    H, I, n_qkv = cfg.H, cfg.I, cfg.n_qkv
+    parts = [n_qkv * H, H * H, 2 * I * H, H * I]
+    total = sum(parts)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbuf = 4
+    bufs = [torch.full((total,), i + 1, dtype=torch.int8, device="cuda") for i in range(nbuf)]
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def read(buf, off, n):
+        rc = L.a8w8m_stream_read(buf.data_ptr() + off, n, out.data_ptr(), cus, st)
+        if rc:
+            raise SystemExit(f"a8w8m_stream_read failed: {rc}")
+
+    def whole(i):
+        read(bufs[i % nbuf], 0, total)
+
+    def four(i):
+        off = 0
+        for n in parts:
+            read(bufs[i % nbuf], off, n)
+            off += n
+
+    for i in range(args.warmup):
+        whole(i)
+        four(i)
+    torch.cuda.synchronize()
+    n = min(args.steps, 200)
+    w = event_stats(torch, whole, n)
+    f = event_stats(torch, four, n)
+    gbs = total / (w["median"] * 1e-6) / 1e9
+    emit({
+        "metric": "streaming-read ceiling over the layer's INT8 weight bytes", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(w["median"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "i8", "data": "device buffers, rotated (4 x 330 MB)",
+        "config": {"workload": "plain streaming read of 330.3 MB (one read) and of the four "
+                               "GEMMs' weight bytes (four reads back to back)",
+                   "bytes": total, "parts": parts, "cus": cus},
+        "one_read_us": w, "four_reads_us": f,
+        "four_reads_gb_s": round(total / (f["median"] * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "stream_runs (measure/stream_read.hip)",
+                     "algorithmic_bytes_per_launch": total},
+        "cpu_baseline": None})
 
 
 def main():
@@ -605,6 +808,9 @@ def main():
     if args.decode_layer:
         bench_decode_layer(args, torch, B)
         return
+    if args.stream_ceiling:
+        bench_stream_ceiling(args, torch)
+        return
     cfg = synth.CONFIGS[args.config]
     if cfg.kind == "prefill" and args.layer:
         bench_prefill_layer(args, torch, B)
@@ -612,8 +818,11 @@ def main():
     if cfg.kind == "prefill":
         bench_prefill(args, cfg, torch, B)
         return
+    if cfg.kind == "mlp":
+        bench_mlp(args, cfg, torch, B)
+        return
     if cfg.kind not in ("layer", "stack"):
-        raise SystemExit("bench.py times the layer-linears configs (2, 3) or the prefill (4)")
+        raise SystemExit(f"config {cfg.index}: unknown kind {cfg.kind}")
     layers = cfg.layers if cfg.kind == "stack" else 1
     M, H, I, n_qkv = cfg.M, cfg.H, cfg.I, cfg.n_qkv
     nsets = layers if cfg.kind == "stack" else max(1, args.sets)
@@ -681,6 +890,8 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / args.steps * 1e3
     layers_per_step = layers
+    # The same steps one by one between HIP events: the spread of a step.
+    per_step = event_stats(torch, step, min(args.steps, 200 if cfg.kind != "stack" else 20))
     us_per_layer = ms_per_step * 1e3 / layers_per_step
     gbs = wbytes_layer * layers_per_step / (ms_per_step * 1e-3) / 1e9
 
@@ -725,13 +936,16 @@ def main():
     for i in range(n_ev):
         step(i, taps_fn)
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    k_all = np.array([a.elapsed_time(b) for a, b in evs])
+    k_ms = float(np.mean(k_all))
     gu_bytes = 2 * I * H + 2 * I * 4 + M * H + M * 4 + M * I * 4   # weights, scales, q_x, s_x, h
     achieved = gu_bytes / (k_ms * 1e-3) / 1e9
-    traffic = measured_traffic(gu_bytes)
+    traffic = measured_traffic(cfg)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_kernel<EPI_SILU> (Gate/Up)", "kernel_us": round(k_ms * 1e3, 2),
+            "kernel": "decode_kernel<EPI_SILU> (Gate/Up)" if M <= 4 else
+                      "streamk_kernel<EPI_SILU> (Gate/Up)", "kernel_us": round(k_ms * 1e3, 2),
+            "kernel_us_stats": pct_stats(k_all * 1e3),
             "algorithmic_bytes_per_launch": gu_bytes}
 
     cpu = None
@@ -744,6 +958,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic (seeded PCG64, Qwen3-14B shapes, random INT8 weights)",
         "us_per_layer": round(us_per_layer, 2),
+        "us_per_step_events": per_step,
         "graph_us_per_layer": round(graph_us, 2) if graph_us is not None else None,
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "config": {"workload": cfg.name, "M": M, "hidden": H, "intermediate": I,
@@ -752,7 +967,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu,
     }
-    print(json.dumps(out))
+    emit((out))
 
 
 if __name__ == "__main__":

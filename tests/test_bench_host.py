@@ -48,11 +48,11 @@ def test_pmc_summary_calibrates_on_the_pack_copy(tmp_path, monkeypatch):
     assert s["hbm_bytes_per_dispatch"] == round(1001.0 * 1024 * 2 + 10.0 * 1024)
     assert s["kernel_source_hash"] == bench.kernel_source_hash()
     # the bench line takes the traffic only while the kernel source is the one measured
-    assert bench.measured_traffic(0) == s["hbm_bytes_per_dispatch"]
+    assert bench.measured_traffic(cfg) == s["hbm_bytes_per_dispatch"]
     s["kernel_source_hash"] = "0" * 16
     with open(tmp_path / "pmc.json", "w") as f:
         json.dump(s, f)
-    assert bench.measured_traffic(0) is None
+    assert bench.measured_traffic(cfg) is None
 
 
 def test_pmc_summary_rejects_a_copy_of_unknown_size(tmp_path, monkeypatch):
@@ -64,3 +64,17 @@ def test_pmc_summary_rejects_a_copy_of_unknown_size(tmp_path, monkeypatch):
     with pytest.raises(SystemExit):
         bench.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), ["f", "w"], cfg)
     assert not os.path.exists(tmp_path / "pmc.json")
+
+
+def test_a_roofline_fraction_above_one_fails_the_run(capsys):
+    """A fraction above 1 means the timed interval missed the kernel's work."""
+    bench.emit({"metric": "m", "roofline": {"frac": 0.64}})
+    with pytest.raises(SystemExit) as e:
+        bench.emit({"metric": "m", "roofline": {"frac": 4.3}})
+    assert e.value.code == 3
+    assert capsys.readouterr().out.count('"metric"') == 2   # the line is still printed
+
+
+def test_percentile_stats():
+    s = bench.pct_stats(list(range(1, 101)))
+    assert s["median"] == 50.5 and s["p10"] == 10.9 and s["p90"] == 90.1 and s["mean"] == 50.5

@@ -2,7 +2,8 @@
 
 Usage: ``python -m w8a8_quantized_decode_amd.build`` (or ``build()`` from Python).
 Every source in ``csrc/`` is compiled with hipcc as HIP for gfx950 and linked into
-``w8a8_quantized_decode_amd/liba8w8.so``.
+``w8a8_quantized_decode_amd/liba8w8.so``; the measurement aid in ``measure/`` (the
+streaming-read ceiling that bench.py reports) becomes ``libmeasure.so``.
 """
 
 from __future__ import annotations
@@ -17,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "liba8w8.so")
+MEASURE = os.path.join(PKG, "measure")
+MEASURE_LIB = os.path.join(PKG, "libmeasure.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
@@ -56,7 +59,8 @@ def sources() -> list[str]:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+    obj = os.path.join(OBJ_DIR, os.path.basename(os.path.dirname(src)) + "_" +
+                       os.path.basename(src) + ".o")
     cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + FLAGS + FILE_FLAGS.get(
         os.path.basename(src), [])
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -77,8 +81,16 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    msrcs = sorted(os.path.join(MEASURE, f) for f in os.listdir(MEASURE) if f.endswith(".hip"))
+    mobjs = [_compile(f) for f in msrcs]
+    tmp = MEASURE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp] + mobjs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, MEASURE_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {MEASURE_LIB}", file=sys.stderr)
     return LIB
 
 
