@@ -52,6 +52,7 @@ constexpr int64_t kBfMaxK = int64_t(kBfUnits) * 8 * kDcCtlThreads;   // 6144
 constexpr int64_t kF32MaxK = int64_t(kF32Units) * 4 * kDcCtlThreads; // 18432
 constexpr int kSlotWords = 4 * kWave;            // tagged 64-bit words per matrix per piece
 constexpr size_t kDcMaxLds = 150 * 1024;
+constexpr size_t kDcLdsPerCu = 160 * 1024;
 // Leftover-quarter steps a control wave requests before its prologue and holds in
 // registers meanwhile (the rest of its share follows after the prologue), sized within
 // the register budget of a 1024-thread workgroup: Qwen3-14B has 5 steps per control wave
@@ -69,6 +70,22 @@ struct DcSmem {
   float sw[kDcMaxTiles + 1][2][16];                 // channel scales (slot kDcMaxTiles: leftover)
   uint16_t res[kDcMaxTiles + 1][kFuseMaxRows][16];  // residual
 };
+
+// Agent-coherent tagged words of the leftover exchange (64-bit: tag in the high half, an
+// INT32 sum in the low half), four per lane, laid out component-major: word c * 64 + lane.
+__device__ __forceinline__ void store_tagged_lanes(uint64_t* block, int lane, i32x4 v, uint32_t tag) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    __hip_atomic_store(block + c * kWave + lane, (uint64_t(tag) << 32) | uint32_t(v[c]),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ TaggedX4 load_tagged_lanes(const uint64_t* block, int lane) {
+  TaggedX4 t;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    t.w[c] = __hip_atomic_load(block + c * kWave + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return t;
+}
 
 // LDS hand-offs between waves that may have global loads in flight.  The workgroup-scope
 // fences and atomic loads of the memory model also wait for every outstanding global load
@@ -712,8 +729,18 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
       i32x4 lacc[NMAT];
 #pragma unroll
       for (int i = 0; i < NMAT; ++i) lacc[i] = i32x4{0, 0, 0, 0};
-      for (int32_t s0 = ls0; s0 < ls1; s0 += V) {
-        if (s0 != ls0) load_lo(s0);
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        if (ls0 + u < ls1) {
+          const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ls0 + u) * 64);
+          const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < NMAT; ++i) lacc[i] = mfma_i8(lw[u][i], bv, lacc[i]);
+        }
+      }
+      // Steps past the V requested early (Down: 5 of its 17) load now.
+      for (int32_t s0 = ls0 + V; s0 < ls1; s0 += V) {
+        load_lo(s0);
 #pragma unroll
         for (int u = 0; u < V; ++u) {
           if (s0 + u < ls1) {
@@ -788,24 +815,42 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
         for (int w = 0; w < kDcCtl; ++w)
           piece[i] += *reinterpret_cast<const i32x4*>(lred + w * kPart + (i * kWave + lane) * 4);
       }
+      // Slot block layout: word c * 64 + lane holds component c of the lane's sums, so
+      // each store instruction writes 512 contiguous bytes (whole lines).
       if (qq != 0) {
 #pragma unroll
         for (int i = 0; i < NMAT; ++i)
-          store_tagged(slots + (int64_t(b) * NMAT + i) * kSlotWords + lane * 4, piece[i], tag32);
+          store_tagged_lanes(slots + (int64_t(b) * NMAT + i) * kSlotWords, lane, piece[i], tag32);
       } else {
-        for (int attempt = 0; attempt < (1 << 16) && !ok; ++attempt) {
+        // Poll one word per neighbour (lanes 0-2: word 0 of its first block, the first
+        // one it writes) until each carries the call's tag, then read every word; a word
+        // still missing sends the wave back to the full read.  (A full read as the first
+        // attempt measured slower: when it fails, it costs a round trip under the weight
+        // stream before the polling starts.)  Every wait is bounded.
+        bool seen = false;
+        for (int attempt = 0; attempt < (1 << 16) && !seen; ++attempt) {
+          bool mine = true;
+          if (lane < 3) {
+            const uint64_t w0 = __hip_atomic_load(slots + int64_t(b + 1 + lane) * NMAT * kSlotWords,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            mine = uint32_t(w0 >> 32) == tag32;
+          }
+          seen = __builtin_amdgcn_ballot_w64(!mine) == 0;
+          if (!seen) __builtin_amdgcn_s_sleep(8);
+        }
+        for (int attempt = 0; attempt < (1 << 12) && seen && !ok; ++attempt) {
           bool all = true;
 #pragma unroll
           for (int j = 0; j < 3; ++j)
 #pragma unroll
             for (int i = 0; i < NMAT; ++i) {
               const TaggedX4 tw =
-                  load_tagged(slots + (int64_t(b + 1 + j) * NMAT + i) * kSlotWords + lane * 4);
+                  load_tagged_lanes(slots + (int64_t(b + 1 + j) * NMAT + i) * kSlotWords, lane);
               got[j][i] = i32x4{0, 0, 0, 0};
               add_tagged(got[j][i], tw, tag32, all);
             }
           ok = __builtin_amdgcn_ballot_w64(!all) == 0;
-          if (!ok) __builtin_amdgcn_s_sleep(8);
+          if (!ok) __builtin_amdgcn_s_sleep(2);
         }
       }
     }
@@ -918,7 +963,9 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom
   g.stage_g = static_cast<int32_t>(kBfUnits * unit_bytes);
   size_t lds = size_t(g.lred_off) + size_t(kDcCtl) * part;
   if (codes + stage > lds) lds = codes + stage;
-  if (lds > kDcMaxLds) return false;
+  // Dynamic LDS plus the kernel's static LDS within the CU's 160 KB.
+  const size_t stat = sizeof(DcSmem);
+  if (lds > kDcMaxLds || lds + stat > kDcLdsPerCu) return false;
   g.lds = static_cast<int32_t>(lds);
   return true;
 }
