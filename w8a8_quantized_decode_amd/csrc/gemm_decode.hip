@@ -57,7 +57,9 @@ constexpr size_t kDcLdsPerCu = 160 * 1024;
 // registers meanwhile (the rest of its share follows after the prologue), sized within
 // the register budget of a 1024-thread workgroup: Qwen3-14B has 5 steps per control wave
 // (K = 5120) and 17 for Down (K = 17408).
-constexpr int lo_steps(int epi) { return epi == EPI_DOWN ? 12 : (epi == EPI_SILU ? 5 : 8); }
+constexpr int lo_steps(int epi) { return epi == EPI_DOWN ? 12 : 5; }
+// ... and steps requested into LDS beside them (Down only: one weight matrix).
+constexpr int lo_lds_steps(int epi) { return epi == EPI_DOWN ? 5 : 0; }
 
 struct DcSmem {
   double sum_slot[kFuseMaxRows][kDcCtl];
@@ -66,6 +68,9 @@ struct DcSmem {
   int ctl_sync;        // control-wave barrier counter
   int lo_arrive;       // control waves done with their share of the leftover quarter
   int pf_done;         // control waves done storing the epilogue inputs
+  int scales_ready;    // Down, one row: the row scale is in row_scale[0]
+  int task_next;       // ... next 64-chunk code task
+  int task_done;       // ... code tasks finished
   int codes_ready;     // set by the control waves once the codes are in LDS
   float sw[kDcMaxTiles + 1][2][16];                 // channel scales (slot kDcMaxTiles: leftover)
   uint16_t res[kDcMaxTiles + 1][kFuseMaxRows][16];  // residual
@@ -336,24 +341,29 @@ __device__ void ctl_row_bf16(const StreamKArgs& p, DcSmem& sm, int8_t* act, int 
   }
 }
 
-// Partial maxima of |h| per 16-channel tile of the producing GEMM: [npmax, M].
+// Partial maxima of |h| per 16-channel tile of the producing GEMM: [npmax, M].  The first
+// kPmWords of them are copied straight into an LDS array of their own (pm_lds), words
+// e = u * 1024 + ct * 4 + i at pm_lds[e]; being a separate LDS object, it does not make
+// the compiler wait for these copies where it reads other LDS, and being loads it does
+// not make it wait for later loads where it reads these.
 constexpr int kPmUnits = 2;  // 4-value units per control thread (8 * 256 = 2048 words)
-struct PmRegs {
-  f32x4 v[kPmUnits];
-};
+constexpr int kPmWords = kPmUnits * 4 * kDcCtlThreads;
 
-__device__ __forceinline__ void fetch_pmax(const StreamKArgs& p, PmRegs& r) {
-  const int ct = threadIdx.x;
+__device__ __forceinline__ void stage_pmax(const StreamKArgs& p, float* pm_lds) {
+  const int ct = threadIdx.x, w = ct / kWave;
   const int64_t n = p.npmax * p.M;
 #pragma unroll
   for (int u = 0; u < kPmUnits; ++u) {
     const int64_t e = int64_t(u) * 4 * kDcCtlThreads + ct * 4;
-    r.v[u] = *reinterpret_cast<const f32x4*>(p.pmax + (e < n ? e : 0));
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(p.pmax + (e < n ? e : 0)),
+                                     reinterpret_cast<__shared__ uint32_t*>(
+                                         pm_lds + (u * kDcCtlThreads + w * kWave) * 4),
+                                     16, 0, 0);
   }
 }
 
 // Row scales of the requantized input from the partial maxima (all rows at once).
-__device__ void ctl_requant_scales(const StreamKArgs& p, DcSmem& sm, const PmRegs& r, bool taps,
+__device__ void ctl_requant_scales(const StreamKArgs& p, DcSmem& sm, const float* pm_lds, bool taps,
                                    int& gen) {
   const int ct = threadIdx.x, wave = ct / kWave;
   // Word e of the [npmax, M] table belongs to row e % M (32-bit: npmax * M < 2^26).
@@ -364,13 +374,14 @@ __device__ void ctl_requant_scales(const StreamKArgs& p, DcSmem& sm, const PmReg
 #pragma unroll
   for (int u = 0; u < kPmUnits; ++u) {
     const uint32_t e0 = uint32_t(u) * 4 * kDcCtlThreads + uint32_t(ct) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(pm_lds + e0);
     uint32_t m = e0 % Mu;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (e0 + i < n) {
 #pragma unroll
         for (int mm = 0; mm < kFuseMaxRows; ++mm)
-          if (uint32_t(mm) == m) mx[mm] = fmaxf(mx[mm], r.v[u][i]);
+          if (uint32_t(mm) == m) mx[mm] = fmaxf(mx[mm], v[i]);
       }
       m = m + 1 == Mu ? 0 : m + 1;
     }
@@ -418,6 +429,81 @@ __device__ void ctl_row_f32(const StreamKArgs& p, const DcSmem& sm, int8_t* act,
       if (taps && p.tap_q) *reinterpret_cast<uint32_t*>(p.tap_q + int64_t(m) * p.K + k) = c;
     }
   }
+}
+
+// Down with one row: the codes of the staged FP32 row in tasks of 128 chunks (chunk c = the
+// four values from k = 4c, staged at hs + 16c), which any wave takes from an LDS counter
+// until none is left: the control waves right after the row scale, the stream waves as
+// soon as their first weight batch is requested.  A wave counts its finished tasks once,
+// when the counter runs out.
+// Wave-level counter updates: one add per wave, made by lane 0 with the execution mask
+// narrowed inside the asm block and restored there, so the caller's control flow has no
+// lane-dependent branch (a loop around such a branch may be split by lane, and a copy that
+// lane 0 does not run would never see the counter move).  The fetch returns lane 0's old
+// value to every lane.
+__device__ __forceinline__ int lds_fetch_add_wave(int* p, int v) {
+  int old;
+  uint64_t saved;
+  __asm__ __volatile__(
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "s_nop 1\n\t"
+      "ds_add_rtn_u32 %0, %2, %3\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b64 exec, %1\n\t"
+      "s_nop 1"
+      : "=&v"(old), "=&s"(saved)
+      : "v"(lds_addr(p)), "v"(v)
+      : "memory");
+  return __builtin_amdgcn_readlane(old, 0);
+}
+__device__ __forceinline__ void lds_add_wave(int* p, int v) {
+  uint64_t saved;
+  __asm__ __volatile__(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "s_nop 1\n\t"
+      "ds_add_u32 %1, %2\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b64 exec, %0\n\t"
+      "s_nop 1"
+      : "=&s"(saved)
+      : "v"(lds_addr(p)), "v"(v)
+      : "memory");
+}
+
+constexpr int kTaskChunks = 2 * kWave;   // chunks per code task (two per lane)
+
+__device__ __forceinline__ int code_tasks(int64_t K) {
+  return static_cast<int>((K / 4 + kTaskChunks - 1) / kTaskChunks);
+}
+
+__device__ void codes_tasks_f32(const StreamKArgs& p, DcSmem& sm, int8_t* act, const int8_t* hs,
+                                bool taps) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const float s = sm.row_scale[0];
+  const float rs = 1.0f / s;
+  const int32_t nchunks = static_cast<int32_t>(p.K / 4);
+  const int ntasks = code_tasks(p.K);
+  int done = 0;
+  for (;;) {
+    const int t = lds_fetch_add_wave(&sm.task_next, 1);
+    if (t >= ntasks) break;
+#pragma unroll
+    for (int j = 0; j < kTaskChunks / kWave; ++j) {
+      const int32_t c = t * kTaskChunks + j * kWave + lane;
+      if (c < nchunks) {
+        const f32x4 h = *reinterpret_cast<const f32x4*>(hs + int64_t(c) * 16);
+        const uint32_t q = codes4_fast(h, s, rs);
+        *reinterpret_cast<uint32_t*>(act + int64_t(c) * 4) = q;
+        if (taps && p.tap_q) *reinterpret_cast<uint32_t*>(p.tap_q + int64_t(c) * 4) = q;
+      }
+    }
+    ++done;
+  }
+  // The wave's codes are written before its tasks are counted.
+  lds_release_only();
+  if (done > 0) lds_add_wave(&sm.task_done, done);
 }
 
 // ------------------------------------------------------------------ epilogue
@@ -517,6 +603,9 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     sm.ctl_sync = 0;
     sm.lo_arrive = 0;
     sm.pf_done = 0;
+    sm.scales_ready = 0;
+    sm.task_next = 0;
+    sm.task_done = 0;
     sm.codes_ready = 0;
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the counters are set before barrier #1
   }
@@ -524,11 +613,11 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   // ---- phase 1: the control waves request row 0 of the input first, into LDS.
   int8_t* stage = lds + dg.acc_off;        // overlaps the accumulators (zeroed after it)
   int8_t* stage_g = stage + dg.stage_g;    // the RMSNorm gain
-  PmRegs pm;
+  __shared__ __align__(16) float pm_lds[kReq ? kPmWords : 4];
   uint32_t epoch = 0;
   if (wave < kDcCtl) {
     if constexpr (kReq) {
-      fetch_pmax(p, pm);
+      stage_pmax(p, pm_lds);
       stage_chunks<kF32Units>(p.hin, p.K * 4, stage);
     } else {
       stage_chunks<kBfUnits>(p.x, p.K * 2, stage);
@@ -600,47 +689,53 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
 #pragma unroll
     for (int i = 0; i < NMAT; ++i) acc[i] = i32x4{0, 0, 0, 0};
   };
+  auto step = [&](const i32x4 (&wu)[NMAT]) {
+    if (cf == cend) {
+      flush();
+      ++csg;
+      cend += Ss;
+    }
+    if (ck == St) ck = 0;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ck) * 64);
+    const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NMAT; ++i) acc[i] = mfma_i8(wu[i], bv, acc[i]);
+    ++cf;
+    ++ck;
+  };
+  // A batch that may run past the range's end (the last one).
   auto compute = [&](const i32x4 (&wv)[U][NMAT]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (cf < rend) {
-        if (cf == cend) {
-          flush();
-          ++csg;
-          cend += Ss;
-        }
-        if (ck == St) ck = 0;
-        const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ck) * 64);
-        const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
+    for (int u = 0; u < U; ++u)
+      if (cf < rend) step(wv[u]);
+  };
+  // A batch wholly inside the range (no range test).
+  auto compute_full = [&](const i32x4 (&wv)[U][NMAT]) {
 #pragma unroll
-        for (int i = 0; i < NMAT; ++i) acc[i] = mfma_i8(wv[u][i], bv, acc[i]);
-        ++cf;
-        ++ck;
-      }
-    }
+    for (int u = 0; u < U; ++u) step(wv[u]);
   };
   // Batches 0 and 1 are requested by the caller; this streams the rest and flushes.
   auto stream_rest = [&](i32x4 (&wA)[U][NMAT], i32x4 (&wB)[U][NMAT]) {
     int32_t i = 0;
-    for (; i + 3 < nb; i += 2) {
-      compute(wA);
+    for (; i + 3 < nb; i += 2) {   // batches i and i + 1 are whole
+      compute_full(wA);
       __builtin_amdgcn_sched_barrier(0);
       load_batch(wA, i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      compute(wB);
+      compute_full(wB);
       __builtin_amdgcn_sched_barrier(0);
       load_batch(wB, i + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (nb - i == 3) {
-      compute(wA);
+      compute_full(wA);
       __builtin_amdgcn_sched_barrier(0);
       load_batch(wA, i + 2);
       __builtin_amdgcn_sched_barrier(0);
-      compute(wB);
+      compute_full(wB);
       compute(wA);
     } else {
-      compute(wA);
+      compute_full(wA);
       compute(wB);
     }
     if (rn > 0) flush();
@@ -648,13 +743,49 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
 
   if (wave >= kDcCtl) {
     // ================================================================= stream waves
-    i32x4 wA[U][NMAT], wB[U][NMAT];
-    load_batch(wA, 0);
-    load_batch(wB, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_wait_flag(&sm.codes_ready, 1);   // the codes are in LDS, the accumulators cleared
-    __builtin_amdgcn_sched_barrier(0);
-    stream_rest(wA, wB);
+    // Down with one row: help with the codes once the first batch is requested.
+    const bool help = kReq && p.M == 1;
+    auto help_codes = [&]() {
+      if (help) {
+        lds_wait_flag(&sm.scales_ready, 1);
+        codes_tasks_f32(p, sm, act, lds + dg.acc_off, taps);
+      }
+    };
+    // A stream wave has no memory operation in flight before its first batch, so waiting
+    // until at most that batch is outstanding costs nothing.  It tells the compiler that
+    // the control waves' LDS-DMA requests (which it cannot tell apart from this wave's
+    // own) are done; while it believes one is in flight, every wait for a weight it
+    // emits waits for all loads, and the two batches no longer overlap.
+    auto after_first_batch = [&]() {
+      __asm__ __volatile__("" ::: "memory");
+      constexpr int kB = U * NMAT;   // vmcnt(kB); expcnt and lgkmcnt unconstrained
+      __builtin_amdgcn_s_waitcnt((kB & 0xF) | 0x0F70 | ((kB >> 4) << 14));
+      __asm__ __volatile__("" ::: "memory");
+    };
+    if (nb <= 1) {
+      // A range of one batch (O and single-tile QKV workgroups at Qwen3-14B shapes):
+      // no second batch, whose loads would only re-read the last step.
+      i32x4 wA[U][NMAT];
+      load_batch(wA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      after_first_batch();
+      help_codes();
+      lds_wait_flag(&sm.codes_ready, 1);   // the codes are in LDS, the accumulators cleared
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wA);
+      if (rn > 0) flush();
+    } else {
+      i32x4 wA[U][NMAT], wB[U][NMAT];
+      load_batch(wA, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      after_first_batch();
+      help_codes();
+      load_batch(wB, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_wait_flag(&sm.codes_ready, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      stream_rest(wA, wB);
+    }
   } else {
     // ================================================================= control waves
     // The leftover quarter's weights are requested right behind the row: the control waves
@@ -668,6 +799,24 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     const int32_t ls0 = qq * Q + wave * ql + (wave < qr ? wave : qr);
     const int32_t ls1 = ls0 + ql + (wave < qr ? 1 : 0);
     i32x4 lw[V][NMAT];
+    // Down's share is longer than its register budget: the next VL steps go straight into
+    // an LDS array of their own, requested with the rest.
+    constexpr int VL = lo_lds_steps(EPI);
+    __shared__ __align__(16) int8_t lo_lds[VL > 0 ? kDcCtl * VL * 1024 : 16];
+    auto load_lo_lds = [&]() {
+#pragma unroll
+      for (int u = 0; u < VL; ++u) {
+        const int32_t sv = ls0 + V + u;
+        const int32_t sq = sv < ls1 ? sv : ls1 - 1;
+        const int64_t o = (LAYOUT == LAYOUT_TILED) ? (int64_t(lt) * St + sq) * 1024
+                                                   : int64_t(lt) * 16 * p.K + int64_t(sq) * 64;
+        // Lane l's 16 bytes land at lo_lds + (wave * VL + u) * 1024 + 16 * l.
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(w0l + o),
+                                         reinterpret_cast<__shared__ uint32_t*>(
+                                             lo_lds + (wave * VL + u) * 1024),
+                                         16, 0, 0);
+      }
+    };
     auto load_lo = [&](int32_t s0) {
 #pragma unroll
       for (int u = 0; u < V; ++u) {
@@ -678,12 +827,16 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
         if constexpr (NMAT == 2) lw[u][1] = ld16_stream(w1l + o);
       }
     };
-    // (Down: after the row scales, which need the partial maxima loaded before the row: the
-    // compiler's waits for those would otherwise also cover these loads.)
-    if (!kReq && dg.leftover) {
+    if (dg.leftover) {
+      // The LDS-bound steps first: this wave's last copy into LDS is then older than its
+      // register loads, and the wait below covers it.  (While the compiler counts a copy
+      // into LDS as possibly in flight, every wait it emits is for all loads: the row scales
+      // would wait for the leftover's weights.)
+      if constexpr (VL > 0) load_lo_lds();
       load_lo(ls0);
       __builtin_amdgcn_sched_barrier(0);
-      // The row (requested before these V * NMAT loads, which complete in order) has landed.
+      // The row, the partial maxima and the LDS-bound steps, requested before these V * NMAT
+      // loads, which complete in order, have landed.
       __asm__ __volatile__("" ::: "memory");
       constexpr int kAfter = V * NMAT;   // vmcnt(kAfter); expcnt and lgkmcnt unconstrained
       __builtin_amdgcn_s_waitcnt((kAfter & 0xF) | 0x0F70 | ((kAfter >> 4) << 14));
@@ -694,10 +847,17 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     int gen = 0;
     ctl_sync(sm, gen);    // ... and every control wave's
     if constexpr (kReq) {
-      ctl_requant_scales(p, sm, pm, taps, gen);
-      if (dg.leftover) load_lo(ls0);
+      ctl_requant_scales(p, sm, pm_lds, taps, gen);
       __builtin_amdgcn_sched_barrier(0);
-      ctl_row_f32(p, sm, act, 0, stage, taps);
+      if (p.M == 1) {
+        // One row: every wave takes code tasks (the stream waves once their first batch
+        // is requested); the row is dead when all tasks are done.
+        if (tid == 0) lds_set_flag(&sm.scales_ready, 1);
+        codes_tasks_f32(p, sm, act, stage, taps);
+        lds_wait_flag(&sm.task_done, code_tasks(p.K));
+      } else {
+        ctl_row_f32(p, sm, act, 0, stage, taps);
+      }
       for (int m = 1; m < p.M; ++m) {
         ctl_sync(sm, gen);  // row m - 1 read by every control wave
         stage_chunks<kF32Units>(p.hin + int64_t(m) * p.ldhin, p.K * 4, stage);
@@ -738,8 +898,19 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
           for (int i = 0; i < NMAT; ++i) lacc[i] = mfma_i8(lw[u][i], bv, lacc[i]);
         }
       }
-      // Steps past the V requested early (Down: 5 of its 17) load now.
-      for (int32_t s0 = ls0 + V; s0 < ls1; s0 += V) {
+      if constexpr (VL > 0) {
+#pragma unroll
+        for (int u = 0; u < VL; ++u) {
+          if (ls0 + V + u < ls1) {
+            const i32x4 wv = *reinterpret_cast<const i32x4*>(lo_lds + (wave * VL + u) * 1024 + lane * 16);
+            const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ls0 + V + u) * 64);
+            const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
+            lacc[0] = mfma_i8(wv, bv, lacc[0]);
+          }
+        }
+      }
+      // Steps past those requested early (shapes with longer quarters) load now.
+      for (int32_t s0 = ls0 + V + VL; s0 < ls1; s0 += V) {
         load_lo(s0);
 #pragma unroll
         for (int u = 0; u < V; ++u) {
@@ -964,7 +1135,8 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom
   size_t lds = size_t(g.lred_off) + size_t(kDcCtl) * part;
   if (codes + stage > lds) lds = codes + stage;
   // Dynamic LDS plus the kernel's static LDS within the CU's 160 KB.
-  const size_t stat = sizeof(DcSmem);
+  const size_t stat = sizeof(DcSmem) +
+                      (epi == EPI_DOWN ? kPmWords * 4 + size_t(kDcCtl) * lo_lds_steps(EPI_DOWN) * 1024 : 32);
   if (lds > kDcMaxLds || lds + stat > kDcLdsPerCu) return false;
   g.lds = static_cast<int32_t>(lds);
   return true;
