@@ -411,6 +411,38 @@ __device__ void ctl_requant_scales(const StreamKArgs& p, DcSmem& sm, const float
   ctl_sync(sm, gen);
 }
 
+// One row: its scale from the partial maxima after a single exchange of the four control
+// waves' maxima; every control thread derives it (the maximum is exact in any order), and
+// thread 0 stores it for the stream waves and the epilogue.
+__device__ float ctl_requant_scale_one(const StreamKArgs& p, DcSmem& sm, const float* pm_lds,
+                                       bool taps, int& gen) {
+  const int ct = threadIdx.x, wave = ct / kWave;
+  const uint32_t n = static_cast<uint32_t>(p.npmax);
+  float mx = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kPmUnits; ++u) {
+    const uint32_t e0 = uint32_t(u) * 4 * kDcCtlThreads + uint32_t(ct) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(pm_lds + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e0 + i < n) mx = fmaxf(mx, v[i]);
+  }
+  for (uint32_t e = uint32_t(kPmUnits) * 4 * kDcCtlThreads + ct; e < n; e += kDcCtlThreads)
+    mx = fmaxf(mx, p.pmax[e]);
+  mx = wave_max_dpp(mx);
+  if ((ct & (kWave - 1)) == 0) sm.max_slot[0][wave] = mx;
+  ctl_sync(sm, gen);
+  float a = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDcCtl; ++w) a = fmaxf(a, sm.max_slot[0][w]);
+  const float s = a / 127.0f;
+  if (ct == 0) {
+    sm.row_scale[0] = s;
+    if (taps && p.tap_s) p.tap_s[0] = s;
+  }
+  return s;
+}
+
 // Codes of one FP32 row staged at hs into act[0..K): values k = u * 1024 + ct * 4 + i.
 __device__ void ctl_row_f32(const StreamKArgs& p, const DcSmem& sm, int8_t* act, int m,
                             const int8_t* hs, bool taps) {
@@ -479,9 +511,8 @@ __device__ __forceinline__ int code_tasks(int64_t K) {
 }
 
 __device__ void codes_tasks_f32(const StreamKArgs& p, DcSmem& sm, int8_t* act, const int8_t* hs,
-                                bool taps) {
+                                bool taps, float s) {
   const int lane = threadIdx.x & (kWave - 1);
-  const float s = sm.row_scale[0];
   const float rs = 1.0f / s;
   const int32_t nchunks = static_cast<int32_t>(p.K / 4);
   const int ntasks = code_tasks(p.K);
@@ -748,7 +779,7 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     auto help_codes = [&]() {
       if (help) {
         lds_wait_flag(&sm.scales_ready, 1);
-        codes_tasks_f32(p, sm, act, lds + dg.acc_off, taps);
+        codes_tasks_f32(p, sm, act, lds + dg.acc_off, taps, sm.row_scale[0]);
       }
     };
     // A stream wave has no memory operation in flight before its first batch, so waiting
@@ -847,15 +878,19 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     int gen = 0;
     ctl_sync(sm, gen);    // ... and every control wave's
     if constexpr (kReq) {
-      ctl_requant_scales(p, sm, pm_lds, taps, gen);
-      __builtin_amdgcn_sched_barrier(0);
       if (p.M == 1) {
         // One row: every wave takes code tasks (the stream waves once their first batch
         // is requested); the row is dead when all tasks are done.
-        if (tid == 0) lds_set_flag(&sm.scales_ready, 1);
-        codes_tasks_f32(p, sm, act, stage, taps);
+        const float s0 = ctl_requant_scale_one(p, sm, pm_lds, taps, gen);
+        if (tid == 0) {
+          lds_release_only();   // the row scale before the flag
+          lds_set_flag(&sm.scales_ready, 1);
+        }
+        codes_tasks_f32(p, sm, act, stage, taps, s0);
         lds_wait_flag(&sm.task_done, code_tasks(p.K));
       } else {
+        ctl_requant_scales(p, sm, pm_lds, taps, gen);
+        __builtin_amdgcn_sched_barrier(0);
         ctl_row_f32(p, sm, act, 0, stage, taps);
       }
       for (int m = 1; m < p.M; ++m) {
