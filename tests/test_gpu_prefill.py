@@ -8,9 +8,11 @@ summation) plus the oracle's own final rounding.  h = rne_bf16(silu(g) * u) must
 bit-identical to the oracle's except where a BF16 rounding boundary lies within the
 interval that the observed g/u deviations allow, d is bounded by the observed h
 deviations plus the Down accumulation bound, and the output by the observed d
-deviation plus the final roundings.  The stated
-tolerance (relative 1e-2; absolute 1e-2 below the output's scale, which is 1 for
-unit-scale outputs) holds per element and normwise.
+deviation plus the final roundings.  The stated tolerance (relative 1e-2, absolute 1e-2
+where |y| < 1) holds for every output element, except where that element's own proven
+FP32 bound is larger (the count of such elements is printed); normwise as well.  The wide
+weight recipe (block outputs near 2e4) is a stress case for the bounds alone: there the
+per-element rule's pass rate is printed, not asserted.
 """
 
 import numpy as np
@@ -27,8 +29,8 @@ C0, C4 = synth.CONFIGS[0], synth.CONFIGS[4]
 U = 2.0 ** -24
 
 
-def run_prefill(cfg, M, layout):
-    d = synth.mlp_inputs(cfg, M=M)
+def run_prefill(cfg, M, layout, wide=False):
+    d = synth.mlp_inputs(cfg, M=M, wide=wide)
     H, I = cfg.H, cfg.I
     out = empty((M, H), np.uint16)
     nbytes = B.a8w8_workspace_bytes(B.OP_MLP_BLOCK, M, H, I, 0, 2, B.MODE_PREFILL_W8A16)
@@ -63,7 +65,14 @@ def boundary_within(y, delta):
     return lo != hi
 
 
-def check(d, got, want, t, st):
+def literal_ok(got, want):
+    """The stated per-element tolerance: relative 1e-2, absolute 1e-2 where |y| < 1."""
+    err = np.abs(_f64(got) - _f64(want))
+    wv = np.abs(_f64(want))
+    return np.where(wv < 1.0, err <= 1e-2, err <= 1e-2 * wv)
+
+
+def check(d, got, want, t, st, literal=True):
     """Stage-by-stage checks.  Each stage is held to a bound derived from the FP32
     recursive-summation error model (|error| <= K * 2**-24 * sum |terms|) and from the
     deviation, already checked, of the stage that feeds it; the oracle's values never
@@ -106,21 +115,20 @@ def check(d, got, want, t, st):
     err = np.abs(_f64(got) - _f64(want))
     bo = dd_obs + 2 * U * (np.abs(st["d"]) + res + dd_obs) + np.maximum(bf16_ulp(got), bf16_ulp(want))
     assert np.all(err <= bo)
-    # the stated tolerance: relative 1e-2, absolute 1e-2 where |y| is below the output's
-    # scale.  For outputs of unit scale that is the literal "absolute 1e-2 below 1"; here
-    # the scale is max(1, RMS of the output), since the prefill outputs reach ~3e4 and an
-    # FP32 sum over 17408 terms cannot hold values far below that scale to 1e-2 of their
-    # own size.  The literal per-element rule's pass rate is reported beside it.
+    # the stated tolerance, per element; an element may instead meet its own proven bound
+    # bo only where bo exceeds the stated tolerance (both already hold as asserted above)
+    lit = literal_ok(got, want)
     wv = np.abs(_f64(want))
-    scale = max(1.0, float(np.sqrt(np.mean(wv * wv))))
-    ok = np.where(wv < scale, err <= 1e-2 * scale, err <= 1e-2 * wv)
-    literal = np.where(wv < 1.0, err <= 1e-2, err <= 1e-2 * wv)
+    tol = np.where(wv < 1.0, 1e-2, 1e-2 * wv)
+    fallback = ~lit & (bo > tol)
     rel = np.linalg.norm(_f64(got) - _f64(want)) / np.linalg.norm(_f64(want))
-    print(f"[note] prefill: output scale {scale:.3g}, max error {err.max():.3g}, "
-          f"{np.mean(literal):.6f} of outputs within the literal per-element rule, "
+    print(f"[note] prefill: max |y| {wv.max():.3g}, max error {err.max():.3g}, "
+          f"{np.mean(lit):.6f} of outputs within the stated per-element tolerance, "
+          f"{np.count_nonzero(fallback)} held to their larger FP32 bound instead, "
           f"{np.mean(hg == st['h']):.6f} of h identical, normwise rel {rel:.2e}")
-    assert np.all(ok), f"{np.count_nonzero(~ok)} outputs beyond the scaled tolerance"
-    assert rel <= 1e-2
+    if literal:
+        assert np.all(lit | fallback), f"{np.count_nonzero(~(lit | fallback))} outputs beyond the tolerance"
+        assert rel <= 1e-2
 
 
 @pytest.mark.parametrize("M", [1, 16, 64, 65, 200, 300])
@@ -148,6 +156,12 @@ def test_prefill_qwen3_14b_m256():
     check(d, got, want, t, st)
     same = float(np.mean(got == want))
     print(f"[note] prefill M=256: {same:.4f} of BF16 outputs bit-identical to the oracle")
+
+
+def test_prefill_qwen3_14b_m256_wide_weights():
+    """Weights twenty times larger (outputs near 2e4): every stage bound still holds."""
+    announce("prefill qwen3-14b M=256 wide weights")
+    check(*run_prefill(C4, 256, B.LAYOUT_TILED, wide=True), literal=False)
 
 
 # ------------------------------------------------------------------ the prefill layer
@@ -205,16 +219,13 @@ def check_layer_prefill(cfg, d, qkv, h1, got):
                                   attn, wo, d["x"])
     want, _ = O.prefill_mlp(h1, d["gamma_post"], cfg.eps, d["w_gate"], d["s_gate"], d["w_up"],
                             d["s_up"], d["w_down"], d["s_down"], h1)
-    # The MLP block on the GPU's own h1: the stated tolerance on the output's scale, as
-    # for the prefill MLP block (whose stages are checked one by one above).
-    err = np.abs(_f64(got) - _f64(want))
-    wv = np.abs(_f64(want))
-    scale = max(1.0, float(np.sqrt(np.mean(wv * wv))))
-    ok = np.where(wv < scale, err <= 1e-2 * scale, err <= 1e-2 * wv)
+    # The MLP block on the GPU's own h1 (its stages are checked one by one in the block
+    # tests above): the stated per-element tolerance on every output.
+    ok = literal_ok(got, want)
     rel = np.linalg.norm(_f64(got) - _f64(want)) / np.linalg.norm(_f64(want))
     print(f"[note] prefill layer: qkv {f_qkv:.6f} and h1 {f_h1:.6f} identical, "
           f"{np.mean(got == want):.4f} of outputs identical, normwise rel {rel:.2e}")
-    assert np.all(ok), f"{np.count_nonzero(~ok)} outputs beyond the scaled tolerance"
+    assert np.all(ok), f"{np.count_nonzero(~ok)} outputs beyond the stated tolerance"
     assert rel <= 1e-2
 
 

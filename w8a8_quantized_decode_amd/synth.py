@@ -9,8 +9,15 @@ Distributions (the workloads of the Qwen3-14B A8W8 decode linears):
 * activations ``x`` and residual ``res``: FP32 standard normal, stored as BF16 by
   keeping the top 16 bits of the FP32 pattern (truncation, a sampling choice);
 * RMSNorm gains: FP32 uniform on [0.5, 1.5), truncated to BF16 the same way;
-* weights: INT8 uniform on [-127, 127] (255 values), ``[N_out, K_in]`` row-major;
-* per-output-channel scales: uniform on [1e-3, 1e-2), stored as FP32.
+* weights: INT8 codes from a discretized normal, rint(32 z) for standard-normal z,
+  clipped to [-127, 127], ``[N_out, K_in]`` row-major;
+* per-output-channel scales: uniform on [4e-4, 8e-4), stored as FP32.
+
+With these, a dequantized weight has a standard deviation near 0.02 and a layer's
+outputs are of order one, as in a trained model's linears.  The ``wide`` variant keeps
+the first recipe (codes uniform on [-127, 127], scales uniform on [1e-3, 1e-2)): weights
+twenty times larger and block outputs near 2e4, a stress case for the FP32 accumulation
+bounds.
 """
 
 from __future__ import annotations
@@ -48,12 +55,16 @@ def uniform_bf16(seed: int, shape, lo: float, hi: float) -> np.ndarray:
     return _trunc_bf16(_rng(seed).uniform(lo, hi, size=shape).astype(np.float32))
 
 
-def int8_weights(seed: int, shape) -> np.ndarray:
-    return _rng(seed).integers(-127, 128, size=shape, dtype=np.int8)
+def int8_weights(seed: int, shape, wide: bool = False) -> np.ndarray:
+    if wide:
+        return _rng(seed).integers(-127, 128, size=shape, dtype=np.int8)
+    z = _rng(seed).standard_normal(size=shape, dtype=np.float32)
+    return np.clip(np.rint(z * np.float32(32.0)), -127, 127).astype(np.int8)
 
 
-def channel_scales(seed: int, n: int) -> np.ndarray:
-    return _rng(seed).uniform(1e-3, 1e-2, size=(n,)).astype(np.float32)
+def channel_scales(seed: int, n: int, wide: bool = False) -> np.ndarray:
+    lo, hi = (1e-3, 1e-2) if wide else (4e-4, 8e-4)
+    return _rng(seed).uniform(lo, hi, size=(n,)).astype(np.float32)
 
 
 @dataclass(frozen=True)
@@ -89,18 +100,19 @@ CONFIGS = [
 ]
 
 
-def mlp_inputs(cfg: Config, layer: int = 0, M: int | None = None, with_x: bool = True):
+def mlp_inputs(cfg: Config, layer: int = 0, M: int | None = None, with_x: bool = True,
+               wide: bool = False):
     """Seeded MLP-block tensors as numpy arrays (BF16 as uint16 bits)."""
     c, H, I = cfg.index, cfg.H, cfg.I
     M = cfg.M if M is None else M
     d = {
         "gamma_post": uniform_bf16(seed_for(c, layer, "gamma_post"), (H,), 0.5, 1.5),
-        "w_gate": int8_weights(seed_for(c, layer, "w_gate"), (I, H)),
-        "s_gate": channel_scales(seed_for(c, layer, "s_gate"), I),
-        "w_up": int8_weights(seed_for(c, layer, "w_up"), (I, H)),
-        "s_up": channel_scales(seed_for(c, layer, "s_up"), I),
-        "w_down": int8_weights(seed_for(c, layer, "w_down"), (H, I)),
-        "s_down": channel_scales(seed_for(c, layer, "s_down"), H),
+        "w_gate": int8_weights(seed_for(c, layer, "w_gate"), (I, H), wide),
+        "s_gate": channel_scales(seed_for(c, layer, "s_gate"), I, wide),
+        "w_up": int8_weights(seed_for(c, layer, "w_up"), (I, H), wide),
+        "s_up": channel_scales(seed_for(c, layer, "s_up"), I, wide),
+        "w_down": int8_weights(seed_for(c, layer, "w_down"), (H, I), wide),
+        "s_down": channel_scales(seed_for(c, layer, "s_down"), H, wide),
     }
     if with_x:
         d["x"] = normal_bf16(seed_for(c, layer, "x"), (M, H))
@@ -108,16 +120,17 @@ def mlp_inputs(cfg: Config, layer: int = 0, M: int | None = None, with_x: bool =
     return d
 
 
-def layer_inputs(cfg: Config, layer: int = 0, M: int | None = None, with_x: bool = True):
+def layer_inputs(cfg: Config, layer: int = 0, M: int | None = None, with_x: bool = True,
+                 wide: bool = False):
     """Seeded tensors of one full layer (QKV, O and the MLP block)."""
     c, H = cfg.index, cfg.H
-    d = mlp_inputs(cfg, layer, M, with_x)
+    d = mlp_inputs(cfg, layer, M, with_x, wide)
     d.pop("res", None)
     d["gamma_in"] = uniform_bf16(seed_for(c, layer, "gamma_in"), (H,), 0.5, 1.5)
-    d["w_qkv"] = int8_weights(seed_for(c, layer, "w_qkv"), (cfg.n_qkv, H))
-    d["s_qkv"] = channel_scales(seed_for(c, layer, "s_qkv"), cfg.n_qkv)
-    d["w_o"] = int8_weights(seed_for(c, layer, "w_o"), (H, cfg.n_q_heads * cfg.head_dim))
-    d["s_o"] = channel_scales(seed_for(c, layer, "s_o"), H)
+    d["w_qkv"] = int8_weights(seed_for(c, layer, "w_qkv"), (cfg.n_qkv, H), wide)
+    d["s_qkv"] = channel_scales(seed_for(c, layer, "s_qkv"), cfg.n_qkv, wide)
+    d["w_o"] = int8_weights(seed_for(c, layer, "w_o"), (H, cfg.n_q_heads * cfg.head_dim), wide)
+    d["s_o"] = channel_scales(seed_for(c, layer, "s_o"), H, wide)
     return d
 
 
