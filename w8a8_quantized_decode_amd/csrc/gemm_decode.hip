@@ -32,7 +32,8 @@
 // G/4 tiles are cut into K quarters, one per workgroup; each quarter is computed early by
 // the control waves and published as tagged words, and the owner of quarter 0 adds the
 // four and runs that tile's epilogue long before the stream ends.  Otherwise the tiles
-// are dealt whole, q or q + 1 per workgroup (QKV: 448 tiles, O: 320 tiles).
+// are dealt whole, q or q + 1 per workgroup; QKV and O take a smaller grid that divides
+// their tiles (448 = 224 x 2, 320 = 160 x 2), so every workgroup has the same share.
 #include "device_common.h"
 #include "internal.h"
 
@@ -1143,7 +1144,18 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom
   // Prologue registers: the control waves hold a whole input row.
   if (epi == EPI_DOWN ? K > kF32MaxK : K > kBfMaxK) return false;
   if (T >= (int64_t(1) << 24) || St >= (int64_t(1) << 20)) return false;
-  const int64_t G = T < kDcMaxGrid ? T : kDcMaxGrid;
+  int64_t G = T < kDcMaxGrid ? T : kDcMaxGrid;
+  // QKV and O: equal whole tiles for every workgroup when a grid of at least 5/8 of the
+  // largest one divides the tiles (Qwen3-14B: QKV 448 = 224 x 2, O 320 = 160 x 2).  Measured
+  // on MI355X, a plain weight stream keeps its rate on 160 or more CUs, and O then needs no
+  // leftover exchange (its span fell from 8.0 to 6.9 us).  For Down the longer stream per
+  // workgroup cost more than the exchange it saves.
+  if ((epi == EPI_BF16 || epi == EPI_BF16_RES) && T > kDcMaxGrid)
+    for (int64_t gg = kDcMaxGrid; gg * 8 >= kDcMaxGrid * 5; --gg)
+      if (T % gg == 0 && T / gg <= kDcMaxTiles) {
+        G = gg;
+        break;
+      }
   const int64_t q = T / G, r = T % G;
   // Leftover quarters: the last G/4 tiles are split in K quarters, one per workgroup,
   // each inside one K partition.
