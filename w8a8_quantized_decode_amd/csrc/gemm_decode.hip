@@ -2,8 +2,9 @@
 // cores with the fused input quantization (RMSNorm + per-row quantization, or the
 // requantization of h for Down) and the fused dequant / SiLU / residual / split-K
 // epilogues.  It serves the layer chain and the MLP block at decode batch sizes
-// (M <= kFuseMaxRows) for the shapes it covers (plan_decode); the stream-K kernel in
-// gemm_streamk.hip serves the others.
+// (M <= kFuseMaxRows) for the shapes it covers (plan_decode), and, with the input codes
+// given (row-quantization kernels before it), up to kDcMaxRows rows when the codes fit
+// in LDS; the stream-K kernel in gemm_streamk.hip serves the others.
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
 // paths", What changed > Gate/Up INT8 path (INT8 x INT8 -> INT32 Gate/Up matmuls with
@@ -47,6 +48,7 @@ constexpr int kDcThreads = kDcWaves * kWave;
 constexpr int kDcCtlThreads = kDcCtl * kWave;
 constexpr int kDcMaxGrid = 256;
 constexpr int kDcMaxTiles = 5;                   // whole tiles per workgroup
+constexpr int kDcMaxRows = 16;                   // rows with given codes (one matrix-core tile)
 constexpr int kBfUnits = 3;                      // BF16 row: 8-value units per control thread
 constexpr int kF32Units = 18;                    // FP32 row: 4-value units per control thread
 constexpr int64_t kBfMaxK = int64_t(kBfUnits) * 8 * kDcCtlThreads;   // 6144
@@ -65,7 +67,7 @@ constexpr int lo_lds_steps(int epi) { return epi == EPI_DOWN ? 5 : 0; }
 struct DcSmem {
   double sum_slot[kFuseMaxRows][kDcCtl];
   float max_slot[kFuseMaxRows][kDcCtl];
-  float row_scale[kFuseMaxRows];
+  float row_scale[kDcMaxRows];
   int ctl_sync;        // control-wave barrier counter
   int lo_arrive;       // control waves done with their share of the leftover quarter
   int pf_done;         // control waves done storing the epilogue inputs
@@ -74,7 +76,7 @@ struct DcSmem {
   int task_done;       // ... code tasks finished
   int codes_ready;     // set by the control waves once the codes are in LDS
   float sw[kDcMaxTiles + 1][2][16];                 // channel scales (slot kDcMaxTiles: leftover)
-  uint16_t res[kDcMaxTiles + 1][kFuseMaxRows][16];  // residual
+  uint16_t res[kDcMaxTiles + 1][kDcMaxRows][16];    // residual
 };
 
 // Agent-coherent tagged words of the leftover exchange (64-bit: tag in the high half, an
@@ -251,6 +253,26 @@ __device__ __forceinline__ void stage_chunks(const void* src, int64_t nbytes, in
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(s8 + off),
                                      reinterpret_cast<__shared__ uint32_t*>(
                                          stage + (int64_t(u) * kDcCtlThreads + w * kWave) * 16),
+                                     16, 0, 0);
+  }
+}
+
+// Given codes (M rows of K bytes at a, row stride lda) copied into act[M][K] with direct
+// global-to-LDS loads: 1 KB units u = wave, wave + 4, ... of the contiguous LDS rows, lane
+// l taking chunk 64 u + l.  A unit past the codes' end writes into the accumulator area
+// behind them (zeroed after the copy) from a clamped source.
+__device__ __forceinline__ void stage_codes(const StreamKArgs& p, int8_t* act) {
+  const int ct = threadIdx.x, w = ct / kWave, l = ct & (kWave - 1);
+  const int64_t cpr = p.K / 16;                    // 16-byte chunks per row
+  const int64_t nch = p.M * cpr;
+  const int64_t units = (nch + kWave - 1) / kWave;
+  for (int64_t u = w; u < units; u += kDcCtl) {
+    const int64_t c = u * kWave + l;
+    const int64_t cc = c < nch ? c : 0;
+    const int64_t m = cc / cpr;
+    const int8_t* src = p.a + m * p.lda + (cc - m * cpr) * 16;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src),
+                                     reinterpret_cast<__shared__ uint32_t*>(act + u * kWave * 16),
                                      16, 0, 0);
   }
 }
@@ -647,13 +669,22 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   int8_t* stage_g = stage + dg.stage_g;    // the RMSNorm gain
   __shared__ __align__(16) float pm_lds[kReq ? kPmWords : 4];
   uint32_t epoch = 0;
+  // Given codes (rows quantized by an earlier kernel): copied as they are, with the row
+  // scales; no prologue arithmetic.
+  const bool codes_in = p.prologue == PRO_CODES;
+  float sa_row = 0.0f;
   if (wave < kDcCtl) {
-    if constexpr (kReq) {
-      stage_pmax(p, pm_lds);
-      stage_chunks<kF32Units>(p.hin, p.K * 4, stage);
+    if (codes_in) {
+      stage_codes(p, act);
+      if (tid < p.M) sa_row = p.sa[tid];
     } else {
-      stage_chunks<kBfUnits>(p.x, p.K * 2, stage);
-      if (p.gamma) stage_chunks<kBfUnits>(p.gamma, p.K * 2, stage_g);
+      if constexpr (kReq) {
+        stage_pmax(p, pm_lds);
+        stage_chunks<kF32Units>(p.hin, p.K * 4, stage);
+      } else {
+        stage_chunks<kBfUnits>(p.x, p.K * 2, stage);
+        if (p.gamma) stage_chunks<kBfUnits>(p.gamma, p.K * 2, stage_g);
+      }
     }
     epoch = *p.epoch_in;
   }
@@ -776,7 +807,7 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   if (wave >= kDcCtl) {
     // ================================================================= stream waves
     // Down with one row: help with the codes once the first batch is requested.
-    const bool help = kReq && p.M == 1;
+    const bool help = kReq && p.M == 1 && !codes_in;
     auto help_codes = [&]() {
       if (help) {
         lds_wait_flag(&sm.scales_ready, 1);
@@ -878,7 +909,9 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     }
     int gen = 0;
     ctl_sync(sm, gen);    // ... and every control wave's
-    if constexpr (kReq) {
+    if (codes_in) {
+      if (tid < p.M) sm.row_scale[tid] = sa_row;
+    } else if constexpr (kReq) {
       if (p.M == 1) {
         // One row: every wave takes code tasks (the stream waves once their first batch
         // is requested); the row is dead when all tasks are done.
@@ -972,7 +1005,7 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     // load is issued before the first store, so they cost one memory round trip.
     const int ct = tid;
     constexpr int kSwN = (kDcMaxTiles + 1) * 16 * NMAT;                  // <= 192
-    constexpr int kResN = (kDcMaxTiles + 1) * kFuseMaxRows * 16;         // 384
+    constexpr int kResN = (kDcMaxTiles + 1) * kDcMaxRows * 16;           // 1536
     constexpr int kResIt = (kResN + kDcCtlThreads - 1) / kDcCtlThreads;  // 2
     float swv = 0.0f;
     int32_t sw_t = -1;
@@ -991,8 +1024,8 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
 #pragma unroll
     for (int it = 0; it < kResIt; ++it) {
       const int e = ct + it * kDcCtlThreads;
-      r_slot[it] = e / (kFuseMaxRows * 16);
-      const int rem = e % (kFuseMaxRows * 16);
+      r_slot[it] = e / (kDcMaxRows * 16);
+      const int rem = e % (kDcMaxRows * 16);
       r_m[it] = rem / 16;
       r_c[it] = rem % 16;
       r_t[it] = -1;
@@ -1132,9 +1165,11 @@ hipError_t launch_l(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
 
 }  // namespace
 
-bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom& g) {
+bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, bool codes_in,
+                 DecodeGeom& g) {
   g = DecodeGeom{};
-  if (M < 1 || M > kFuseMaxRows || N % 16 || K % 64 || N <= 0) return false;
+  if (M < 1 || M > (codes_in ? kDcMaxRows : kFuseMaxRows) || N % 16 || K % 64 || N <= 0)
+    return false;
   const int nmat = epi == EPI_SILU ? 2 : 1;
   const int P = epi == EPI_DOWN ? parts : 1;
   const int64_t T = N / 16, St = K / 64;
@@ -1142,7 +1177,7 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom
   const int64_t Ss = St / P;
   if (P > 8) return false;
   // Prologue registers: the control waves hold a whole input row.
-  if (epi == EPI_DOWN ? K > kF32MaxK : K > kBfMaxK) return false;
+  if (!codes_in && (epi == EPI_DOWN ? K > kF32MaxK : K > kBfMaxK)) return false;
   if (T >= (int64_t(1) << 24) || St >= (int64_t(1) << 20)) return false;
   int64_t G = T < kDcMaxGrid ? T : kDcMaxGrid;
   // QKV and O: equal whole tiles for every workgroup when a grid of at least 5/8 of the
@@ -1177,7 +1212,7 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom
   g.lred_off = static_cast<int32_t>(codes + size_t(ntmax) * P * part);
   // Staging of the input row at acc_off: FP32 h (Down) or BF16 x followed by the gain.
   const size_t unit_bytes = size_t(kDcCtlThreads) * 16;
-  const size_t stage = epi == EPI_DOWN ? kF32Units * unit_bytes : 2 * kBfUnits * unit_bytes;
+  const size_t stage = codes_in ? 0 : epi == EPI_DOWN ? kF32Units * unit_bytes : 2 * kBfUnits * unit_bytes;
   g.stage_g = static_cast<int32_t>(kBfUnits * unit_bytes);
   size_t lds = size_t(g.lred_off) + size_t(kDcCtl) * part;
   if (codes + stage > lds) lds = codes + stage;

@@ -960,8 +960,9 @@ StreamKPlan plan_streamk(int epi, int64_t M, int64_t N, int64_t K, int parts, bo
   // Tagged slots: one 64-bit word (two INT32 elements) per partial sum.
   pl.slot_elems = 2 * size_t(pl.mgroups) * size_t(T * C + wgs) * size_t(nmat) * pl.mb * 4 * kWave;
   pl.done_elems = size_t(pl.mgroups) * size_t(T);
-  // Fused prologues at shapes the one-workgroup-per-CU kernel covers run on it.
-  if (fused && plan_decode(epi, M, N, K, P, pl.dec)) {
+  // Shapes the one-workgroup-per-CU kernel covers run on it: with the fused prologue, or
+  // with the codes given by the row-quantization kernels.
+  if (plan_decode(epi, M, N, K, P, !fused, pl.dec)) {
     pl.use_decode = 1;
     const size_t se = decode_slot_elems(pl.dec, nmat);
     if (se > pl.slot_elems) pl.slot_elems = se;

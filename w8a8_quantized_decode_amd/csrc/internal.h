@@ -179,8 +179,10 @@ struct DecodeGeom {
   int32_t stage_g;           // offset of the staged RMSNorm gain from acc_off (the staging area)
   int32_t lds;               // dynamic LDS bytes
 };
-// False when the shape is not covered (then the stream-K kernel runs).
-bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, DecodeGeom& g);
+// False when the shape is not covered (then the stream-K kernel runs).  codes_in: the
+// input codes and row scales are given (PRO_CODES) instead of quantized in the kernel.
+bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, bool codes_in,
+                 DecodeGeom& g);
 size_t decode_slot_elems(const DecodeGeom& g, int nmat);
 
 struct StreamKPlan {
