@@ -66,7 +66,8 @@ def test_quantize_rows_empty_is_noop():
 
 
 LINEAR_CASES = [(1, 16, 64), (1, 7168, 5120), (5, 48, 320), (16, 5120, 5120), (17, 64, 128),
-                (100, 32, 192), (64, 256, 17408), (1, 5120, 17408), (33, 80, 8704)]
+                (100, 32, 192), (64, 256, 17408), (1, 5120, 17408), (33, 80, 8704),
+                (3, 96, 2048), (16, 64, 1024), (12, 4096, 3072)]
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_CASES)

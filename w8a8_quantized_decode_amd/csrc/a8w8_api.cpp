@@ -108,6 +108,13 @@ ChainPlan make_plan(int64_t M, int64_t H, int64_t I, int64_t n_qkv, int split_k,
   return ok ? c : plans_for(M, H, I, n_qkv, split_k, layer, false);
 }
 
+// True when the GEMM reads its given codes from global memory in the 16-row tiled order
+// (the row-quantization kernel before it then writes them so).
+bool codes_tiled(const StreamKPlan& p) { return p.use_decode && p.dec.gcodes; }
+
+// Rows of a codes buffer: the tiled order always holds 16.
+size_t code_rows(int64_t M) { return size_t(M < 16 ? 16 : M); }
+
 // Layout: done words and tagged partial-sum slots, shared by the GEMMs (they run one
 // after another on the stream; done words and slot tags carry the GEMM's number), then
 // the intermediate activations.
@@ -148,18 +155,18 @@ Buffers carve(Carver& c, const ChainPlan& pl, int64_t M, int64_t H, int64_t I, i
   b.slots = c.take<int32_t>(slot_elems);
   if (layer) {
     if (!pl.fused) {
-      b.q_in = c.take<int8_t>(size_t(M) * H);
+      b.q_in = c.take<int8_t>(code_rows(M) * H);
       b.s_in = c.take<float>(size_t(M));
-      b.q_a = c.take<int8_t>(size_t(M) * H);
+      b.q_a = c.take<int8_t>(code_rows(M) * H);
       b.s_a = c.take<float>(size_t(M));
     }
     b.qkv = c.take<uint16_t>(size_t(M) * n_qkv);
     b.h1 = c.take<uint16_t>(size_t(M) * H);
   }
   if (!pl.fused) {
-    b.q_x = c.take<int8_t>(size_t(M) * H);
+    b.q_x = c.take<int8_t>(code_rows(M) * H);
     b.s_x = c.take<float>(size_t(M));
-    b.q_h = c.take<int8_t>(size_t(M) * I);
+    b.q_h = c.take<int8_t>(code_rows(M) * I);
     b.s_h = c.take<float>(size_t(M));
   }
   b.h = c.take<float>(size_t(M) * I);
@@ -316,10 +323,12 @@ a8w8_status run_mlp_prefill(const uint16_t* x, const uint16_t* gamma, float eps,
   return A8W8_OK;
 }
 
+// tiled: the codes in the 16-row tiled order a decode GEMM reads from global memory.
 hipError_t quant_kernel(const void* x, int64_t ldx, int f32, const uint16_t* gamma, float eps,
                         int64_t M, int64_t K, int8_t* q, float* s, float* xn_tap, int8_t* q_tap,
-                        float* s_tap, hipStream_t st) {
+                        float* s_tap, hipStream_t st, bool tiled = false) {
   QuantRowsArgs a{};
+  a.q_tiled = tiled ? 1 : 0;
   a.x = x;
   a.ldx = ldx;
   a.x_is_f32 = f32;
@@ -365,7 +374,7 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_POST));
     A8W8_HIP(quant_kernel(x, H, 0, gamma, eps, M, H, b.q_x, b.s_x, t ? t->xn : nullptr,
-                          t ? t->q_x : nullptr, t ? t->s_x : nullptr, st));
+                          t ? t->q_x : nullptr, t ? t->s_x : nullptr, st, codes_tiled(pl.gu)));
     A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_POST));
     g.prologue = PRO_CODES;
     g.a = b.q_x;
@@ -397,7 +406,7 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_REQUANT));
     A8W8_HIP(quant_kernel(b.h, I, 1, nullptr, 0.0f, M, I, b.q_h, b.s_h, nullptr,
-                          t ? t->q_h : nullptr, t ? t->s_h : nullptr, st));
+                          t ? t->q_h : nullptr, t ? t->s_h : nullptr, st, codes_tiled(pl.dn)));
     A8W8_HIP(tm.after(A8W8_KERNEL_REQUANT));
     d.prologue = PRO_CODES;
     d.a = b.q_h;
@@ -672,7 +681,7 @@ static a8w8_status layer_decode(const uint16_t* x_bf16, const uint16_t* gamma_in
     A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_IN));
     A8W8_HIP(quant_kernel(x_bf16, H, 0, gamma_in_bf16, eps, M, H, b.q_in, b.s_in,
                           taps ? taps->xn_in : nullptr, taps ? taps->q_in : nullptr,
-                          taps ? taps->s_in : nullptr, st));
+                          taps ? taps->s_in : nullptr, st, codes_tiled(pl.qkv)));
     A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_IN));
     g.prologue = PRO_CODES;
     g.a = b.q_in;
@@ -707,7 +716,8 @@ static a8w8_status layer_decode(const uint16_t* x_bf16, const uint16_t* gamma_in
   } else {
     A8W8_HIP(tm.before(A8W8_KERNEL_QUANT_ATTN));
     A8W8_HIP(quant_kernel(o_in, o_ld, 0, nullptr, 0.0f, M, H, b.q_a, b.s_a, nullptr,
-                          taps ? taps->q_attn : nullptr, taps ? taps->s_attn : nullptr, st));
+                          taps ? taps->q_attn : nullptr, taps ? taps->s_attn : nullptr, st,
+                          codes_tiled(pl.o)));
     A8W8_HIP(tm.after(A8W8_KERNEL_QUANT_ATTN));
     og.prologue = PRO_CODES;
     og.a = b.q_a;

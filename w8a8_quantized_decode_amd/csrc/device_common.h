@@ -36,6 +36,13 @@ __device__ __forceinline__ int64_t prefill_operand_index(int64_t m, int64_t k, i
          ((m & 31) + 32 * ((k >> 3) & 1)) * 8 + (k & 7);
 }
 
+// Decode codes in the weights' tiled operand order (one 16-row tile, rows past M unused):
+// one 1 KB block per 64-byte k step, lane l = (m % 16) + 16 * ((k % 64) / 16) holding
+// 16 bytes.  16 * K bytes for up to 16 rows.  Byte index of (m, k):
+__device__ __forceinline__ int64_t tiled_code_index(int64_t m, int64_t k) {
+  return (k >> 6) * 1024 + ((m & 15) + 16 * ((k >> 4) & 3)) * 16 + (k & 15);
+}
+
 // Low / high BF16 of a packed pair.
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {

@@ -257,23 +257,26 @@ __device__ __forceinline__ void stage_chunks(const void* src, int64_t nbytes, in
   }
 }
 
-// Given codes (M rows of K bytes at a, row stride lda) copied into act[M][K] with direct
-// global-to-LDS loads: 1 KB units u = wave, wave + 4, ... of the contiguous LDS rows, lane
-// l taking chunk 64 u + l.  A unit past the codes' end writes into the accumulator area
-// behind them (zeroed after the copy) from a clamped source.
-__device__ __forceinline__ void stage_codes(const StreamKArgs& p, int8_t* act) {
+// Given codes (M rows of K bytes at a, row stride lda) copied into act[M][act_ld] with
+// direct global-to-LDS loads: 1 KB units u = wave, wave + 4, ... of chunks (64 u + lane);
+// a unit lies inside one row when rows are padded (K / 16 chunks a multiple of 64), and
+// the rows are contiguous otherwise.  A unit past the codes' end writes into the
+// accumulator area behind them (zeroed after the copy) from a clamped source.
+__device__ __forceinline__ void stage_codes(const StreamKArgs& p, int8_t* act, int32_t act_ld) {
   const int ct = threadIdx.x, w = ct / kWave, l = ct & (kWave - 1);
-  const int64_t cpr = p.K / 16;                    // 16-byte chunks per row
-  const int64_t nch = p.M * cpr;
-  const int64_t units = (nch + kWave - 1) / kWave;
-  for (int64_t u = w; u < units; u += kDcCtl) {
-    const int64_t c = u * kWave + l;
-    const int64_t cc = c < nch ? c : 0;
-    const int64_t m = cc / cpr;
-    const int8_t* src = p.a + m * p.lda + (cc - m * cpr) * 16;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src),
-                                     reinterpret_cast<__shared__ uint32_t*>(act + u * kWave * 16),
-                                     16, 0, 0);
+  const int32_t cpr = static_cast<int32_t>(p.K / 16);   // 16-byte chunks per row
+  const int32_t nch = static_cast<int32_t>(p.M) * cpr;
+  const int32_t units = (nch + kWave - 1) / kWave;
+  for (int32_t u = w; u < units; u += kDcCtl) {
+    const int32_t c = u * kWave + l;
+    const int32_t cc = c < nch ? c : 0;
+    const int32_t m = cc / cpr;
+    const int8_t* src = p.a + int64_t(m) * p.lda + int64_t(cc - m * cpr) * 16;
+    const int32_t m0 = (u * kWave) / cpr;   // the unit's row (its first chunk's)
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const uint32_t*>(src),
+        reinterpret_cast<__shared__ uint32_t*>(act + m0 * act_ld + (u * kWave - m0 * cpr) * 16),
+        16, 0, 0);
   }
 }
 
@@ -626,10 +629,13 @@ __device__ __forceinline__ int32_t acc_elem(const int32_t* seg_acc, int mat, int
 }
 
 // ------------------------------------------------------------------ the kernel
-template <int EPI, int NMAT, int LAYOUT>
+// GC: the given codes are read from global memory with the weights (codes too large for
+// LDS: Down at 16 rows), one 16-byte code load per weight load, in batches of 4 steps.
+template <int EPI, int NMAT, int LAYOUT, bool GC>
 __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, DecodeGeom dg) {
   constexpr bool kReq = EPI == EPI_DOWN;   // FP32 input requantized with partial maxima
-  constexpr int U = NMAT == 2 ? 4 : 8;      // K steps per batch (8 loads of 16 bytes per lane)
+  constexpr int U = (NMAT == 2 || GC) ? 4 : 8;   // K steps per batch (8 loads of 16 bytes per lane)
+  constexpr int NB = NMAT + (GC ? 1 : 0);        // loads per step: the weights (and the codes)
   __shared__ DcSmem sm;
   extern __shared__ __align__(16) int8_t lds[];
   int8_t* act = lds;                                               // [M][act_ld] codes
@@ -671,11 +677,11 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   uint32_t epoch = 0;
   // Given codes (rows quantized by an earlier kernel): copied as they are, with the row
   // scales; no prologue arithmetic.
-  const bool codes_in = p.prologue == PRO_CODES;
+  const bool codes_in = GC || p.prologue == PRO_CODES;   // (GC: always given codes)
   float sa_row = 0.0f;
   if (wave < kDcCtl) {
     if (codes_in) {
-      stage_codes(p, act);
+      if constexpr (!GC) stage_codes(p, act, dg.act_ld);
       if (tid < p.M) sa_row = p.sa[tid];
     } else {
       if constexpr (kReq) {
@@ -726,13 +732,22 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     const int32_t tl = f / St;
     return (int64_t(tb0) + tl) * 16 * p.K + int64_t(f - tl * St) * 64;
   };
-  auto load_batch = [&](i32x4 (&wv)[U][NMAT], int32_t i) {
+  // GC: the codes of each step from global memory (tiled: 1 KB per K step, 16 bytes per
+  // lane), K step from a load cursor (batches are requested in order); cached loads,
+  // since every workgroup reads the same codes.
+  const int8_t* cal = p.a + lane * 16;
+  int32_t lk = r0 % St;
+  auto load_batch = [&](i32x4 (&wv)[U][NB], int32_t i) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int32_t f = r0 + i * U + u;
       const int64_t o = wofs(f < rlast ? f : rlast);
       wv[u][0] = ld16_stream(w0l + o);
       if constexpr (NMAT == 2) wv[u][1] = ld16_stream(w1l + o);
+      if constexpr (GC) {
+        wv[u][NMAT] = *reinterpret_cast<const i32x4*>(cal + int64_t(lk) * 1024);
+        if (++lk == St) lk = 0;
+      }
     }
   };
   // Step cursor (wave-uniform): next step, its segment, the segment's end, its K step.
@@ -752,14 +767,16 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
 #pragma unroll
     for (int i = 0; i < NMAT; ++i) acc[i] = i32x4{0, 0, 0, 0};
   };
-  auto step = [&](const i32x4 (&wu)[NMAT]) {
+  auto step = [&](const i32x4 (&wu)[NB]) {
     if (cf == cend) {
       flush();
       ++csg;
       cend += Ss;
     }
     if (ck == St) ck = 0;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ck) * 64);
+    i32x4 v;
+    if constexpr (GC) v = wu[NB - 1];
+    else v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ck) * 64);
     const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NMAT; ++i) acc[i] = mfma_i8(wu[i], bv, acc[i]);
@@ -767,18 +784,18 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     ++ck;
   };
   // A batch that may run past the range's end (the last one).
-  auto compute = [&](const i32x4 (&wv)[U][NMAT]) {
+  auto compute = [&](const i32x4 (&wv)[U][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (cf < rend) step(wv[u]);
   };
   // A batch wholly inside the range (no range test).
-  auto compute_full = [&](const i32x4 (&wv)[U][NMAT]) {
+  auto compute_full = [&](const i32x4 (&wv)[U][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) step(wv[u]);
   };
   // Batches 0 and 1 are requested by the caller; this streams the rest and flushes.
-  auto stream_rest = [&](i32x4 (&wA)[U][NMAT], i32x4 (&wB)[U][NMAT]) {
+  auto stream_rest = [&](i32x4 (&wA)[U][NB], i32x4 (&wB)[U][NB]) {
     int32_t i = 0;
     for (; i + 3 < nb; i += 2) {   // batches i and i + 1 are whole
       compute_full(wA);
@@ -821,14 +838,14 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     // emits waits for all loads, and the two batches no longer overlap.
     auto after_first_batch = [&]() {
       __asm__ __volatile__("" ::: "memory");
-      constexpr int kB = U * NMAT;   // vmcnt(kB); expcnt and lgkmcnt unconstrained
+      constexpr int kB = U * NB;   // vmcnt(kB); expcnt and lgkmcnt unconstrained
       __builtin_amdgcn_s_waitcnt((kB & 0xF) | 0x0F70 | ((kB >> 4) << 14));
       __asm__ __volatile__("" ::: "memory");
     };
     if (nb <= 1) {
       // A range of one batch (O and single-tile QKV workgroups at Qwen3-14B shapes):
       // no second batch, whose loads would only re-read the last step.
-      i32x4 wA[U][NMAT];
+      i32x4 wA[U][NB];
       load_batch(wA, 0);
       __builtin_amdgcn_sched_barrier(0);
       after_first_batch();
@@ -838,7 +855,7 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
       compute(wA);
       if (rn > 0) flush();
     } else {
-      i32x4 wA[U][NMAT], wB[U][NMAT];
+      i32x4 wA[U][NB], wB[U][NB];
       load_batch(wA, 0);
       __builtin_amdgcn_sched_barrier(0);
       after_first_batch();
@@ -864,8 +881,15 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     i32x4 lw[V][NMAT];
     // Down's share is longer than its register budget: the next VL steps go straight into
     // an LDS array of their own, requested with the rest.
+    // With codes in global memory (GC) the codes of all V + VL steps are copied into LDS
+    // too, behind the weights' copies.
     constexpr int VL = lo_lds_steps(EPI);
-    __shared__ __align__(16) int8_t lo_lds[VL > 0 ? kDcCtl * VL * 1024 : 16];
+    constexpr int VC = GC ? V + VL : 0;
+    constexpr int kLoLds = kDcCtl * VL * 1024;
+    __shared__ __align__(16) int8_t lo_lds[VL + VC > 0 ? kLoLds + kDcCtl * VC * 1024 : 16];
+    auto lo_code_lds = [&](int u) -> i32x4 {   // GC: codes of step ls0 + u
+      return *reinterpret_cast<const i32x4*>(lo_lds + kLoLds + (wave * VC + u) * 1024 + lane * 16);
+    };
     auto load_lo_lds = [&]() {
 #pragma unroll
       for (int u = 0; u < VL; ++u) {
@@ -879,6 +903,14 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
                                              lo_lds + (wave * VL + u) * 1024),
                                          16, 0, 0);
       }
+#pragma unroll
+      for (int u = 0; u < VC; ++u) {
+        const int32_t sq = ls0 + u < ls1 ? ls0 + u : ls1 - 1;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(cal + int64_t(sq) * 1024),
+                                         reinterpret_cast<__shared__ uint32_t*>(
+                                             lo_lds + kLoLds + (wave * VC + u) * 1024),
+                                         16, 0, 0);
+      }
     };
     auto load_lo = [&](int32_t s0) {
 #pragma unroll
@@ -890,12 +922,13 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
         if constexpr (NMAT == 2) lw[u][1] = ld16_stream(w1l + o);
       }
     };
+
     if (dg.leftover) {
       // The LDS-bound steps first: this wave's last copy into LDS is then older than its
       // register loads, and the wait below covers it.  (While the compiler counts a copy
       // into LDS as possibly in flight, every wait it emits is for all loads: the row scales
       // would wait for the leftover's weights.)
-      if constexpr (VL > 0) load_lo_lds();
+      if constexpr (VL + VC > 0) load_lo_lds();
       load_lo(ls0);
       __builtin_amdgcn_sched_barrier(0);
       // The row, the partial maxima and the LDS-bound steps, requested before these V * NMAT
@@ -955,13 +988,21 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     // The leftover quarter's matrix work (its first V steps have landed by now).
     int prev = -1;
     if (dg.leftover) {
+      // Codes of leftover step st past the early ones (clamped into the share).
+      auto lo_code = [&](int32_t st) -> i32x4 {
+        const int32_t sc = st < ls1 ? st : ls1 - 1;
+        if constexpr (GC) return *reinterpret_cast<const i32x4*>(cal + int64_t(sc) * 1024);
+        else return *reinterpret_cast<const i32x4*>(act + aoff + int64_t(sc) * 64);
+      };
       i32x4 lacc[NMAT];
 #pragma unroll
       for (int i = 0; i < NMAT; ++i) lacc[i] = i32x4{0, 0, 0, 0};
 #pragma unroll
       for (int u = 0; u < V; ++u) {
         if (ls0 + u < ls1) {
-          const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ls0 + u) * 64);
+          i32x4 v;
+          if constexpr (GC) v = lo_code_lds(u);
+          else v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ls0 + u) * 64);
           const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
 #pragma unroll
           for (int i = 0; i < NMAT; ++i) lacc[i] = mfma_i8(lw[u][i], bv, lacc[i]);
@@ -972,7 +1013,9 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
         for (int u = 0; u < VL; ++u) {
           if (ls0 + V + u < ls1) {
             const i32x4 wv = *reinterpret_cast<const i32x4*>(lo_lds + (wave * VL + u) * 1024 + lane * 16);
-            const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ls0 + V + u) * 64);
+            i32x4 v;
+            if constexpr (GC) v = lo_code_lds(V + u);
+            else v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(ls0 + V + u) * 64);
             const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
             lacc[0] = mfma_i8(wv, bv, lacc[0]);
           }
@@ -983,8 +1026,8 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
         load_lo(s0);
 #pragma unroll
         for (int u = 0; u < V; ++u) {
+          const i32x4 v = lo_code(s0 + u);
           if (s0 + u < ls1) {
-            const i32x4 v = *reinterpret_cast<const i32x4*>(act + aoff + int64_t(s0 + u) * 64);
             const i32x4 bv = aval ? v : i32x4{0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < NMAT; ++i) lacc[i] = mfma_i8(lw[u][i], bv, lacc[i]);
@@ -1144,9 +1187,9 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   if (b == 0 && tid == 0) *p.epoch_out = epoch + 1;
 }
 
-template <int EPI, int NMAT, int LAYOUT>
+template <int EPI, int NMAT, int LAYOUT, bool GC = false>
 hipError_t launch_t(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
-  const auto kern = decode_kernel<EPI, NMAT, LAYOUT>;
+  const auto kern = decode_kernel<EPI, NMAT, LAYOUT, GC>;
   if (g.lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, g.lds);
@@ -1179,6 +1222,15 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, bool codes
   // Prologue registers: the control waves hold a whole input row.
   if (!codes_in && (epi == EPI_DOWN ? K > kF32MaxK : K > kBfMaxK)) return false;
   if (T >= (int64_t(1) << 24) || St >= (int64_t(1) << 20)) return false;
+  // Static LDS of the kernel beside the dynamic part.
+  const size_t stat = sizeof(DcSmem) +
+                      (epi == EPI_DOWN ? kPmWords * 4 + size_t(kDcCtl) * lo_lds_steps(EPI_DOWN) * 1024 : 32);
+  // Down with given codes that do not fit LDS (Qwen3-14B at 16 rows: 278 KB of codes): the
+  // waves read the codes from global memory beside the weights, in the tiled order (every
+  // workgroup reads the same codes, which stay in L2).
+  const size_t part = size_t(nmat) * 4 * kWave * 4;   // bytes of one segment's sums
+  const bool gc = codes_in && epi == EPI_DOWN &&
+                  size_t(M) * size_t(K + 16) + size_t(kDcCtl + 1) * P * part + stat > kDcLdsPerCu;
   int64_t G = T < kDcMaxGrid ? T : kDcMaxGrid;
   // QKV and O: equal whole tiles for every workgroup when a grid of at least 5/8 of the
   // largest one divides the tiles (Qwen3-14B: QKV 448 = 224 x 2, O 320 = 160 x 2).  Measured
@@ -1205,9 +1257,13 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, bool codes
   g.whole_q = static_cast<int32_t>(q);
   g.whole_r = static_cast<int32_t>(left ? 0 : r);
   g.leftover = left ? 1 : 0;
-  g.act_ld = static_cast<int32_t>(K);
-  const size_t codes = (size_t(M) * size_t(K) + 255) / 256 * 256;
-  const size_t part = size_t(nmat) * 4 * kWave * 4;   // bytes of one segment's sums
+  g.gcodes = gc ? 1 : 0;
+  // Rows of codes 16 bytes apart in LDS banks: the 16 rows a step reads (one per lane
+  // group) then fall in different banks.  (With K a multiple of 256 bytes and no padding
+  // they all fall in the same four.)
+  const bool pad = M > 1 && (K / 16) % kWave == 0;
+  g.act_ld = static_cast<int32_t>(pad ? K + 16 : K);
+  const size_t codes = gc ? 0 : (size_t(M) * size_t(g.act_ld) + 255) / 256 * 256;
   g.acc_off = static_cast<int32_t>(codes);
   g.lred_off = static_cast<int32_t>(codes + size_t(ntmax) * P * part);
   // Staging of the input row at acc_off: FP32 h (Down) or BF16 x followed by the gain.
@@ -1217,9 +1273,10 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, bool codes
   size_t lds = size_t(g.lred_off) + size_t(kDcCtl) * part;
   if (codes + stage > lds) lds = codes + stage;
   // Dynamic LDS plus the kernel's static LDS within the CU's 160 KB.
-  const size_t stat = sizeof(DcSmem) +
-                      (epi == EPI_DOWN ? kPmWords * 4 + size_t(kDcCtl) * lo_lds_steps(EPI_DOWN) * 1024 : 32);
-  if (lds > kDcMaxLds || lds + stat > kDcLdsPerCu) return false;
+  // (GC: the kernel's leftover array also holds the codes of the leftover's early steps.)
+  const size_t stat_k =
+      stat + (gc ? size_t(kDcCtl) * (lo_steps(EPI_DOWN) + lo_lds_steps(EPI_DOWN)) * 1024 : 0);
+  if (lds > kDcMaxLds || lds + stat_k > kDcLdsPerCu) return false;
   g.lds = static_cast<int32_t>(lds);
   return true;
 }
@@ -1235,7 +1292,12 @@ hipError_t launch_decode(const StreamKArgs& a, const DecodeGeom& g, hipStream_t 
     case EPI_BF16: return launch_l<EPI_BF16, 1>(a, g, s);
     case EPI_BF16_RES: return launch_l<EPI_BF16_RES, 1>(a, g, s);
     case EPI_SILU: return launch_l<EPI_SILU, 2>(a, g, s);
-    case EPI_DOWN: return launch_l<EPI_DOWN, 1>(a, g, s);
+    case EPI_DOWN:
+      if (g.gcodes) {
+        if (a.layout == LAYOUT_TILED) return launch_t<EPI_DOWN, 1, LAYOUT_TILED, true>(a, g, s);
+        return launch_t<EPI_DOWN, 1, LAYOUT_ROWMAJOR, true>(a, g, s);
+      }
+      return launch_l<EPI_DOWN, 1>(a, g, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -16,7 +16,8 @@ struct QuantRowsArgs {
   const uint16_t* gamma;    // [K] BF16 RMSNorm gain or nullptr (no norm)
   float eps;
   int64_t M, K;
-  int8_t* q;                // [M, K] codes (row stride K)
+  int8_t* q;                // [M, K] codes (row stride K), or tiled (q_tiled)
+  int q_tiled;              // 1: q in the 16-row tiled operand order (M <= 16, 16 * K bytes)
   float* s;                 // [M] row scales
   float* xn_tap;            // [M, K] FP32 or nullptr
   int8_t* q_tap;            // [M, K] or nullptr (copy of q)
@@ -128,7 +129,7 @@ struct StreamKArgs {
   StreamKGeom g2;
   int32_t wgs1, toff2;
   // PRO_CODES
-  const int8_t* a;          // [M, lda] INT8 codes
+  const int8_t* a;          // [M, lda] INT8 codes (DecodeGeom::gcodes: 16-row tiled, 16 * K bytes)
   int64_t lda;
   const float* sa;          // [M] activation row scales
   // PRO_QUANT_BF16
@@ -174,6 +175,8 @@ struct DecodeGeom {
   int32_t whole_q, whole_r;  // workgroup b: q (+1 if b < r) whole tiles from b*q + min(b, r)
   int32_t leftover;          // 1: tiles grid*q .. grid*q + grid/4 - 1 are cut in K quarters,
                              // quarter b % 4 of tile grid*q + b/4 computed by workgroup b
+  int32_t gcodes;            // 1: the given codes are read from global memory in the 16-row
+                             // tiled operand order (tiled_code_index), not staged in LDS
   int32_t act_ld;            // bytes of codes per row in LDS (= K)
   int32_t acc_off, lred_off; // LDS offsets of the segment accumulators and the control waves' partials
   int32_t stage_g;           // offset of the staged RMSNorm gain from acc_off (the staging area)

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_reg_kernel(QuantRows
       }
     }
     const u32x2 pk = {lo, hi};
-    *reinterpret_cast<u32x2*>(p.q + row * K + k) = pk;
+    *reinterpret_cast<u32x2*>(p.q + (p.q_tiled ? tiled_code_index(row, k) : row * K + k)) = pk;
     if (p.q_tap) *reinterpret_cast<u32x2*>(p.q_tap + row * K + k) = pk;
   }
 }
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(QuantRowsArgs
       }
     }
     const u32x2 pk = {lo, hi};
-    *reinterpret_cast<u32x2*>(p.q + row * K + k) = pk;
+    *reinterpret_cast<u32x2*>(p.q + (p.q_tiled ? tiled_code_index(row, k) : row * K + k)) = pk;
     if (p.q_tap) *reinterpret_cast<u32x2*>(p.q_tap + row * K + k) = pk;
   }
 }
