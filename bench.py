@@ -943,14 +943,14 @@ def main():
     traffic = measured_traffic(cfg)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_kernel<EPI_SILU> (Gate/Up)" if M <= 4 else
+            "kernel": "decode_kernel<EPI_SILU> (Gate/Up)" if M <= 16 else
                       "streamk_kernel<EPI_SILU> (Gate/Up)", "kernel_us": round(k_ms * 1e3, 2),
             "kernel_us_stats": pct_stats(k_all * 1e3),
             "algorithmic_bytes_per_launch": gu_bytes}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(synth.CONFIGS[2], args.cpu_seconds)
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,

@@ -404,9 +404,23 @@ a8w8_status run_mlp_decode(const uint16_t* x, const uint16_t* gamma, float eps,
     d.tap_q = t ? t->q_h : nullptr;
     d.tap_s = t ? t->s_h : nullptr;
   } else {
+    // The row scales come from the Gate/Up epilogue's partial maxima of h.
     A8W8_HIP(tm.before(A8W8_KERNEL_REQUANT));
-    A8W8_HIP(quant_kernel(b.h, I, 1, nullptr, 0.0f, M, I, b.q_h, b.s_h, nullptr,
-                          t ? t->q_h : nullptr, t ? t->s_h : nullptr, st, codes_tiled(pl.dn)));
+    QuantRowsArgs rq{};
+    rq.x = b.h;
+    rq.ldx = I;
+    rq.x_is_f32 = 1;
+    rq.M = M;
+    rq.K = I;
+    rq.q = b.q_h;
+    rq.q_tiled = codes_tiled(pl.dn) ? 1 : 0;
+    rq.s = b.s_h;
+    rq.q_tap = t ? t->q_h : nullptr;
+    rq.s_tap = t ? t->s_h : nullptr;
+    rq.write_codes = 1;
+    rq.pmax = b.pmax;
+    rq.npmax = I / 16;
+    A8W8_HIP(M <= 65535 ? launch_requant_pmax(rq, st) : launch_quant_rows(rq, st));
     A8W8_HIP(tm.after(A8W8_KERNEL_REQUANT));
     d.prologue = PRO_CODES;
     d.a = b.q_h;

@@ -1200,10 +1200,10 @@ hipError_t launch_t(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, int NMAT>
+template <int EPI, int NMAT, bool GC = false>
 hipError_t launch_l(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
-  if (a.layout == LAYOUT_TILED) return launch_t<EPI, NMAT, LAYOUT_TILED>(a, g, s);
-  return launch_t<EPI, NMAT, LAYOUT_ROWMAJOR>(a, g, s);
+  if (a.layout == LAYOUT_TILED) return launch_t<EPI, NMAT, LAYOUT_TILED, GC>(a, g, s);
+  return launch_t<EPI, NMAT, LAYOUT_ROWMAJOR, GC>(a, g, s);
 }
 
 }  // namespace
@@ -1225,12 +1225,17 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, bool codes
   // Static LDS of the kernel beside the dynamic part.
   const size_t stat = sizeof(DcSmem) +
                       (epi == EPI_DOWN ? kPmWords * 4 + size_t(kDcCtl) * lo_lds_steps(EPI_DOWN) * 1024 : 32);
-  // Down with given codes that do not fit LDS (Qwen3-14B at 16 rows: 278 KB of codes): the
-  // waves read the codes from global memory beside the weights, in the tiled order (every
-  // workgroup reads the same codes, which stay in L2).
+  // Given codes read from global memory beside the weights, in the tiled order (every
+  // workgroup reads the same codes, which stay in L2), instead of copied into LDS first:
+  // Down when the codes do not fit LDS (Qwen3-14B at 16 rows: 278 KB), and QKV and O at
+  // more than 4 rows, whose copy of the codes (80 KB at 16 rows) holds back the stream
+  // by about 3 us (measured on MI355X at 16 rows: QKV 12.0 -> 11.3 us, O 11.0 -> 10.8 us).
+  // Gate/Up keeps the copy: three loads per step instead of two cost it 6 us.
   const size_t part = size_t(nmat) * 4 * kWave * 4;   // bytes of one segment's sums
-  const bool gc = codes_in && epi == EPI_DOWN &&
-                  size_t(M) * size_t(K + 16) + size_t(kDcCtl + 1) * P * part + stat > kDcLdsPerCu;
+  const bool gc =
+      codes_in && ((M > 4 && (epi == EPI_BF16 || epi == EPI_BF16_RES)) ||
+                   (epi == EPI_DOWN &&
+                    size_t(M) * size_t(K + 16) + size_t(kDcCtl + 1) * P * part + stat > kDcLdsPerCu));
   int64_t G = T < kDcMaxGrid ? T : kDcMaxGrid;
   // QKV and O: equal whole tiles for every workgroup when a grid of at least 5/8 of the
   // largest one divides the tiles (Qwen3-14B: QKV 448 = 224 x 2, O 320 = 160 x 2).  Measured
@@ -1274,8 +1279,7 @@ bool plan_decode(int epi, int64_t M, int64_t N, int64_t K, int parts, bool codes
   if (codes + stage > lds) lds = codes + stage;
   // Dynamic LDS plus the kernel's static LDS within the CU's 160 KB.
   // (GC: the kernel's leftover array also holds the codes of the leftover's early steps.)
-  const size_t stat_k =
-      stat + (gc ? size_t(kDcCtl) * (lo_steps(EPI_DOWN) + lo_lds_steps(EPI_DOWN)) * 1024 : 0);
+  const size_t stat_k = stat + (gc ? size_t(kDcCtl) * (lo_steps(epi) + lo_lds_steps(epi)) * 1024 : 0);
   if (lds > kDcMaxLds || lds + stat_k > kDcLdsPerCu) return false;
   g.lds = static_cast<int32_t>(lds);
   return true;
@@ -1289,14 +1293,15 @@ size_t decode_slot_elems(const DecodeGeom& g, int nmat) {
 hipError_t launch_decode(const StreamKArgs& a, const DecodeGeom& g, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   switch (a.epi) {
-    case EPI_BF16: return launch_l<EPI_BF16, 1>(a, g, s);
-    case EPI_BF16_RES: return launch_l<EPI_BF16_RES, 1>(a, g, s);
+    case EPI_BF16:
+      if (g.gcodes) return launch_l<EPI_BF16, 1, true>(a, g, s);
+      return launch_l<EPI_BF16, 1>(a, g, s);
+    case EPI_BF16_RES:
+      if (g.gcodes) return launch_l<EPI_BF16_RES, 1, true>(a, g, s);
+      return launch_l<EPI_BF16_RES, 1>(a, g, s);
     case EPI_SILU: return launch_l<EPI_SILU, 2>(a, g, s);
     case EPI_DOWN:
-      if (g.gcodes) {
-        if (a.layout == LAYOUT_TILED) return launch_t<EPI_DOWN, 1, LAYOUT_TILED, true>(a, g, s);
-        return launch_t<EPI_DOWN, 1, LAYOUT_ROWMAJOR, true>(a, g, s);
-      }
+      if (g.gcodes) return launch_l<EPI_DOWN, 1, true>(a, g, s);
       return launch_l<EPI_DOWN, 1>(a, g, s);
     default: return hipErrorInvalidValue;
   }

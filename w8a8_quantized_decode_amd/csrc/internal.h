@@ -26,8 +26,12 @@ struct QuantRowsArgs {
   int a_bf16_tiled;         // a_bf16 layout: 0 row-major [M, K]; 1 prefill operand layout
   uint16_t* a_bf16_tap;     // [M, K] or nullptr
   int write_codes;          // 0: skip the INT8 codes (prefill only needs a_bf16)
+  const float* pmax;        // launch_requant_pmax: [npmax, M] absolute maxima of x's rows per tile
+  int64_t npmax;
 };
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t stream);
+// FP32 rows (x_is_f32, no gain) with their absolute maxima given as pmax: M <= 65535.
+hipError_t launch_requant_pmax(const QuantRowsArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- weight layouts
 // LAYOUT_ROWMAJOR: w[n * K + k].

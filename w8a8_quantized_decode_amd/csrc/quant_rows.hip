@@ -84,11 +84,16 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_reg_kernel(QuantRows
                      row * p.ldx * (kF32In ? sizeof(float) : sizeof(uint16_t));
   // Chunk c of this thread starts at k = (c * kQuantThreads + tid) * V, the order the
   // looping kernel visits them in.
+  // The gain is requested with the row: its loads then overlap the row's.
   float v[kRegChunks][V];
+  float gm[kRms ? kRegChunks : 1][V];
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c) {
     const int64_t k = (int64_t(c) * kQuantThreads + tid) * V;
-    if (k < K) L::load(xrow, k, v[c]);
+    if (k < K) {
+      L::load(xrow, k, v[c]);
+      if constexpr (kRms) load_gamma(p.gamma, k, gm[c]);
+    }
   }
 
   if (kRms) {
@@ -113,10 +118,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_reg_kernel(QuantRows
     for (int c = 0; c < kRegChunks; ++c) {
       const int64_t k = (int64_t(c) * kQuantThreads + tid) * V;
       if (k >= K) break;
-      float g[V];
-      load_gamma(p.gamma, k, g);
 #pragma unroll
-      for (int i = 0; i < V; ++i) v[c][i] = (v[c][i] * r) * g[i];
+      for (int i = 0; i < V; ++i) v[c][i] = (v[c][i] * r) * gm[c][i];
     }
   }
 
@@ -280,7 +283,61 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(QuantRowsArgs
   }
 }
 
+// Requantization of FP32 rows whose absolute maxima are given per 16-column tile (the
+// partial maxima written by the Gate/Up epilogue): the scale needs no pass over the row
+// (the maximum of the partial maxima is the row's absolute maximum), so each row is cut
+// into chunks of kRqChunk values, one workgroup each, and every workgroup derives the
+// scale itself.  Codes as in the kernels above.
+constexpr int kRqThreads = 256;
+constexpr int kRqChunk = kRqThreads * 8;
+
+__global__ __launch_bounds__(kRqThreads) void requant_pmax_kernel(QuantRowsArgs p) {
+  __shared__ float s_max[kRqThreads / kWave];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int64_t row = blockIdx.y;
+  const int64_t K = p.K;
+  const int64_t k = int64_t(blockIdx.x) * kRqChunk + int64_t(tid) * 8;
+  float v[8];
+  if (k < K) RowLoader<true>::load(static_cast<const float*>(p.x) + row * p.ldx, k, v);
+  float a = 0.0f;
+  for (int64_t t = tid; t < p.npmax; t += kRqThreads) a = fmaxf(a, p.pmax[t * p.M + row]);
+  a = wave_max_f32(a);
+  if (lane == 0) s_max[wave] = a;
+  __syncthreads();
+  a = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kRqThreads / kWave; ++w) a = fmaxf(a, s_max[w]);
+  const float s = a / 127.0f;
+  if (blockIdx.x == 0 && tid == 0) {
+    p.s[row] = s;
+    if (p.s_tap) p.s_tap[row] = s;
+  }
+  if (k >= K) return;
+  uint32_t lo = 0, hi = 0;
+  if (s != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= (uint32_t(quant_code(v[i], s)) & 0xFFu) << (8 * i);
+      hi |= (uint32_t(quant_code(v[4 + i], s)) & 0xFFu) << (8 * i);
+    }
+  }
+  const u32x2 pk = {lo, hi};
+  *reinterpret_cast<u32x2*>(p.q + (p.q_tiled ? tiled_code_index(row, k) : row * K + k)) = pk;
+  if (p.q_tap) *reinterpret_cast<u32x2*>(p.q_tap + row * K + k) = pk;
+}
+
 }  // namespace
+
+hipError_t launch_requant_pmax(const QuantRowsArgs& a, hipStream_t stream) {
+  if (a.M == 0) return hipSuccess;
+  if (a.M > 65535 || !a.x_is_f32 || a.gamma || !a.pmax || a.K % 8) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((a.K + kRqChunk - 1) / kRqChunk),
+                  static_cast<unsigned>(a.M)),
+      block(kRqThreads);
+  hipLaunchKernelGGL(requant_pmax_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows(const QuantRowsArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
