@@ -31,8 +31,8 @@ METRIC = "µs/layer and INT8-weight HBM GB/s (% of peak), A8W8 decode linears at
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 GATEUP_KERNEL = 5     # kernel number of the Gate/Up GEMM inside a8w8_layer_linears
-GATEUP_NAME = "decode_kernel<2, 2,"        # its symbol in rocprofv3 counter tables (M <= 4)
-GATEUP_NAME_SK = "streamk_kernel<2, 2,"    # ... with more rows (M = 16: the stream-K kernel)
+GATEUP_NAME = "decode_kernel<2, 2,"        # its symbol in rocprofv3 counter tables (M <= 16)
+GATEUP_NAME_SK = "streamk_kernel<2, 2,"    # ... with more rows (the stream-K kernel)
 PACK_NAME = "pack_tiled_kernel"            # plain permuting copy: the counter calibration
 PMC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_pmc.json")
 PMC_MD = os.path.join(ROOT, "profiles", "layer_linears_m1_pmc.md")
@@ -43,7 +43,7 @@ PMC_MD_M16 = os.path.join(ROOT, "profiles", "stack40_m16_pmc.md")
 def pmc_target(cfg):
     """(summary json, summary markdown, Gate/Up kernel symbol) of a config's counters."""
     if cfg.M > 4:
-        return PMC_FILE_M16, PMC_MD_M16, GATEUP_NAME_SK
+        return PMC_FILE_M16, PMC_MD_M16, GATEUP_NAME if cfg.M <= 16 else GATEUP_NAME_SK
     return PMC_FILE, PMC_MD, GATEUP_NAME
 
 
