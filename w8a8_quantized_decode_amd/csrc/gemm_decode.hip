@@ -3,8 +3,10 @@
 // requantization of h for Down) and the fused dequant / SiLU / residual / split-K
 // epilogues.  It serves the layer chain and the MLP block at decode batch sizes
 // (M <= kFuseMaxRows) for the shapes it covers (plan_decode), and, with the input codes
-// given (row-quantization kernels before it), up to kDcMaxRows rows when the codes fit
-// in LDS; the stream-K kernel in gemm_streamk.hip serves the others.
+// given (row-quantization kernels before it), up to kDcMaxRows rows: the codes are
+// copied into LDS at the start, or (QKV and O above 4 rows, Down when they do not fit)
+// read from global memory beside the weights in the tiled order (template argument GC).
+// The stream-K kernel in gemm_streamk.hip serves the other shapes.
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
 // paths", What changed > Gate/Up INT8 path (INT8 x INT8 -> INT32 Gate/Up matmuls with
@@ -1049,7 +1051,7 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     const int ct = tid;
     constexpr int kSwN = (kDcMaxTiles + 1) * 16 * NMAT;                  // <= 192
     constexpr int kResN = (kDcMaxTiles + 1) * kDcMaxRows * 16;           // 1536
-    constexpr int kResIt = (kResN + kDcCtlThreads - 1) / kDcCtlThreads;  // 2
+    constexpr int kResIt = (kResN + kDcCtlThreads - 1) / kDcCtlThreads;  // 6
     float swv = 0.0f;
     int32_t sw_t = -1;
     int sw_slot = 0, sw_mat = 0, sw_c = 0;
