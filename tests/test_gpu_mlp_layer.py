@@ -269,7 +269,7 @@ TOY_LAYER = synth.Config(0, "toy layer", 1, 256, 768, "layer", n_q_heads=2, n_kv
                          head_dim=128)
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 5, 16])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 11, 16])
 @pytest.mark.parametrize("layout", [B.LAYOUT_ROWMAJOR, B.LAYOUT_TILED])
 def test_layer_toy(M, layout):
     announce(f"layer toy M={M} layout={layout}")
@@ -288,7 +288,7 @@ def test_layer_fused_edge_rows(cfg):
     assert q[1, :10].tolist() == TIE_CODES and host(t["s_in"])[1] == 1.0
 
 
-@pytest.mark.parametrize("M,layout", [(1, 1), (1, 0), (16, 1)])
+@pytest.mark.parametrize("M,layout", [(1, 1), (1, 0), (16, 1), (16, 0), (7, 1)])
 def test_layer_qwen3_14b(M, layout):
     announce(f"layer qwen3-14b M={M} layout={layout}")
     got, qkv, want, t, st = run_layer(C2, M, layout=layout)
