@@ -32,7 +32,8 @@ def _layer_want(cfg, d):
     return want
 
 
-@pytest.mark.parametrize("cfg,M", [(TOY_LAYER, 2), (C2, 1)], ids=["toy-M2", "qwen3-14b-M1"])
+@pytest.mark.parametrize("cfg,M", [(TOY_LAYER, 2), (TOY_LAYER, 9), (C2, 1), (C2, 16)],
+                         ids=["toy-M2", "toy-M9", "qwen3-14b-M1", "qwen3-14b-M16"])
 def test_layer_graph_replay(cfg, M):
     announce(f"layer graph replay {cfg.name} M={M}")
     t = torch()
