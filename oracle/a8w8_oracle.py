@@ -29,12 +29,13 @@ round to nearest-even); ``fl32(.)`` is one FP32 operation.
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against brute force,
 closed forms, invariants or error bounds.  The end-to-end compositions
 (``mlp_block_decode``, ``layer_linears_decode``, ``prefill_mlp``,
-``layer_linears_prefill``) are pinned only
-through their stage pins plus an error bound against exact (unquantized) FP64 math:
-the pages print no worked example of a whole block, so as compositions they are
-"parity unpinned" beyond those stage pins.  ``decode_layer`` (the layer with real
-attention) is pinned beyond its stages by the one-position context, the
-identity-attention layer's QKV and h1, and the cache slot it writes.
+``layer_linears_prefill``) are pinned beyond their stage pins by an element-by-element
+scalar brute force on tiny shapes (``tests/test_oracle_composed.py``), written from the
+same readings without calling this module and compared bit for bit, intermediates
+included, and by an error bound against exact (unquantized) FP64 math; the pages print
+no worked example of a whole block.  ``decode_layer`` (the layer with real attention)
+is pinned beyond its stages by the one-position context, the identity-attention
+layer's QKV and h1, and the cache slot it writes.
 """
 
 from __future__ import annotations
