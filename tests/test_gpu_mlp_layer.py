@@ -118,7 +118,8 @@ def test_mlp_toy(M, split_k, layout):
 
 
 @pytest.mark.parametrize("M,split_k,layout", [(1, 2, 1), (1, 2, 0), (16, 2, 1), (16, 4, 0),
-                                               (9, 1, 1), (1, 8, 1), (4, 1, 1), (5, 4, 0)])
+                                               (16, 8, 1), (9, 1, 1), (12, 1, 0), (1, 8, 1),
+                                               (4, 1, 1), (5, 4, 0)])
 def test_mlp_qwen3_14b(M, split_k, layout):
     announce(f"mlp qwen3-14b M={M} split_k={split_k} layout={layout}")
     got, want, t, st = run_mlp(C1, M, split_k, layout=layout)
