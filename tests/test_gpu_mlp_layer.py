@@ -126,6 +126,20 @@ def test_mlp_qwen3_14b(M, split_k, layout):
     _check_out(got, want, _check_mlp_taps(t, st, split_k))
 
 
+# A mid-size block: Down's codes at 14-16 rows (K = 9216) pass the LDS budget, so Down reads
+# them from global memory on a 32-tile grid without leftover quarters; 9216 / 16 chunks
+# per row is a multiple of 64, so rows of codes in LDS are padded.
+MID = synth.Config(5, "mid-size A8W8 MLP block", 1, 512, 9216, "mlp")
+
+
+@pytest.mark.parametrize("M,split_k", [(6, 2), (14, 1), (14, 2), (16, 4)])
+@pytest.mark.parametrize("layout", [B.LAYOUT_ROWMAJOR, B.LAYOUT_TILED])
+def test_mlp_mid_size(M, split_k, layout):
+    announce(f"mlp mid-size M={M} split_k={split_k} layout={layout}")
+    got, want, t, st = run_mlp(MID, M, split_k, layout=layout)
+    _check_out(got, want, _check_mlp_taps(t, st, split_k))
+
+
 TIE_GAIN = [127.0, 2.5, -3.5, 0.5, -0.5, 1.5, 126.5, -127.0, 0.0, 3.25]
 TIE_CODES = [127, 2, -4, 0, 0, 2, 126, -127, 0, 3]
 
