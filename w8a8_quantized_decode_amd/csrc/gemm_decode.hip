@@ -680,11 +680,17 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
   // Given codes (rows quantized by an earlier kernel): copied as they are, with the row
   // scales; no prologue arithmetic.
   const bool codes_in = GC || p.prologue == PRO_CODES;   // (GC: always given codes)
-  float sa_row = 0.0f;
   if (wave < kDcCtl) {
     if (codes_in) {
       if constexpr (!GC) stage_codes(p, act, dg.act_ld);
-      if (tid < p.M) sa_row = p.sa[tid];
+      // The row scales go straight into LDS like the codes: copied through a register,
+      // their use would make the compiler wait for every load in flight, the leftover
+      // quarter's weights included (measured on MI355X at 16 rows: the codes were
+      // released 2 us after they had landed).
+      if (tid < p.M)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(p.sa + tid),
+                                         reinterpret_cast<__shared__ uint32_t*>(sm.row_scale),
+                                         4, 0, 0);
     } else {
       if constexpr (kReq) {
         stage_pmax(p, pm_lds);
@@ -945,7 +951,7 @@ __global__ __launch_bounds__(kDcThreads) void decode_kernel(StreamKArgs p, Decod
     int gen = 0;
     ctl_sync(sm, gen);    // ... and every control wave's
     if (codes_in) {
-      if (tid < p.M) sm.row_scale[tid] = sa_row;
+      // The row scales are in LDS already.
     } else if constexpr (kReq) {
       if (p.M == 1) {
         // One row: every wave takes code tasks (the stream waves once their first batch
