@@ -382,6 +382,9 @@ template <int EPI>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillGemmArgs p) {
   constexpr int kOut = (EPI == EPI_PF_SILU) ? kPfCb / 2 : kPfCb;
   constexpr int kItems = kPfWaves * kPfRb * kOut * 4 * kWave;  // per tile
+  // Split-tile pieces fetched together (at 16 the Gate/Up copy spilled to scratch, and
+  // after a spill-free rewrite it was still no faster than 8).
+  constexpr int kReduceBatch = 8;
   const Sched sc{p};
   const int32_t SQ = p.quads;
   const int32_t u = static_cast<int32_t>(blockIdx.y);
@@ -403,14 +406,27 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillGemmArgs p) 
     if (m >= p.M) continue;
     const int q0 = (rb * kPfCb + cb) * 4 + g;
     const int q1 = (rb * kPfCb + (cb + 2) % kPfCb) * 4 + g;  // the Up group (EPI_PF_SILU)
+    // The pieces are fetched kReduceBatch at a time, all loads of a batch in flight
+    // together (a piece past the last re-reads the last one and is not added), and
+    // added one by one in K order.
     f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
-    for (int32_t w = wa; w <= wb; ++w) {
-      const float* src = p.slots + (int64_t(sc.slot(w, t)) * kPfWaves + wave) * kPfSlotWave;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src + (q0 * kWave + lane) * 4);
-      x = (w == wa) ? a : x + a;
-      if constexpr (EPI == EPI_PF_SILU) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(src + (q1 * kWave + lane) * 4);
-        y = (w == wa) ? b : y + b;
+    for (int32_t w0 = wa; w0 <= wb; w0 += kReduceBatch) {
+      f32x4 pa[kReduceBatch], pb[kReduceBatch];
+#pragma unroll
+      for (int i = 0; i < kReduceBatch; ++i) {
+        const int32_t w = min(w0 + i, wb);
+        const float* src = p.slots + (int64_t(sc.slot(w, t)) * kPfWaves + wave) * kPfSlotWave;
+        pa[i] = *reinterpret_cast<const f32x4*>(src + (q0 * kWave + lane) * 4);
+        if constexpr (EPI == EPI_PF_SILU)
+          pb[i] = *reinterpret_cast<const f32x4*>(src + (q1 * kWave + lane) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < kReduceBatch; ++i) {
+        const int32_t w = w0 + i;
+        if (w <= wb) {
+          x = (w == wa) ? pa[i] : x + pa[i];
+          if constexpr (EPI == EPI_PF_SILU) y = (w == wa) ? pb[i] : y + pb[i];
+        }
       }
     }
     const int64_t n0 = int64_t(nt) * (kOut * 32) + cb * 32 + g * 8 + (lane >> 5) * 4;
