@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -112,11 +113,24 @@ def emit(line: dict) -> None:
         sys.exit(3)
 
 
-def kernel_source_hash() -> str:
+def code_text(src: str) -> str:
+    """Source text without comments and with whitespace runs collapsed: what the compiler
+    sees of it, so that a comment edit does not mark the counters stale."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the decode kernels' code (comments and layout excluded)."""
     h = hashlib.sha256()
     for f in ("gemm_decode.hip", "gemm_streamk.hip", "device_common.h", "internal.h"):
-        with open(os.path.join(ROOT, "w8a8_quantized_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(ROOT, "w8a8_quantized_decode_amd", "csrc", f)) as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -198,8 +198,8 @@ a8w8_status a8w8_quantize_rows(const uint16_t* x_bf16, int64_t ldx,
  * K % 64 == 0, 0 < K <= 131072 (INT32 accumulators cannot overflow), N % 16 == 0,
  * M <= 65535 * 64 (one grid row per 64 rows).  y may alias residual_bf16.  One kernel.
  * (pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data paths",
- * What changed > Gate/Up INT8 path: INT8 x INT8 -> INT32 with the activation-row and
- * weight-channel scales applied at dequantization; the decode layer's QKV and output
+ * What changed > Gate/Up INT8 path: INT8 x INT8 products summed in INT32, the sums turned
+ * into FP32 with the row scale and the channel scale; the decode layer's QKV and output
  * projections use the same arithmetic, What changed > Decode scheduling.)
  */
 a8w8_status a8w8_linear(const int8_t* q, const float* row_scale, a8w8_qweight W,
@@ -304,7 +304,7 @@ a8w8_status a8w8_layer_linears_static(const uint16_t* x_bf16, const uint16_t* ga
 
 /*
  * All linears of one prefill layer, W8A16 on the shared INT8 weights (pypto-lib PR #810,
- * What changed > Gate/Up INT8 path: prefill dequantizes each weight tile to BF16; the
+ * What changed > Gate/Up INT8 path: prefill turns each INT8 weight tile into BF16 values; the
  * layer composition is the decode layer's with that linear).  Same shapes as
  * a8w8_layer_linears; attention replaced by identity.
  * Steps: a = rne_bf16(RMSNorm(x, gamma_in)) -> qkv = rne_bf16(a W'_qkv^T) -> the Q slice

@@ -517,7 +517,7 @@ def decode_attention(q_bits, n_q_heads: int, n_kv_heads: int, head_dim: int, k_c
 
 def o_projection(attn_bits, x_bits, w_o, s_o) -> np.ndarray:
     """O on the attention output with the layer input as residual, as in
-    ``layer_linears_decode``: the attention rows are quantized once per row, multiplied
+    ``layer_linears_decode``: each attention row gets INT8 codes and one scale, is multiplied
     in INT32 and dequantized, and ``h1 = rne_bf16(fl32(y_o + f(x)))``."""
     q_a, s_a = quantize_rows(bf16_to_f32(np.asarray(attn_bits, dtype=np.uint16)))
     acc_o = int_gemm(q_a, w_o)

@@ -55,6 +55,19 @@ def test_pmc_summary_calibrates_on_the_pack_copy(tmp_path, monkeypatch):
     assert bench.measured_traffic(cfg) is None
 
 
+def test_kernel_hash_ignores_comments_but_not_code():
+    a = "int x = 1;  // the count\n/* a block\n comment */ x += 2;\n"
+    assert bench.code_text(a) == bench.code_text("int x = 1;\n\n    x += 2;")
+    assert bench.code_text(a) != bench.code_text("int x = 1; x += 3;")
+    files = {}
+    for f in ("gemm_decode.hip", "gemm_streamk.hip", "device_common.h", "internal.h"):
+        with open(os.path.join(bench.ROOT, "w8a8_quantized_decode_amd", "csrc", f)) as fh:
+            files[f] = fh.read()
+    h = bench.kernel_source_hash()
+    assert bench.kernel_source_hash(lambda f: files[f] + "\n// a new remark\n") == h
+    assert bench.kernel_source_hash(lambda f: files[f] + "\nint extra_symbol;\n") != h
+
+
 def test_pmc_summary_rejects_a_copy_of_unknown_size(tmp_path, monkeypatch):
     cfg = synth.CONFIGS[2]
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(PACK, 12345, 1.0), (GATEUP, 1, 1.0)])

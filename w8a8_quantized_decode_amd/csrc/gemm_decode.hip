@@ -9,9 +9,9 @@
 // The stream-K kernel in gemm_streamk.hip serves the other shapes.
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
-// paths", What changed > Gate/Up INT8 path (INT8 x INT8 -> INT32 Gate/Up matmuls with
-// the activation-row and weight-channel scales applied at dequantization, the
-// post-attention RMSNorm output quantized once per row) and > Decode scheduling (Down
+// paths", What changed > Gate/Up INT8 path (Gate/Up as INT8 x INT8 products summed in
+// INT32, the sums turned into FP32 with the row scale and the channel scale, the
+// normalized activations after attention given one INT8 scale per row) and > Decode scheduling (Down
 // split two ways along K into independent accumulators), with the CodeRabbit walkthrough
 // row "Split down projection accumulation" (FP32 partials summed, the residual added,
 // the sum narrowed with round-to-nearest-even).  QKV and O reuse the pattern.

@@ -2,8 +2,8 @@
 // gfx950 matrix cores, with the dequant (+ residual) -> RNE BF16 epilogue.
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
-// paths", What changed > Gate/Up INT8 path (INT8 x INT8 -> INT32 products with the
-// activation-row and weight-channel scales applied at dequantization).
+// paths", What changed > Gate/Up INT8 path (INT8 x INT8 products summed in INT32, the
+// sums turned into FP32 with the row scale and the channel scale).
 //
 // This entry point takes no workspace, so every 16-channel output tile is owned by one
 // workgroup: its waves split K, keep U steps of weight loads in flight (two register

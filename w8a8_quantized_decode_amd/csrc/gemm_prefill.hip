@@ -2,7 +2,7 @@
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
 // paths", What changed > Gate/Up INT8 path: prefill keeps the INT8 checkpoint weights
-// and dequantizes each weight tile to BF16 before the matrix multiply.  Every weight
+// and turns every INT8 weight tile into BF16 values ahead of the matrix-core product.  Every weight
 // element becomes W' = rne_bf16(fl32(w * s[n])), the activations are BF16, products
 // accumulate in FP32 (v_mfma_f32_32x32x16_bf16).
 //

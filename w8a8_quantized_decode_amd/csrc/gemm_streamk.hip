@@ -3,9 +3,9 @@
 // epilogues.  It serves the MLP block and the layer chain.
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
-// paths", What changed > Gate/Up INT8 path (INT8 x INT8 -> INT32 Gate/Up matmuls, the
-// activation-row and weight-channel scales applied at dequantization, the
-// post-attention RMSNorm output quantized once per row) and > Decode scheduling (Down
+// paths", What changed > Gate/Up INT8 path (Gate/Up as INT8 x INT8 products summed in
+// INT32, the sums turned into FP32 with the row scale and the channel scale, the
+// normalized activations after attention given one INT8 scale per row) and > Decode scheduling (Down
 // split two ways along K into independent accumulators), plus the CodeRabbit
 // walkthrough row "Split down projection accumulation" (FP32 partials summed and
 // narrowed together with the residual).  QKV and O reuse the same pattern.

@@ -2,8 +2,8 @@
 //
 // Method: pypto-lib PR #810 "perf(qwen3-a8w8): optimize decode scheduling and data
 // paths", What changed > Decode scheduling (one batched activation-quantization pass
-// over all decode rows) and > Gate/Up INT8 path (the post-attention RMSNorm output is
-// quantized once per row; the codes carry an FP32 row scale).
+// over all decode rows) and > Gate/Up INT8 path (each row of normalized activations after
+// attention gets its own INT8 codes and one FP32 scale).
 //
 // One workgroup per row.  A row of up to kRegChunks * 4096 values is read once into
 // registers (all its loads in flight together) and the three passes (sum of squares,
