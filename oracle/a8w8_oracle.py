@@ -368,8 +368,8 @@ def prefill_linear(a_bits, w, s, residual_bits=None):
 
     ``W' = dequant_weight_bf16(w, s)``; the dot products are accumulated in FP64 and
     rounded once to FP32, the residual (when given) is one FP32 add, and the result is
-    narrowed with RNE ([PR810] What changed > Gate/Up INT8 path: prefill keeps the shared
-    INT8 weights by dequantizing each tile to BF16; the Gemini review: narrowing with
+    narrowed with RNE ([PR810] What changed > Gate/Up INT8 path: prefill reads the INT8
+    weights that decode uses, turned into BF16 tile by tile; the Gemini review: narrowing with
     ``mode="rint"``).
     """
     y = _bf16_matmul_f64_to_f32(a_bits, dequant_weight_bf16(w, s))

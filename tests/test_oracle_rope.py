@@ -3,8 +3,8 @@
 RoPE is checked against independent statements of a rotation (complex multiplication in
 FP64), its invariants (angle 0 is the identity, rotations compose, the norm is kept, and
 the dot product of a rotated query and key depends only on the position difference),
-and the batched application is checked against the per-row one, since the pages record a
-non-equivalent batched Q RoPE path as the cause of a repeated-output bug.  The KV write
+and the batched application is checked against the per-row one, since the pages blame a
+bug that repeated output on a batched Q RoPE that did not match the per-row one.  The KV write
 is checked slot by slot against the block table, and everything else in the cache is
 left untouched.
 """
@@ -93,8 +93,9 @@ def test_qk_norm_rope_kv_slots_and_heads():
 
 def test_batched_q_rope_equals_per_row():
     """All rows' Q heads rotated in one batched call with each row's own angles equal the
-    per-row results; a batched call that takes the first row's angles for every row (the
-    kind of non-equivalent batched Q RoPE the pages report) does not."""
+    per-row results; a batched call that takes the first row's angles for every row (a
+    batched form that no longer matches the per-row one, the kind of fault the pages
+    report) does not."""
     qkv, qg, kg, c, s, pos, bt, kc, vc, nq, nkv, d = _case(M=4, nblocks=12)
     eps = 1e-6
     q, _, _ = qk_norm_rope_kv(qkv, nq, nkv, d, qg, kg, eps, c, s, pos, bt, kc, vc)
