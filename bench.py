@@ -806,8 +806,8 @@ def main():
         pmc_summary(*args.pmc_summary, args.pmc_commands, synth.CONFIGS[args.config])
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
+                          "(sharding over several GPUs is not implemented)"}))
         sys.exit(2)
     import torch
     from w8a8_quantized_decode_amd import binding as B

@@ -53,7 +53,7 @@ typedef enum a8w8_status {
                                a multiple the kernels need                          */
   A8W8_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                     */
   A8W8_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than a8w8_workspace_bytes  */
-  A8W8_ERR_UNSUPPORTED = 5, /* valid request this build does not implement          */
+  A8W8_ERR_UNSUPPORTED = 5, /* valid request the library does not implement          */
   A8W8_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed           */
 } a8w8_status;
 

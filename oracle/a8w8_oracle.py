@@ -389,7 +389,7 @@ def layer_linears_prefill(x_bits, gamma_in_bits, gamma_post_bits, eps, w_qkv, s_
     ``h1 = prefill_linear(attn, W_o, residual=x)``; then ``prefill_mlp`` with
     ``x = res = h1``.  The pages name prefill on the shared INT8 weights ([PR810] What
     changed > Gate/Up INT8 path) and a prefill hidden-state path in the serving PR; the
-    layer composition is this build's reading.
+    layer composition is a reading of those passages.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     xn_in = rmsnorm(x_bits, gamma_in_bits, eps)
