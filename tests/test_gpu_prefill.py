@@ -158,6 +158,15 @@ def test_prefill_qwen3_14b_m256():
     print(f"[note] prefill M=256: {same:.4f} of BF16 outputs bit-identical to the oracle")
 
 
+@pytest.mark.parametrize("M", [64, 300])
+def test_prefill_qwen3_14b_other_rows(M):
+    """Qwen3-14B shapes at one partial row tile (M = 64) and at two row tiles with a
+    ragged tail (M = 300: 544 Gate/Up tiles, two whole ones per workgroup and 32 split;
+    80 Down tiles, all split, about 21 K quads per workgroup)."""
+    announce(f"prefill qwen3-14b M={M}")
+    check(*run_prefill(C4, M, B.LAYOUT_TILED))
+
+
 def test_prefill_qwen3_14b_m256_wide_weights():
     """Weights twenty times larger (outputs near 2e4): every stage bound still holds."""
     announce("prefill qwen3-14b M=256 wide weights")
