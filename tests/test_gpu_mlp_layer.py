@@ -303,7 +303,8 @@ def test_layer_fused_edge_rows(cfg):
     assert q[1, :10].tolist() == TIE_CODES and host(t["s_in"])[1] == 1.0
 
 
-@pytest.mark.parametrize("M,layout", [(1, 1), (1, 0), (16, 1), (16, 0), (7, 1)])
+@pytest.mark.parametrize("M,layout", [(1, 1), (1, 0), (16, 1), (16, 0), (7, 1), (3, 1), (4, 0),
+                                      (5, 1), (24, 1)])
 def test_layer_qwen3_14b(M, layout):
     announce(f"layer qwen3-14b M={M} layout={layout}")
     got, qkv, want, t, st = run_layer(C2, M, layout=layout)
