@@ -107,6 +107,15 @@ def test_decode_layer_qwen3_14b_m16():
     _run(C2, ctx, True)
 
 
+@pytest.mark.parametrize("M", [4, 5])
+def test_decode_layer_qwen3_14b_few_rows(M):
+    """4 rows: the last row count whose GEMMs quantize their rows in the fused prologue;
+    5 rows: the first whose QKV and O read codes quantized by a kernel before them."""
+    announce(f"decode layer qwen3-14b M={M}")
+    ctx = np.random.default_rng(12 + M).integers(1, 1536, size=M).tolist()
+    _run(C2, ctx, True)
+
+
 @pytest.mark.parametrize("M", [1, 16])
 def test_decode_layer_first_token(M):
     """Context 1: attention reads only the slot the QK step has just written in the same
